@@ -1,0 +1,325 @@
+#!/usr/bin/env python3
+"""Benchmark of the fp32 GEMM + GEMV hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+One step is one pass of the whole path on resident synthetic inputs:
+  * GEMM  C = A B at the transformer-projection shape M = 8192 tokens, K = 4096,
+    N = 14336 (A ~ N(0, 1), B ~ N(0, 1/K));
+  * GEMV  y = A x for the fully-connected layer, 4096 inputs x 4096 outputs
+    (A, x ~ U[-1, 1)).
+W untimed steps, then K timed steps between two device synchronisations. The JSON
+line's `value` is the step's FLOP rate (the GEMM is more than 99.9% of it); the
+`gemm` and `gemv` objects give each kernel's own rate from HIP events recorded on
+the launch stream around every launch in the timed region. After the timed steps
+a burst of GEMV launches over 8 rotating 64 MiB matrices (more than the 256 MB
+Infinity Cache) gives the GEMV's HBM rate. Results are then verified against the
+CPU oracle (64+ sampled GEMM rows in full, every GEMV output) and the oracle's
+own time on a bounded sample of the same work is reported as `cpu_baseline`.
+
+Profiling helpers (same script, for rocprofv3 runs): --only gemm | gemv | copy
+runs just that kernel `--steps` times with no oracle; `copy` is a plain
+device-to-device copy of known size used to calibrate HBM counters.
+"""
+import argparse
+import hashlib
+import json
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import workloads as wl  # noqa: E402
+from tiled_gemm_gemv_amd import roofline as rl  # noqa: E402
+
+METRIC = "fp32 GEMM TFLOP/s & % MFMA peak; GEMV GB/s & % HBM peak (1 MI355X)"
+GEMV_SETS = 8
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
+GEMM_SRC = os.path.join(ROOT, "tiled_gemm_gemv_amd", "csrc", "mm_gemm.hip")
+GEMV_SRC = os.path.join(ROOT, "tiled_gemm_gemv_amd", "csrc", "mm_gemv.hip")
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def source_digest(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def read_traffic():
+    """Per-dispatch HBM bytes measured with rocprofv3 counters, if they were taken on
+    the current kernel sources (profiles/hbm_traffic.txt, `key: value` lines)."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return {}
+    vals = {}
+    with open(TRAFFIC_FILE) as f:
+        for line in f:
+            if ":" in line and not line.lstrip().startswith("#"):
+                k, v = line.split(":", 1)
+                vals[k.strip()] = v.strip()
+    out = {}
+    for kern, src in (("gemm", GEMM_SRC), ("gemv", GEMV_SRC)):
+        if vals.get(f"{kern}_source_sha256") == source_digest(src):
+            try:
+                out[kern] = float(vals[f"{kern}_hbm_bytes_per_dispatch"])
+            except (KeyError, ValueError):
+                pass
+    return out
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or "unknown"
+
+
+def host_threads():
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(n, 16))
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--gemv-reps", type=int, default=400)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="target length of the oracle's timed sample")
+    ap.add_argument("--only", choices=["gemm", "gemv", "copy"], default=None,
+                    help="profiling helper: launch only this kernel --steps times")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the GEMM and GEMV here need no exchange between GPUs; see DESIGN.md for how "
+              "the work would be split).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import tiled_gemm_gemv_amd as mm
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    mm.load()
+    stream = torch.cuda.current_stream()
+
+    wg = wl.WORKLOADS["gemm_proj"]
+    wv = wl.WORKLOADS["gemv4096"]
+    M, N, K = wg.M, wg.N, wg.K
+    VM, VN = wv.M, wv.N
+
+    if args.only == "copy":
+        # plain copy of 256 MiB: reads and writes 268,435,456 bytes per launch
+        src = torch.empty(64 << 20, dtype=torch.float32, device=dev).uniform_()
+        dst = torch.empty_like(src)
+        for _ in range(args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copy: {args.steps} x {src.numel() * 4} bytes")
+        return
+
+    log(f"generating inputs: {wg.describe()}, {wv.describe()}")
+    A_h, B_h = wl.gemm_inputs(wg)
+    Av_h, xv_h = wl.gemv_inputs(wv)
+    A = torch.from_numpy(A_h).to(dev)
+    B = torch.from_numpy(B_h).to(dev)
+    C = torch.empty((M, N), dtype=torch.float32, device=dev)
+    # GEMV sets: set 0 holds the workload's inputs, sets 1..7 the same values moved
+    # to other addresses (so every launch reads its matrix from HBM).
+    Avs = [torch.from_numpy(Av_h).to(dev) for _ in range(GEMV_SETS)]
+    xvs = [torch.from_numpy(xv_h).to(dev) for _ in range(GEMV_SETS)]
+    yvs = [torch.empty(VM, dtype=torch.float32, device=dev) for _ in range(GEMV_SETS)]
+    torch.cuda.synchronize()
+
+    def gemm():
+        mm.mm_gemm_f32(M, N, K, A, K, B, N, C, N, stream)
+
+    def gemv(i):
+        mm.mm_gemv_f32(VM, VN, Avs[i], xvs[i], yvs[i], stream)
+
+    if args.only == "gemm":
+        for _ in range(args.steps):
+            gemm()
+        torch.cuda.synchronize()
+        log(f"gemm: {args.steps} launches")
+        return
+    if args.only == "gemv":
+        for i in range(args.steps):
+            gemv(i % GEMV_SETS)
+        torch.cuda.synchronize()
+        log(f"gemv: {args.steps} launches")
+        return
+
+    # ---------------------------------------------------------------- warm-up
+    log(f"warm-up: {args.warmup} steps")
+    for s in range(args.warmup):
+        gemm()
+        gemv(s % GEMV_SETS)
+    torch.cuda.synchronize()
+
+    # ------------------------------------------------------------- timed steps
+    steps = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    log(f"timed: {steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(steps):
+        ev[s][0].record(stream)
+        gemm()
+        ev[s][1].record(stream)
+        gemv(0)
+        ev[s][2].record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    elapsed = t1 - t0
+    gemm_ms = [ev[s][0].elapsed_time(ev[s][1]) for s in range(steps)]
+    gemv_step_ms = [ev[s][1].elapsed_time(ev[s][2]) for s in range(steps)]
+
+    # ------------------------------------------------- GEMV burst, rotating sets
+    reps = args.gemv_reps
+    bev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+    for i in range(GEMV_SETS):
+        gemv(i)
+    torch.cuda.synchronize()
+    bev[0].record(stream)
+    for i in range(reps):
+        gemv(i % GEMV_SETS)
+        bev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    burst_ms = bev[0].elapsed_time(bev[reps]) / reps
+    per_launch_ms = sorted(bev[i].elapsed_time(bev[i + 1]) for i in range(reps))
+    gemv_med_ms = per_launch_ms[reps // 2]
+
+    # --------------------------------------------------------------- accounting
+    gemm_flop = rl.gemm_flops(M, N, K)
+    gemv_flop = rl.gemv_flops(VM, VN)
+    gemm_avg_s = float(np.mean(gemm_ms)) / 1e3
+    gemm_tflops = gemm_flop / gemm_avg_s / 1e12
+    gemv_bytes = rl.gemv_algorithmic_bytes(VM, VN)
+    gemv_gbs = gemv_bytes / (burst_ms / 1e3) / 1e9
+    step_tflops = steps * (gemm_flop + gemv_flop) / elapsed / 1e12
+    traffic = read_traffic()
+
+    # ------------------------------------------- verification + CPU baseline leg
+    import oracle
+    from oracle import verify
+
+    threads = host_threads()
+    rows64 = wl.sample_rows(wg, 64)
+    tc = time.perf_counter()
+    C64, S64 = oracle.gemm(A_h, B_h, rows=rows64, threads=threads)
+    t64 = time.perf_counter() - tc
+    rows = rows64
+    n_more = int(64 * args.cpu_seconds / max(t64, 1e-3)) if t64 > 0 else 64
+    n_more = max(64, min(n_more, M))
+    if n_more > 64:
+        rows = wl.sample_rows(wg, n_more)
+        log(f"oracle: timing {len(rows)} rows of the projection on {threads} threads")
+        tc = time.perf_counter()
+        C64, S64 = oracle.gemm(A_h, B_h, rows=rows, threads=threads)
+        t_cpu = time.perf_counter() - tc
+    else:
+        t_cpu = t64
+    got = C[torch.from_numpy(rows).to(dev)].cpu().numpy()
+    gemm_check = verify.within_tol(got, C64, S64, 1e-5)
+    tv = time.perf_counter()
+    y64, s64 = oracle.gemv(Av_h, xv_h, threads=threads)
+    tv = time.perf_counter() - tv
+    gemv_ok = True
+    for i in range(GEMV_SETS):
+        r = verify.within_tol(yvs[i].cpu().numpy(), y64, s64, 1e-5)
+        gemv_ok = gemv_ok and bool(r)
+    cpu_tflops = rl.gemm_flops(len(rows), N, K) / t_cpu / 1e12
+
+    result = {
+        "metric": METRIC,
+        "value": round(step_tflops, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(elapsed / steps * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": "fp32 GEMM M=8192 K=4096 N=14336 (A~N(0,1), B~N(0,1/K)) + fp32 GEMV "
+                        "4096x4096 (U[-1,1)) per step",
+            "gemm_config": mm.mm_gemm_f32_config_name(mm.mm_gemm_f32_select(M, N, K)),
+            "parallelism": "single GPU",
+        },
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(gemm_tflops, 3),
+            "peak": rl.MI355X_FP32_MFMA_PEAK / 1e12,
+            "unit": "TFLOP/s",
+            "frac": round(gemm_tflops / (rl.MI355X_FP32_MFMA_PEAK / 1e12), 4),
+            "traffic": traffic.get("gemm"),
+        },
+        "gemm": {
+            "kernel_ms_mean": round(float(np.mean(gemm_ms)), 4),
+            "kernel_ms_min": round(float(np.min(gemm_ms)), 4),
+            "tflops": round(gemm_tflops, 3),
+            "frac_fp32_mfma_peak": round(gemm_tflops / (rl.MI355X_FP32_MFMA_PEAK / 1e12), 4),
+            "algorithmic_bytes": rl.gemm_algorithmic_bytes(M, N, K),
+            "verified_rows": int(len(rows)),
+            "verify": str(gemm_check),
+        },
+        "gemv": {
+            "value": round(gemv_gbs, 1),
+            "unit": "GB/s",
+            "kernel_us_burst_mean": round(burst_ms * 1e3, 3),
+            "kernel_us_median_event_pair": round(gemv_med_ms * 1e3, 3),
+            "kernel_us_in_step_mean": round(float(np.mean(gemv_step_ms)) * 1e3, 3),
+            "rotating_sets": GEMV_SETS,
+            "roofline": {
+                "bound": "hbm",
+                "achieved": round(gemv_gbs, 1),
+                "peak": rl.MI355X_HBM_PEAK / 1e9,
+                "unit": "GB/s",
+                "frac": round(gemv_gbs / (rl.MI355X_HBM_PEAK / 1e9), 4),
+                "traffic": traffic.get("gemv"),
+            },
+            "verified": gemv_ok,
+            "cpu_baseline": {
+                "value": round(gemv_bytes / tv / 1e9, 3), "unit": "GB/s", "cores": threads,
+                "kind": "oracle", "sample": "the full 4096x4096 GEMV, fp64 accumulation"},
+        },
+        "cpu_baseline": {
+            "value": round(cpu_tflops, 5),
+            "unit": "TFLOP/s",
+            "cores": threads,
+            "kind": "oracle",
+            "sample": f"{len(rows)} sampled rows (all 14336 columns, K=4096) of the projection "
+                      f"GEMM, fp64 accumulation, {t_cpu:.2f} s on {cpu_model()}",
+        },
+        "verified": bool(gemm_check) and gemv_ok,
+    }
+    print(json.dumps(result), flush=True)
+    if not result["verified"]:
+        log(f"VERIFICATION FAILED: gemm {gemm_check}; gemv ok={gemv_ok}")
+        sys.exit(1)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,121 @@
+/*
+ * mm.h -- C ABI of libmm: fp32 matrix-matrix and matrix-vector products on one
+ * AMD Instinct MI355X (gfx950).
+ *
+ * Operations (plain definitions; the kernels may sum in any order):
+ *
+ *   GEMM  C = A x B,  C[i][j] = sum over k in [0, K) of A[i][k] * B[k][j]
+ *         A is M x K, B is K x N, C is M x N.
+ *         ("Matrix Operations", docs.vulkan.org ML-inference tutorial, section
+ *          "Matrix-Matrix Multiplication (GEMM)"; the same sum in "CUDA
+ *          Programming (6): Shared Memory and Matrix Multiplication
+ *          Optimization", section 3.1, and "GPU Matrix Multiplication: Tiling
+ *          and Shared Memory", section 1.)
+ *
+ *   GEMV  y = A x,    y[i] = sum over j in [0, N) of A[i][j] * x[j]
+ *         A is M x N, x has N entries, y has M entries.
+ *         ("Matrix Operations", section "Matrix-Vector Multiplication".)
+ *
+ * Conventions shared by every entry point:
+ *   - Layout: row-major. Element (i, k) of A lives at A[i * lda + k], (k, j) of B
+ *     at B[k * ldb + j], (i, j) of C at C[i * ldc + j]. The pages lay matrices out
+ *     the same way with packed rows; the leading dimensions generalise that.
+ *   - Memory: every pointer is device memory owned by the caller (hipMalloc or a
+ *     torch tensor on the GPU), 4-byte aligned, and must stay valid until the
+ *     work enqueued on `stream` has finished. Inputs are only read; outputs are
+ *     only written. Outputs must not overlap inputs (undefined, not checked).
+ *     Wider alignment (16 bytes, leading dimensions that are multiples of 4) lets
+ *     the kernels use 16-byte loads; it is never required.
+ *   - Output: only the logical output elements are written (each exactly once);
+ *     bytes in leading-dimension gaps and beyond are left untouched. The output
+ *     is overwritten: there is no scaling of, or accumulation into, its old value.
+ *   - Stream: a hipStream_t passed as void*; NULL means the default stream. Calls
+ *     only enqueue work and return; they never synchronise and never allocate.
+ *     Errors raised by the device while the work runs surface at the caller's
+ *     next synchronisation of that stream.
+ *   - Threads: the library keeps no mutable global state; calls from several
+ *     host threads, on any streams, are safe.
+ *   - Return value: an mm_status. Arguments are checked on the host before any
+ *     HIP call; an invalid call enqueues nothing.
+ */
+#ifndef MM_H
+#define MM_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum mm_status {
+    MM_OK = 0,
+    MM_ERR_INVALID_ARG = 1, /* bad size, leading dimension, pointer or config index */
+    MM_ERR_NO_DEVICE = 2,   /* no usable HIP device in this process */
+    MM_ERR_LAUNCH = 3       /* the HIP runtime refused the launch (see mm_last_error) */
+} mm_status;
+
+/*
+ * mm_gemm_f32: C = A x B in fp32 (fp32 products, fp32 accumulation on the
+ * matrix cores).
+ *   M, N, K   sizes, 0 <= M, N, K <= 2^31 - 1.
+ *   A, lda    M x K, lda >= max(1, K). May be NULL when M == 0 or K == 0.
+ *   B, ldb    K x N, ldb >= max(1, N). May be NULL when K == 0 or N == 0.
+ *   C, ldc    M x N, ldc >= max(1, N). May be NULL when M == 0 or N == 0.
+ *   stream    hipStream_t or NULL.
+ * M == 0 or N == 0: nothing is enqueued and MM_OK is returned.
+ * K == 0: C is filled with zeros (the empty sum; the pages' kernels write a
+ * zero-initialised sum when the k loop does not run).
+ * Errors: MM_ERR_INVALID_ARG (negative or too-large size, leading dimension too
+ * small, NULL pointer with a non-empty extent, byte offset overflow),
+ * MM_ERR_NO_DEVICE, MM_ERR_LAUNCH.
+ */
+int mm_gemm_f32(int64_t M, int64_t N, int64_t K,
+                const float *A, int64_t lda,
+                const float *B, int64_t ldb,
+                float *C, int64_t ldc, void *stream);
+
+/*
+ * mm_gemv_f32: y = A x in fp32 (fp32 products and accumulation).
+ *   M, N      sizes, 0 <= M, N <= 2^31 - 1.
+ *   A         M x N with packed rows (leading dimension N). May be NULL when
+ *             M == 0 or N == 0.
+ *   x         N entries, contiguous. May be NULL when N == 0.
+ *   y         M entries, contiguous. May be NULL when M == 0.
+ *   stream    hipStream_t or NULL.
+ * M == 0: nothing is enqueued. N == 0: y is filled with zeros.
+ * Errors: as for mm_gemm_f32.
+ */
+int mm_gemv_f32(int64_t M, int64_t N, const float *A, const float *x, float *y,
+                void *stream);
+
+/*
+ * Tile configurations of the GEMM. mm_gemm_f32 picks one per shape; the calls
+ * below expose the choice and let a caller (tests, tuning) run a given one.
+ *   mm_gemm_f32_num_configs: number of configurations, >= 1.
+ *   mm_gemm_f32_config_name: static NUL-terminated description of config `cfg`
+ *     (e.g. "256x256x32 w128x64"), or NULL if cfg is out of range.
+ *   mm_gemm_f32_select: the config mm_gemm_f32 would use for (M, N, K).
+ *   mm_gemm_f32_config: mm_gemm_f32 forced to config `cfg`; same arguments and
+ *     errors, plus MM_ERR_INVALID_ARG for cfg out of range. Every config gives a
+ *     correct product for every shape.
+ */
+int mm_gemm_f32_num_configs(void);
+const char *mm_gemm_f32_config_name(int cfg);
+int mm_gemm_f32_select(int64_t M, int64_t N, int64_t K);
+int mm_gemm_f32_config(int cfg, int64_t M, int64_t N, int64_t K,
+                       const float *A, int64_t lda,
+                       const float *B, int64_t ldb,
+                       float *C, int64_t ldc, void *stream);
+
+/* mm_status_string: static text for a status code (never NULL). */
+const char *mm_status_string(int status);
+
+/* mm_last_error: static or thread-local text describing the last failure seen by
+ * this host thread (the HIP error string for MM_ERR_LAUNCH), or "" if none. */
+const char *mm_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MM_H */

@@ -1,0 +1,210 @@
+"""GPU parity of the GEMM (libmm via its C ABI) against the CPU oracle.
+
+Bars: integer-valued inputs must match the oracle bit for bit (every fp32
+operation is exact on them, in any order); random inputs must satisfy
+|C - C_ref| <= 1e-5 * sum_k |A_ik B_kj| per element. Every tile configuration is
+run on the same cases, so the shape-based choice cannot hide a broken one.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import verify
+import tiled_gemm_gemv_amd as mm
+import workloads as wl
+from gpu_helpers import (nan_output, outside_untouched, require_gpu, strided_on_device,
+                         to_device)
+
+pytestmark = pytest.mark.gpu
+
+REL_TOL = 1e-5
+
+
+@pytest.fixture(scope="module")
+def dev():
+    d = require_gpu()
+    mm.load()
+    return d
+
+
+def n_configs():
+    try:
+        return mm.mm_gemm_f32_num_configs()
+    except OSError:
+        return 3
+
+
+CONFIGS = list(range(n_configs()))
+
+
+def gpu_gemm(A, B, dev, cfg=None):
+    Ad, Bd = to_device(A, dev), to_device(B, dev)
+    C = mm.gemm(Ad, Bd, config=cfg)
+    torch.cuda.synchronize()
+    return C.cpu().numpy()
+
+
+def assert_exact(C, A, B):
+    C64, _ = oracle.gemm(A, B)
+    r = verify.exact(C, C64)
+    assert r, str(r)
+
+
+def assert_tol(C, A, B):
+    C64, S64 = oracle.gemm(A, B)
+    r = verify.within_tol(C, C64, S64, REL_TOL)
+    assert r, str(r)
+
+
+@pytest.mark.parametrize("cfg", CONFIGS)
+def test_permutation_rows(dev, cfg):
+    """P B for a permutation P and unique integers in B: pins the MFMA operand and
+    accumulator lane layouts (a swapped row or column shows up as a mismatch)."""
+    M = K = 96
+    N = 80
+    perm = np.random.default_rng(5).permutation(K)
+    P = np.zeros((M, K), np.float32)
+    P[np.arange(M), perm] = 1
+    B = (np.arange(K * N, dtype=np.float32).reshape(K, N) - 1000)
+    C = gpu_gemm(P, B, dev, cfg)
+    assert np.array_equal(C, B[perm])
+
+
+@pytest.mark.parametrize("cfg", CONFIGS)
+def test_one_hot_positions(dev, cfg):
+    """A single 1 in A at (i, k) copies row k of B into row i of C and nothing else;
+    positions cover both lane halves, several 32-blocks and the K tail."""
+    M, K, N = 150, 70, 170
+    B = wl.random_matrix(77, K, N)
+    for (i, k) in [(0, 0), (31, 33), (32, 1), (100, 69), (149, 35), (64, 16)]:
+        A = np.zeros((M, K), np.float32)
+        A[i, k] = 1
+        C = gpu_gemm(A, B, dev, cfg)
+        want = np.zeros((M, N), np.float32)
+        want[i] = B[k]
+        assert np.array_equal(C, want), (i, k)
+
+
+@pytest.mark.parametrize("cfg", CONFIGS + [None])
+@pytest.mark.parametrize("name", ["gemm128", "gemm1024", "gemm_ragged"])
+def test_workload_tolerance(dev, name, cfg):
+    w = wl.WORKLOADS[name]
+    A, B = wl.gemm_inputs(w)
+    assert_tol(gpu_gemm(A, B, dev, cfg), A, B)
+
+
+@pytest.mark.parametrize("cfg", CONFIGS + [None])
+@pytest.mark.parametrize("name", ["gemm128", "gemm1024", "gemm_ragged"])
+def test_workload_integer_exact(dev, name, cfg):
+    w = wl.WORKLOADS[name].with_dist("int4")
+    A, B = wl.gemm_inputs(w)
+    assert_exact(gpu_gemm(A, B, dev, cfg), A, B)
+
+
+EDGE = [1, 2, 3, 15, 16, 17, 31, 32, 33, 63, 64, 65, 127, 128, 129, 255, 256, 257]
+
+
+def edge_shapes(seed, count):
+    rng = np.random.default_rng(seed)
+    shapes = [(1, 1, 1), (257, 257, 257), (1, 257, 33), (257, 1, 65), (33, 65, 1)]
+    while len(shapes) < count:
+        shapes.append(tuple(int(v) for v in rng.choice(EDGE, 3)))
+    return shapes
+
+
+@pytest.mark.parametrize("cfg", CONFIGS)
+def test_edge_shape_sweep(dev, cfg):
+    """Shapes around tile multiples in every dimension; integer inputs, exact."""
+    for t, (M, N, K) in enumerate(edge_shapes(100 + cfg, 30)):
+        A = wl.random_matrix(1000 + t, M, K, "int4")
+        B = wl.random_matrix(2000 + t, K, N, "int4")
+        C = gpu_gemm(A, B, dev, cfg)
+        C64, _ = oracle.gemm(A, B)
+        r = verify.exact(C, C64)
+        assert r, f"shape {(M, N, K)}: {r}"
+
+
+@pytest.mark.parametrize("cfg", CONFIGS)
+@pytest.mark.parametrize("offsets", [(0, 0), (1, 2), (3, 0)])
+def test_strided_poisoned_views(dev, cfg, offsets):
+    """Leading dimensions beyond the width with NaN in every gap, a NaN row past each
+    input and a start that is only 4-byte aligned: any read outside a matrix turns
+    its outputs into NaN, and every C element outside the view must stay NaN."""
+    M, N, K = 203, 181, 97
+    A = wl.random_matrix(31, M, K, "int4")
+    B = wl.random_matrix(32, K, N, "int4")
+    _, Av = strided_on_device(A, K + 3, dev, offset=offsets[0])
+    _, Bv = strided_on_device(B, N + 5, dev, offset=offsets[1])
+    Cbuf, Cv = nan_output(M, N, N + 7, dev)
+    mm.gemm(Av, Bv, out=Cv, config=cfg)
+    torch.cuda.synchronize()
+    assert_exact(Cv.cpu().numpy(), A, B)
+    assert outside_untouched(Cbuf, M, N)
+
+
+@pytest.mark.parametrize("cfg", CONFIGS)
+def test_k_zero_writes_zeros_and_empty_is_noop(dev, cfg):
+    Cbuf, Cv = nan_output(37, 45, 50, dev)
+    A = torch.empty((37, 0), dtype=torch.float32, device=dev)
+    B = torch.empty((0, 45), dtype=torch.float32, device=dev)
+    mm.gemm(A, B, out=Cv, config=cfg)
+    torch.cuda.synchronize()
+    assert (Cv == 0).all().item()
+    assert outside_untouched(Cbuf, 37, 45)
+    Cbuf2, Cv2 = nan_output(0, 45, 45, dev)
+    mm.gemm(torch.empty((0, 3), dtype=torch.float32, device=dev),
+            torch.ones((3, 45), dtype=torch.float32, device=dev), out=Cv2, config=cfg)
+    torch.cuda.synchronize()
+    assert torch.isnan(Cbuf2).all().item()
+
+
+def test_non_default_stream(dev):
+    w = wl.WORKLOADS["gemm_ragged"].with_dist("int4")
+    A, B = wl.gemm_inputs(w)
+    Ad, Bd = to_device(A, dev), to_device(B, dev)
+    s = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):
+        C = torch.empty((A.shape[0], B.shape[1]), dtype=torch.float32, device=dev)
+        mm.gemm(Ad, Bd, out=C)
+    s.synchronize()
+    assert_exact(C.cpu().numpy(), A, B)
+
+
+def test_deterministic(dev):
+    w = wl.WORKLOADS["gemm1024"]
+    A, B = wl.gemm_inputs(w)
+    Ad, Bd = to_device(A, dev), to_device(B, dev)
+    C1 = mm.gemm(Ad, Bd)
+    C2 = mm.gemm(Ad, Bd)
+    torch.cuda.synchronize()
+    assert torch.equal(C1.view(torch.int32), C2.view(torch.int32))
+
+
+def test_transpose_identity(dev):
+    """(A B)^T == B^T A^T, exact on integers, from two GPU calls."""
+    A = wl.random_matrix(41, 300, 130, "int4")
+    B = wl.random_matrix(42, 130, 210, "int4")
+    C = gpu_gemm(A, B, dev)
+    Ct = gpu_gemm(np.ascontiguousarray(B.T), np.ascontiguousarray(A.T), dev)
+    assert np.array_equal(C.T, Ct)
+
+
+@pytest.mark.parametrize("dist", ["normal", "int4"])
+def test_projection_spot_rows(dev, dist):
+    """The 8192 x 4096 x 14336 projection in the configuration the benchmark times:
+    64 sampled rows checked in full against the oracle."""
+    w = wl.WORKLOADS["gemm_proj"]
+    if dist == "int4":
+        w = w.with_dist("int4")
+    A, B = wl.gemm_inputs(w)
+    rows = wl.sample_rows(wl.WORKLOADS["gemm_proj"], 64)
+    Ad, Bd = to_device(A, dev), to_device(B, dev)
+    C = mm.gemm(Ad, Bd)
+    torch.cuda.synchronize()
+    got = C[torch.from_numpy(rows).to(dev)].cpu().numpy()
+    del C, Ad, Bd
+    C64, S64 = oracle.gemm(A, B, rows=rows)
+    r = verify.exact(got, C64) if dist == "int4" else verify.within_tol(got, C64, S64, REL_TOL)
+    assert r, str(r)

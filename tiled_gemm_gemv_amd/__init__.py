@@ -1,0 +1,214 @@
+"""fp32 GEMM and GEMV on one AMD Instinct MI355X, through libmm's C ABI.
+
+The functions named like the C entry points (mm_gemm_f32, mm_gemv_f32, ...)
+marshal their arguments and call libmm.so; every step of the computation runs in
+the library's HIP kernels. Pointer arguments accept a device address (int) or a
+torch tensor on the GPU; `stream` accepts a hipStream_t address (int), a
+torch.cuda.Stream, or None for torch's current stream on the current device.
+
+gemm(A, B, out=None) and gemv(A, x, out=None) are conveniences for torch tensors:
+they check dtypes, devices and strides, allocate the output with torch when none
+is given, and call the C entry points. PyTorch only provides device memory and
+streams here.
+
+There is no fallback: if libmm.so is missing or fails to load, every call raises.
+Build it with `python -m tiled_gemm_gemv_amd.build`.
+"""
+import ctypes
+import os
+
+from .build import LIB as _LIB_PATH
+
+MM_OK = 0
+MM_ERR_INVALID_ARG = 1
+MM_ERR_NO_DEVICE = 2
+MM_ERR_LAUNCH = 3
+
+
+class MMError(RuntimeError):
+    """A libmm call returned a non-zero status."""
+
+    def __init__(self, status, where, detail=""):
+        self.status = status
+        text = _lib_or_none().mm_status_string(status).decode() if _lib_or_none() else str(status)
+        msg = f"{where}: {text} (status {status})"
+        if detail:
+            msg += f": {detail}"
+        super().__init__(msg)
+
+
+_lib = None
+
+
+def _lib_or_none():
+    return _lib
+
+
+def lib_path() -> str:
+    return _LIB_PATH
+
+
+def load():
+    """Load libmm.so (once). Raises OSError if it is missing or cannot be loaded."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise OSError(f"{_LIB_PATH} is not built; run `python -m tiled_gemm_gemv_amd.build`")
+    lib = ctypes.CDLL(_LIB_PATH)
+    i64, vp, ci = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
+    lib.mm_gemm_f32.argtypes = [i64, i64, i64, vp, i64, vp, i64, vp, i64, vp]
+    lib.mm_gemm_f32.restype = ci
+    lib.mm_gemm_f32_config.argtypes = [ci, i64, i64, i64, vp, i64, vp, i64, vp, i64, vp]
+    lib.mm_gemm_f32_config.restype = ci
+    lib.mm_gemm_f32_num_configs.argtypes = []
+    lib.mm_gemm_f32_num_configs.restype = ci
+    lib.mm_gemm_f32_config_name.argtypes = [ci]
+    lib.mm_gemm_f32_config_name.restype = ctypes.c_char_p
+    lib.mm_gemm_f32_select.argtypes = [i64, i64, i64]
+    lib.mm_gemm_f32_select.restype = ci
+    lib.mm_gemv_f32.argtypes = [i64, i64, vp, vp, vp, vp]
+    lib.mm_gemv_f32.restype = ci
+    lib.mm_status_string.argtypes = [ci]
+    lib.mm_status_string.restype = ctypes.c_char_p
+    lib.mm_last_error.argtypes = []
+    lib.mm_last_error.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+# ----------------------------------------------------------------- marshalling
+
+def _addr(p):
+    """Device address of an int, None or torch tensor."""
+    if p is None:
+        return None
+    if isinstance(p, int):
+        return p or None
+    if hasattr(p, "data_ptr"):
+        return p.data_ptr() or None
+    raise TypeError(f"expected a device address or a tensor, got {type(p).__name__}")
+
+
+def _stream(s):
+    if s is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream or None
+    if isinstance(s, int):
+        return s or None
+    if hasattr(s, "cuda_stream"):
+        return s.cuda_stream or None
+    raise TypeError(f"expected a stream address or torch.cuda.Stream, got {type(s).__name__}")
+
+
+def _check(status, where):
+    if status != MM_OK:
+        raise MMError(status, where, load().mm_last_error().decode())
+
+
+# ------------------------------------------------------- C entry points by name
+
+def mm_gemm_f32(M, N, K, A, lda, B, ldb, C, ldc, stream=None):
+    """C = A x B (row-major, leading dimensions lda, ldb, ldc). Raises MMError."""
+    lib = load()
+    _check(lib.mm_gemm_f32(M, N, K, _addr(A), lda, _addr(B), ldb, _addr(C), ldc,
+                           _stream(stream)), "mm_gemm_f32")
+
+
+def mm_gemm_f32_config(cfg, M, N, K, A, lda, B, ldb, C, ldc, stream=None):
+    """mm_gemm_f32 with tile configuration `cfg` forced. Raises MMError."""
+    lib = load()
+    _check(lib.mm_gemm_f32_config(cfg, M, N, K, _addr(A), lda, _addr(B), ldb, _addr(C), ldc,
+                                  _stream(stream)), "mm_gemm_f32_config")
+
+
+def mm_gemv_f32(M, N, A, x, y, stream=None):
+    """y = A x (A M x N with packed rows). Raises MMError."""
+    lib = load()
+    _check(lib.mm_gemv_f32(M, N, _addr(A), _addr(x), _addr(y), _stream(stream)), "mm_gemv_f32")
+
+
+def mm_gemm_f32_num_configs():
+    return load().mm_gemm_f32_num_configs()
+
+
+def mm_gemm_f32_config_name(cfg):
+    name = load().mm_gemm_f32_config_name(cfg)
+    return name.decode() if name is not None else None
+
+
+def mm_gemm_f32_select(M, N, K):
+    return load().mm_gemm_f32_select(M, N, K)
+
+
+def mm_status_string(status):
+    return load().mm_status_string(status).decode()
+
+
+def mm_last_error():
+    return load().mm_last_error().decode()
+
+
+# ----------------------------------------------------- torch-tensor front ends
+
+def _matrix(t, name):
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != torch.float32:
+        raise TypeError(f"{name} must be float32, got {t.dtype}")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on the GPU, got {t.device}")
+    if t.dim() != 2:
+        raise ValueError(f"{name} must be 2-D")
+    rows, cols = t.shape
+    if cols > 1 and t.stride(1) != 1:
+        raise ValueError(f"{name} must have unit column stride")
+    ld = t.stride(0) if rows > 1 else max(cols, 1)
+    if ld < max(cols, 1):
+        raise ValueError(f"{name} row stride {ld} is below its width {cols}")
+    return ld
+
+
+def gemm(A, B, out=None, config=None, stream=None):
+    """out = A @ B for fp32 GPU tensors (any row strides, unit column stride)."""
+    import torch
+    lda = _matrix(A, "A")
+    ldb = _matrix(B, "B")
+    M, K = A.shape
+    K2, N = B.shape
+    if K2 != K:
+        raise ValueError(f"inner dimensions differ: {tuple(A.shape)} x {tuple(B.shape)}")
+    if B.device != A.device:
+        raise ValueError("A and B are on different devices")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=A.device)
+    if tuple(out.shape) != (M, N):
+        raise ValueError(f"out has shape {tuple(out.shape)}, expected {(M, N)}")
+    ldc = _matrix(out, "out")
+    with torch.cuda.device(A.device):
+        if config is None:
+            mm_gemm_f32(M, N, K, A, lda, B, ldb, out, ldc, stream)
+        else:
+            mm_gemm_f32_config(config, M, N, K, A, lda, B, ldb, out, ldc, stream)
+    return out
+
+
+def gemv(A, x, out=None, stream=None):
+    """out = A @ x for an fp32 GPU matrix with packed rows and a contiguous vector."""
+    import torch
+    _matrix(A, "A")
+    M, N = A.shape
+    if not A.is_contiguous():
+        raise ValueError("A must have packed rows (contiguous)")
+    if x.dtype != torch.float32 or x.dim() != 1 or x.shape[0] != N or not x.is_contiguous():
+        raise ValueError(f"x must be a contiguous float32 vector of {N} entries")
+    if x.device != A.device:
+        raise ValueError("A and x are on different devices")
+    if out is None:
+        out = torch.empty(M, dtype=torch.float32, device=A.device)
+    if out.dtype != torch.float32 or tuple(out.shape) != (M,) or not out.is_contiguous():
+        raise ValueError(f"out must be a contiguous float32 vector of {M} entries")
+    with torch.cuda.device(A.device):
+        mm_gemv_f32(M, N, A, x, out, stream)
+    return out

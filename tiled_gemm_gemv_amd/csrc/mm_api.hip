@@ -1,0 +1,147 @@
+// mm_api.hip -- the C ABI of libmm (declared in include/mm.h): host-side argument
+// checks, shape -> kernel configuration, launch, and status codes.
+#include <stdint.h>
+#include <stdio.h>
+
+#include "mm.h"
+#include "mm_internal.h"
+
+namespace {
+
+thread_local char g_last_error[256] = "";
+
+void set_error(const char *what, hipError_t e)
+{
+    snprintf(g_last_error, sizeof g_last_error, "%s: %s (%d)", what, hipGetErrorString(e), (int)e);
+}
+
+void set_error_text(const char *what)
+{
+    snprintf(g_last_error, sizeof g_last_error, "%s", what);
+}
+
+int from_hip(const char *what, hipError_t e)
+{
+    if (e == hipSuccess) return MM_OK;
+    set_error(what, e);
+    if (e == hipErrorNoDevice || e == hipErrorInsufficientDriver) return MM_ERR_NO_DEVICE;
+    return MM_ERR_LAUNCH;
+}
+
+int invalid(const char *why)
+{
+    set_error_text(why);
+    return MM_ERR_INVALID_ARG;
+}
+
+constexpr int64_t kMaxDim = 0x7fffffff;
+
+// Byte extent of a rows x cols matrix with row stride ld is
+// 4 * ((rows - 1) * ld + cols); true if that fits in int64 (rows, cols >= 1).
+bool extent_fits(int64_t rows, int64_t cols, int64_t ld)
+{
+    const int64_t limit = INT64_MAX / 4;
+    if (ld > 0 && rows - 1 > (limit - cols) / ld) return false;
+    return true;
+}
+
+int check_gemm(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda, const float *B,
+               int64_t ldb, const float *C, int64_t ldc)
+{
+    if (M < 0 || N < 0 || K < 0) return invalid("negative size");
+    if (M > kMaxDim || N > kMaxDim || K > kMaxDim) return invalid("size above 2^31 - 1");
+    if (lda < (K > 1 ? K : 1)) return invalid("lda < max(1, K)");
+    if (ldb < (N > 1 ? N : 1)) return invalid("ldb < max(1, N)");
+    if (ldc < (N > 1 ? N : 1)) return invalid("ldc < max(1, N)");
+    if (M > 0 && K > 0 && !A) return invalid("A is NULL");
+    if (K > 0 && N > 0 && !B) return invalid("B is NULL");
+    if (M > 0 && N > 0 && !C) return invalid("C is NULL");
+    if (M > 0 && K > 0 && !extent_fits(M, K, lda)) return invalid("A extent overflows");
+    if (K > 0 && N > 0 && !extent_fits(K, N, ldb)) return invalid("B extent overflows");
+    if (M > 0 && N > 0 && !extent_fits(M, N, ldc)) return invalid("C extent overflows");
+    return MM_OK;
+}
+
+int run_gemm(int cfg, int64_t M, int64_t N, int64_t K, const float *A, int64_t lda, const float *B,
+             int64_t ldb, float *C, int64_t ldc, void *stream)
+{
+    const int st = check_gemm(M, N, K, A, lda, B, ldb, C, ldc);
+    if (st != MM_OK) return st;
+    if (M == 0 || N == 0) return MM_OK;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (K == 0) return from_hip("zero fill launch", mm::zero_fill_launch(C, M, N, ldc, s));
+    mm::GemmArgs a;
+    a.A = A;
+    a.B = B;
+    a.C = C;
+    a.lda = lda;
+    a.ldb = ldb;
+    a.ldc = ldc;
+    a.M = (int)M;
+    a.N = (int)N;
+    a.K = (int)K;
+    if (cfg < 0) cfg = mm::gemm_select_config(M, N, K);
+    return from_hip("gemm launch", mm::gemm_launch(cfg, a, s));
+}
+
+}  // namespace
+
+extern "C" {
+
+int mm_gemm_f32(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda, const float *B,
+                int64_t ldb, float *C, int64_t ldc, void *stream)
+{
+    return run_gemm(-1, M, N, K, A, lda, B, ldb, C, ldc, stream);
+}
+
+int mm_gemm_f32_config(int cfg, int64_t M, int64_t N, int64_t K, const float *A, int64_t lda,
+                       const float *B, int64_t ldb, float *C, int64_t ldc, void *stream)
+{
+    if (cfg < 0 || cfg >= mm::gemm_num_configs()) return invalid("config index out of range");
+    return run_gemm(cfg, M, N, K, A, lda, B, ldb, C, ldc, stream);
+}
+
+int mm_gemm_f32_num_configs(void) { return mm::gemm_num_configs(); }
+
+const char *mm_gemm_f32_config_name(int cfg) { return mm::gemm_config_name(cfg); }
+
+int mm_gemm_f32_select(int64_t M, int64_t N, int64_t K)
+{
+    if (M < 0 || N < 0 || K < 0) return 0;
+    return mm::gemm_select_config(M, N, K);
+}
+
+int mm_gemv_f32(int64_t M, int64_t N, const float *A, const float *x, float *y, void *stream)
+{
+    if (M < 0 || N < 0) return invalid("negative size");
+    if (M > kMaxDim || N > kMaxDim) return invalid("size above 2^31 - 1");
+    if (M > 0 && N > 0 && !A) return invalid("A is NULL");
+    if (N > 0 && !x) return invalid("x is NULL");
+    if (M > 0 && !y) return invalid("y is NULL");
+    if (M > 0 && N > 0 && !extent_fits(M, N, N)) return invalid("A extent overflows");
+    if (M == 0) return MM_OK;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (N == 0) return from_hip("zero fill launch", mm::zero_fill_launch(y, 1, M, M, s));
+    mm::GemvArgs a;
+    a.A = A;
+    a.x = x;
+    a.y = y;
+    a.M = (int)M;
+    a.N = (int)N;
+    return from_hip("gemv launch", mm::gemv_launch(a, s));
+}
+
+const char *mm_status_string(int status)
+{
+    switch (status) {
+    case MM_OK: return "ok";
+    case MM_ERR_INVALID_ARG: return "invalid argument";
+    case MM_ERR_NO_DEVICE: return "no HIP device";
+    case MM_ERR_LAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+    }
+}
+
+const char *mm_last_error(void) { return g_last_error; }
+
+}  // extern "C"

@@ -1,0 +1,40 @@
+// mm_internal.h -- declarations shared by the HIP sources of libmm (not installed).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mm {
+
+// Arguments of one GEMM launch, already validated on the host. Sizes fit in
+// int32; offsets are formed in int64.
+struct GemmArgs {
+    const float *A;
+    const float *B;
+    float *C;
+    int64_t lda, ldb, ldc;
+    int M, N, K;
+};
+
+// Arguments of one GEMV launch (A has packed rows: leading dimension N).
+struct GemvArgs {
+    const float *A;
+    const float *x;
+    float *y;
+    int M, N;
+};
+
+// GEMM tile configurations, in the order of the public config index.
+int gemm_num_configs();
+const char *gemm_config_name(int cfg);
+int gemm_select_config(int64_t M, int64_t N, int64_t K);
+// Enqueue config `cfg` of the GEMM (K >= 1, M >= 1, N >= 1).
+hipError_t gemm_launch(int cfg, const GemmArgs &a, hipStream_t stream);
+
+// Enqueue the GEMV (M >= 1, N >= 1).
+hipError_t gemv_launch(const GemvArgs &a, hipStream_t stream);
+
+// Enqueue a fill of the rows x cols matrix at p (row stride ld) with zeros.
+hipError_t zero_fill_launch(float *p, int64_t rows, int64_t cols, int64_t ld, hipStream_t stream);
+
+}  // namespace mm
