@@ -6,13 +6,23 @@
 // streams from HBM (0.5 FLOP per byte). The pages give each output row to one
 // thread and stage x in shared memory. On CDNA4 one thread per row would make
 // neighbouring lanes read addresses a whole row apart; here one 64-lane wave
-// owns a row instead: its lanes read the row front to back in 16-byte pieces
-// (1 KB per wave instruction, fully coalesced), multiply by the matching pieces
-// of x, and combine the 64 partial sums with a cross-lane reduction. x is read
-// in the same pattern; at 16 KB it stays in the CU's L1 / the L2, so HBM traffic
-// is A plus one copy of x and y. Up to 16 row pieces per lane are in flight at
-// once, which covers the 4096-column rows of the fully-connected layer in one
-// round trip; longer rows loop.
+// owns a row instead: its lanes read the row in 16-byte pieces (1 KB per wave
+// instruction, fully coalesced), multiply by the matching pieces of x, and
+// combine the 64 partial sums with a cross-lane reduction.
+//
+// Launch shape and memory-level parallelism, sized by measurement on MI355X:
+//   * a workgroup is a single wave, so waves start as soon as a CU has room;
+//   * a wave issues the loads for up to 16 KB of its row (16 pieces per lane)
+//     before it does any arithmetic, so a 4096-column row is one round trip;
+//   * A is read with non-temporal loads (it is used once); x (16 KB at the
+//     fully-connected-layer size) is read with ordinary loads and stays in the
+//     CU's L1 and the L2 for the other waves;
+//   * the order in which a wave visits its 16 pieces is rotated by the row
+//     index, so the waves in flight spread over different column offsets and
+//     hence over more HBM channels than rows of a power-of-two length would.
+// Longer rows take several rounds. The summation order (per-lane partial sums
+// over the row's pieces, then a butterfly across lanes) is fixed for a given N,
+// so results are deterministic.
 #include "mm_internal.h"
 
 namespace mm {
@@ -20,9 +30,7 @@ namespace {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kGemvThreads = 256;          // 4 waves, one row each
-constexpr int kRowsPerBlock = kGemvThreads / 64;
-constexpr int kUnroll = 16;                // 16-byte pieces per lane per round
+constexpr int kPieces = 16;  // 16-byte (or 4-byte) pieces per lane per round
 
 __device__ __forceinline__ float wave_sum(float v)
 {
@@ -31,56 +39,83 @@ __device__ __forceinline__ float wave_sum(float v)
     return v;
 }
 
-// VEC: rows and x are 16-byte aligned and N % 4 == 0.
+// VEC: A and x 16-byte aligned and N % 4 == 0. One wave (workgroup) per row.
 template <bool VEC>
-__global__ __launch_bounds__(kGemvThreads) void gemv_f32_kernel(GemvArgs p)
+__global__ __launch_bounds__(64) void gemv_f32_kernel(GemvArgs p)
 {
-    const int lane = threadIdx.x & 63;
-    const int row = blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
-    if (row >= p.M) return;  // whole wave leaves; the kernel has no barrier
-    const float *a = p.A + (int64_t)row * p.N;
+    const int lane = threadIdx.x;
+    const int row = blockIdx.x;
+    const int rot = row & (kPieces - 1);
     float acc = 0.f;
     if constexpr (VEC) {
-        const f32x4 *a4 = reinterpret_cast<const f32x4 *>(a);
+        const f32x4 *a4 = reinterpret_cast<const f32x4 *>(p.A + (int64_t)row * p.N);
         const f32x4 *x4 = reinterpret_cast<const f32x4 *>(p.x);
         const int n4 = p.N >> 2;
-        int c = 0;
-        for (; c + 64 * kUnroll <= n4; c += 64 * kUnroll) {
-            f32x4 va[kUnroll];
+        const int rounds = n4 / (64 * kPieces);
+        // full rounds: 16 pieces of 64 float4 each, no masking
+        for (int r = 0; r < rounds; ++r) {
+            const f32x4 *ar = a4 + r * (64 * kPieces);
+            const f32x4 *xr = x4 + r * (64 * kPieces);
+            // An opaque copy of the lane index: stops the compiler from hoisting
+            // the 32 per-piece addresses out of the loop, which would hold them in
+            // registers for the whole kernel and halve the waves a SIMD can hold.
+            int l = lane;
+            asm volatile("" : "+v"(l));
+            f32x4 va[kPieces], vx[kPieces];
 #pragma unroll
-            for (int u = 0; u < kUnroll; ++u) va[u] = a4[c + u * 64 + lane];
+            for (int u = 0; u < kPieces; ++u) {
+                const int idx = ((u + rot) & (kPieces - 1)) * 64 + l;
+                va[u] = __builtin_nontemporal_load(ar + idx);
+                vx[u] = xr[idx];
+            }
+            // keep every load above ahead of the arithmetic below
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int u = 0; u < kUnroll; ++u) {
-                const f32x4 vx = x4[c + u * 64 + lane];
-                acc += va[u][0] * vx[0];
-                acc += va[u][1] * vx[1];
-                acc += va[u][2] * vx[2];
-                acc += va[u][3] * vx[3];
+            for (int u = 0; u < kPieces; ++u) {
+                acc += va[u][0] * vx[u][0];
+                acc += va[u][1] * vx[u][1];
+                acc += va[u][2] * vx[u][2];
+                acc += va[u][3] * vx[u][3];
             }
         }
-        for (; c < n4; c += 64) {
-            const int idx = c + lane;
-            if (idx < n4) {
-                const f32x4 va = a4[idx];
-                const f32x4 vx = x4[idx];
-                acc += va[0] * vx[0];
-                acc += va[1] * vx[1];
-                acc += va[2] * vx[2];
-                acc += va[3] * vx[3];
+        const int base = rounds * (64 * kPieces);
+        // last, partial round
+        if (base < n4) {
+            f32x4 va[kPieces], vx[kPieces];
+#pragma unroll
+            for (int u = 0; u < kPieces; ++u) {
+                const int idx = base + u * 64 + lane;
+                if (idx < n4) {
+                    va[u] = __builtin_nontemporal_load(a4 + idx);
+                    vx[u] = x4[idx];
+                } else {
+                    va[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+                    vx[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int u = 0; u < kPieces; ++u) {
+                acc += va[u][0] * vx[u][0];
+                acc += va[u][1] * vx[u][1];
+                acc += va[u][2] * vx[u][2];
+                acc += va[u][3] * vx[u][3];
             }
         }
     } else {
-        int c = 0;
-        for (; c + 64 * kUnroll <= p.N; c += 64 * kUnroll) {
-            float va[kUnroll];
+        const float *a = p.A + (int64_t)row * p.N;
+        for (int base = 0; base < p.N; base += 64 * kPieces) {
+            float va[kPieces], vx[kPieces];
 #pragma unroll
-            for (int u = 0; u < kUnroll; ++u) va[u] = a[c + u * 64 + lane];
+            for (int u = 0; u < kPieces; ++u) {
+                const int idx = base + u * 64 + lane;
+                const bool ok = idx < p.N;
+                va[u] = ok ? __builtin_nontemporal_load(a + idx) : 0.f;
+                vx[u] = ok ? p.x[idx] : 0.f;
+            }
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int u = 0; u < kUnroll; ++u) acc += va[u] * p.x[c + u * 64 + lane];
-        }
-        for (; c < p.N; c += 64) {
-            const int idx = c + lane;
-            if (idx < p.N) acc += a[idx] * p.x[idx];
+            for (int u = 0; u < kPieces; ++u) acc += va[u] * vx[u];
         }
     }
     acc = wave_sum(acc);
@@ -102,12 +137,11 @@ __global__ void zero_fill_kernel(float *p, int64_t rows, int64_t cols, int64_t l
 hipError_t gemv_launch(const GemvArgs &a, hipStream_t stream)
 {
     const bool vec = (a.N % 4 == 0) && ((uintptr_t)a.A % 16 == 0) && ((uintptr_t)a.x % 16 == 0);
-    const unsigned blocks = (unsigned)((a.M + kRowsPerBlock - 1) / kRowsPerBlock);
     GemvArgs arg = a;
     void *args[] = {&arg};
     const void *fn = vec ? reinterpret_cast<const void *>(&gemv_f32_kernel<true>)
                          : reinterpret_cast<const void *>(&gemv_f32_kernel<false>);
-    return hipLaunchKernel(fn, dim3(blocks), dim3(kGemvThreads), args, 0, stream);
+    return hipLaunchKernel(fn, dim3((unsigned)a.M), dim3(64), args, 0, stream);
 }
 
 hipError_t zero_fill_launch(float *ptr, int64_t rows, int64_t cols, int64_t ld, hipStream_t stream)
