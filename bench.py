@@ -20,6 +20,13 @@ own time on a bounded sample of the same work is reported as `cpu_baseline`.
 Profiling helpers (same script, for rocprofv3 runs): --only gemm | gemv | copy
 runs just that kernel `--steps` times with no oracle; `copy` is a plain
 device-to-device copy of known size used to calibrate HBM counters.
+
+Sweeps (tables, not the benchmark line): --sweep gemm times every GEMM tile
+configuration on the workload shapes and a few others; --sweep gemv times the GEMV
+at N = 4096 for growing M, which separates its per-launch fixed cost from its
+streaming rate. Both time a run of back-to-back launches between two events on
+the launch stream (for the GEMV this agrees with rocprofv3's kernel durations;
+kernels much shorter than ~5 us are bounded by the host's launch rate instead).
 """
 import argparse
 import hashlib
@@ -104,6 +111,8 @@ def main():
                     help="target length of the oracle's timed sample")
     ap.add_argument("--only", choices=["gemm", "gemv", "copy"], default=None,
                     help="profiling helper: launch only this kernel --steps times")
+    ap.add_argument("--sweep", choices=["gemm", "gemv"], default=None,
+                    help="print a timing table instead of the benchmark line")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -120,6 +129,10 @@ def main():
     torch.cuda.set_device(dev)
     mm.load()
     stream = torch.cuda.current_stream()
+
+    if args.sweep:
+        sweep(args.sweep, torch, mm, dev)
+        return
 
     wg = wl.WORKLOADS["gemm_proj"]
     wv = wl.WORKLOADS["gemv4096"]
@@ -319,6 +332,92 @@ def main():
     if not result["verified"]:
         log(f"VERIFICATION FAILED: gemm {gemm_check}; gemv ok={gemv_ok}")
         sys.exit(1)
+
+
+def burst_time_ms(torch, launch, reps):
+    """Average time per launch over `reps` back-to-back launches on the current
+    stream, between two events, after one untimed pass."""
+    stream = torch.cuda.current_stream()
+    for i in range(reps):
+        launch(i, stream)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(reps):
+        launch(i, stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def sweep(kind, torch, mm, dev):
+    if kind == "gemm":
+        shapes = [(w.M, w.N, w.K, w.name) for w in wl.WORKLOADS.values() if w.op == "gemm"]
+        shapes += [(512, 512, 512, ""), (2048, 2048, 2048, ""), (4096, 4096, 4096, ""),
+                   (8192, 1792, 4096, "projection, 1/8 of N")]
+        nc = mm.mm_gemm_f32_num_configs()
+        print("# fp32 GEMM, TFLOP/s per tile configuration (back-to-back launches between two "
+              "events, inputs N(0,1))")
+        for c in range(nc):
+            print(f"#   cfg {c}: {mm.mm_gemm_f32_config_name(c)}")
+        print("#   * = the configuration mm_gemm_f32 selects for the shape")
+        print(f"{'M':>6s} {'N':>6s} {'K':>6s}  " + " ".join(f"{'cfg' + str(c):>8s}" for c in range(nc))
+              + "  workload")
+        for M, N, K, name in shapes:
+            A = torch.randn(M, K, device=dev)
+            B = torch.randn(K, N, device=dev)
+            C = torch.empty(M, N, device=dev)
+            flop = rl.gemm_flops(M, N, K)
+            reps = max(3, min(200, int(2e11 / flop)))
+            sel = mm.mm_gemm_f32_select(M, N, K)
+            cells = []
+            for c in range(nc):
+                def launch(i, st, c=c):
+                    mm.mm_gemm_f32_config(c, M, N, K, A, K, B, N, C, N, st)
+                ms = burst_time_ms(torch, launch, reps)
+                cells.append(f"{flop / ms / 1e9:7.1f}" + ("*" if c == sel else " "))
+            print(f"{M:6d} {N:6d} {K:6d}  " + " ".join(cells) + f"  {name}", flush=True)
+            del A, B, C
+    else:
+        VN = 4096
+        print("# fp32 GEMV y = A x, N = 4096: time per launch vs M (back-to-back launches "
+              "between two events)")
+        print("#   cold: the launches rotate over matrices totalling >= 512 MiB (more than the "
+              "256 MB Infinity Cache); warm: one matrix, launched repeatedly")
+        print(f"{'M':>7s} {'MiB':>7s} {'cold_us':>9s} {'cold_GB/s':>10s} {'warm_us':>9s} "
+              f"{'warm_GB/s':>10s}")
+        rows = []
+        for VM in (256, 512, 1024, 2048, 4096, 8192, 16384, 32768):
+            sets = max(2, min(16, (512 << 20) // (VM * VN * 4)))
+            As = [torch.rand(VM, VN, device=dev) for _ in range(sets)]
+            xs = [torch.rand(VN, device=dev) for _ in range(sets)]
+            ys = [torch.empty(VM, device=dev) for _ in range(sets)]
+            reps = 8 * sets if VM >= 4096 else 200
+
+            def cold(i, st):
+                k = i % sets
+                mm.mm_gemv_f32(VM, VN, As[k], xs[k], ys[k], st)
+
+            def warm(i, st):
+                mm.mm_gemv_f32(VM, VN, As[0], xs[0], ys[0], st)
+            by = rl.gemv_algorithmic_bytes(VM, VN)
+            tc = burst_time_ms(torch, cold, reps)
+            tw = burst_time_ms(torch, warm, reps)
+            rows.append((VM, by, tc))
+            print(f"{VM:7d} {VM * VN * 4 / 2**20:7.0f} {tc * 1e3:9.2f} {by / tc / 1e6:10.0f} "
+                  f"{tw * 1e3:9.2f} {by / tw / 1e6:10.0f}", flush=True)
+            del As, xs, ys
+        # least-squares line t = t0 + bytes / rate over the cold points with M >= 2048
+        pts = [(b, t) for (m, b, t) in rows if m >= 2048]
+        n = len(pts)
+        mb = sum(b for b, _ in pts) / n
+        mt = sum(t for _, t in pts) / n
+        slope = sum((b - mb) * (t - mt) for b, t in pts) / sum((b - mb) ** 2 for b, _ in pts)
+        t0 = mt - slope * mb                    # ms
+        rate = 1e3 / slope                      # bytes per second
+        print(f"# cold fit over M >= 2048: fixed {t0 * 1e3:.2f} us per launch + streaming at "
+              f"{rate / 1e9:.0f} GB/s ({100 * rate / rl.MI355X_HBM_PEAK:.1f}% of 8 TB/s)")
 
 
 if __name__ == "__main__":

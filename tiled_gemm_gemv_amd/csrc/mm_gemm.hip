@@ -42,12 +42,18 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kXcds = 8;  // MI355X deals consecutive workgroups to 8 XCDs in turn
 
-template <int BM_, int BN_, int BK_, int WM_, int WN_, int GROUP_M_>
+// PF_: how many K-steps ahead the HBM loads run (1 or 2). With 2, a second set of
+// staging registers lets a request overlap two K-steps of MFMAs instead of one.
+// KS_: waves that share each WM x WN output block. Each takes 1/KS of every K-step's
+// k range; at the end the partial sums meet in LDS and are added in a fixed order.
+// It puts more waves on each SIMD when C has few tiles, with no memory beyond C.
+template <int BM_, int BN_, int BK_, int WM_, int WN_, int GROUP_M_, int PF_ = 1, int KS_ = 1>
 struct Tile {
     static constexpr int BM = BM_, BN = BN_, BK = BK_, WM = WM_, WN = WN_;
-    static constexpr int GROUP_M = GROUP_M_;
+    static constexpr int GROUP_M = GROUP_M_, PF = PF_, KS = KS_;
     static constexpr int WAVES_M = BM / WM, WAVES_N = BN / WN;
-    static constexpr int NT = WAVES_M * WAVES_N * 64;
+    static constexpr int WAVES_MN = WAVES_M * WAVES_N;
+    static constexpr int NT = WAVES_MN * KS * 64;
     static constexpr int FM = WM / 32, FN = WN / 32;  // 32 x 32 accumulator blocks per wave
     static constexpr int PITCH = BK + 4;               // LDS row pitch, floats
     static constexpr int A_TILE = BM * PITCH;
@@ -61,6 +67,15 @@ struct Tile {
     static_assert(BM % WM == 0 && BN % WN == 0 && WM % 32 == 0 && WN % 32 == 0, "tile shape");
     static_assert(BK % 8 == 0, "BK must be a multiple of 8");
     static_assert(2 * STAGE * 4 <= 160 * 1024, "two stages must fit the 160 KB LDS");
+    static_assert(PF == 1 || PF == 2, "prefetch depth 1 or 2");
+    static_assert((BK / 8) % KS == 0, "each k share must be whole 4-step groups");
+    static_assert(KS == 1 || (KS - 1) * BM * BN <= 2 * STAGE, "partial sums must fit the LDS");
+    static_assert(NT <= 1024, "at most 1024 threads per workgroup");
+    // One K-step's worth of a thread's staged HBM data.
+    struct Staged {
+        f32x4 a[A_PER_T];     // one 16-byte piece of an A row each
+        f32x4 b[B_PER_T][4];  // 4 k-rows x 4 columns of B each
+    };
 };
 
 // 4 consecutive floats at p (in range).
@@ -120,8 +135,10 @@ __global__ __launch_bounds__(T::NT) void gemm_f32_kernel(GemmArgs p)
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
-    const int wm0 = (wave / T::WAVES_N) * T::WM;
-    const int wn0 = (wave % T::WAVES_N) * T::WN;
+    const int ks = wave / T::WAVES_MN;              // which share of each K-step
+    const int wmn = wave % T::WAVES_MN;             // which output block
+    const int wm0 = (wmn / T::WAVES_N) * T::WM;
+    const int wn0 = (wmn % T::WAVES_N) * T::WN;
     const bool inner_mn = (m0 + T::BM <= p.M) && (n0 + T::BN <= p.N);
     const int nk = (p.K + T::BK - 1) / T::BK;
 
@@ -133,13 +150,12 @@ __global__ __launch_bounds__(T::NT) void gemm_f32_kernel(GemmArgs p)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-    f32x4 ra[T::A_PER_T];     // staged A: one 16-byte piece of a row each
-    f32x4 rb[T::B_PER_T][4];  // staged B: 4 k-rows x 4 columns each
+    typename T::Staged r0, r1;
 
     // HBM -> registers for K-step kt. Piece c of thread tid is index tid + c * NT.
     // A piece: row idx / KQ, k-group idx % KQ (a row's pieces are adjacent lanes).
     // B piece: k-group idx % KQ, column group idx / KQ.
-    auto global_load = [&](int kt) {
+    auto global_load = [&](int kt, typename T::Staged &st) {
         const int k0 = kt * T::BK;
         const bool full = inner_mn && (k0 + T::BK <= p.K);
 #pragma unroll
@@ -149,10 +165,10 @@ __global__ __launch_bounds__(T::NT) void gemm_f32_kernel(GemmArgs p)
                 const int row = idx / T::KQ, kg = idx % T::KQ;
                 const int gm = m0 + row, gk = k0 + 4 * kg;
                 if (full) {
-                    ra[c] = load4<VEC_A>(p.A + (int64_t)gm * p.lda + gk);
+                    st.a[c] = load4<VEC_A>(p.A + (int64_t)gm * p.lda + gk);
                 } else {
                     const int valid = (gm < p.M) ? p.K - gk : 0;
-                    ra[c] = load4_masked<VEC_A>(p.A + (int64_t)gm * p.lda + gk, valid);
+                    st.a[c] = load4_masked<VEC_A>(p.A + (int64_t)gm * p.lda + gk, valid);
                 }
             }
         }
@@ -166,10 +182,10 @@ __global__ __launch_bounds__(T::NT) void gemm_f32_kernel(GemmArgs p)
                 for (int r = 0; r < 4; ++r) {
                     const int gk = k0 + 4 * kg + r;
                     if (full) {
-                        rb[c][r] = load4<VEC_B>(p.B + (int64_t)gk * p.ldb + gn);
+                        st.b[c][r] = load4<VEC_B>(p.B + (int64_t)gk * p.ldb + gn);
                     } else {
                         const int valid = (gk < p.K) ? p.N - gn : 0;
-                        rb[c][r] = load4_masked<VEC_B>(p.B + (int64_t)gk * p.ldb + gn, valid);
+                        st.b[c][r] = load4_masked<VEC_B>(p.B + (int64_t)gk * p.ldb + gn, valid);
                     }
                 }
             }
@@ -177,7 +193,7 @@ __global__ __launch_bounds__(T::NT) void gemm_f32_kernel(GemmArgs p)
     };
 
     // registers -> LDS stage `buf` (B transposed on the way in).
-    auto lds_store = [&](int buf) {
+    auto lds_store = [&](int buf, const typename T::Staged &st) {
         float *As = lds + buf * T::STAGE;
         float *Bs = As + T::A_TILE;
 #pragma unroll
@@ -185,7 +201,7 @@ __global__ __launch_bounds__(T::NT) void gemm_f32_kernel(GemmArgs p)
             const int idx = tid + c * T::NT;
             if (T::A_CHUNKS % T::NT == 0 || idx < T::A_CHUNKS) {
                 const int row = idx / T::KQ, kg = idx % T::KQ;
-                *reinterpret_cast<f32x4 *>(As + row * T::PITCH + 4 * kg) = ra[c];
+                *reinterpret_cast<f32x4 *>(As + row * T::PITCH + 4 * kg) = st.a[c];
             }
         }
 #pragma unroll
@@ -195,51 +211,121 @@ __global__ __launch_bounds__(T::NT) void gemm_f32_kernel(GemmArgs p)
                 const int kg = idx % T::KQ, ng = idx / T::KQ;
 #pragma unroll
                 for (int col = 0; col < 4; ++col) {
-                    const f32x4 v = {rb[c][0][col], rb[c][1][col], rb[c][2][col], rb[c][3][col]};
+                    const f32x4 v = {st.b[c][0][col], st.b[c][1][col], st.b[c][2][col],
+                                     st.b[c][3][col]};
                     *reinterpret_cast<f32x4 *>(Bs + (4 * ng + col) * T::PITCH + 4 * kg) = v;
                 }
             }
         }
     };
 
-    // One K-step on LDS stage `buf`.
-    auto multiply = [&](int buf) {
-        const int half = (lane >> 5) * (T::BK / 2);
+    // One K-step on LDS stage `buf`: this wave's share of its 4-step groups.
+    // `mid` runs halfway through the MFMA stream (used to write the next stage).
+    auto multiply = [&](int buf, auto &&mid) {
+        constexpr int QS = T::BK / 8 / T::KS;
+        const int half = (lane >> 5) * (T::BK / 2) + ks * QS * 4;
         const float *As = lds + buf * T::STAGE + (wm0 + (lane & 31)) * T::PITCH + half;
         const float *Bs = lds + buf * T::STAGE + T::A_TILE + (wn0 + (lane & 31)) * T::PITCH + half;
-#pragma unroll
-        for (int q = 0; q < T::BK / 8; ++q) {
-            f32x4 a[T::FM], b[T::FN];
+        // Fragments are double-buffered: the LDS reads of 4-step group q + 1 are
+        // issued before the MFMAs of group q, so their latency hides behind MFMAs.
+        f32x4 a[2][T::FM], b[2][T::FN];
+        auto read_frags = [&](int q, f32x4 (&fa)[T::FM], f32x4 (&fb)[T::FN]) {
 #pragma unroll
             for (int i = 0; i < T::FM; ++i)
-                a[i] = *reinterpret_cast<const f32x4 *>(As + i * 32 * T::PITCH + 4 * q);
+                fa[i] = *reinterpret_cast<const f32x4 *>(As + i * 32 * T::PITCH + 4 * q);
 #pragma unroll
             for (int j = 0; j < T::FN; ++j)
-                b[j] = *reinterpret_cast<const f32x4 *>(Bs + j * 32 * T::PITCH + 4 * q);
+                fb[j] = *reinterpret_cast<const f32x4 *>(Bs + j * 32 * T::PITCH + 4 * q);
+        };
+        read_frags(0, a[0], b[0]);
+#pragma unroll
+        for (int q = 0; q < QS; ++q) {
+            if (q + 1 < QS) read_frags(q + 1, a[(q + 1) & 1], b[(q + 1) & 1]);
+            if (q == QS / 2) mid();
+            // keep those reads ahead of this group's MFMAs (the scheduler would
+            // otherwise sink them next to their use)
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int s = 0; s < 4; ++s)
 #pragma unroll
                 for (int i = 0; i < T::FM; ++i)
 #pragma unroll
                     for (int j = 0; j < T::FN; ++j)
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[i][s], b[j][s],
-                                                                         acc[i][j], 0, 0, 0);
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(
+                            a[q & 1][i][s], b[q & 1][j][s], acc[i][j], 0, 0, 0);
         }
     };
 
-    if (nk > 0) {
-        global_load(0);
-        lds_store(0);
+    auto nothing = [] {};
+    if constexpr (T::PF == 1) {
+        if (nk > 0) {
+            global_load(0, r0);
+            lds_store(0, r0);
+            __syncthreads();
+        }
+        for (int kt = 0; kt < nk; ++kt) {
+            const int cur = kt & 1;
+            if (kt + 1 < nk) global_load(kt + 1, r0);
+            multiply(cur, nothing);
+            // The other stage was last read in step kt - 1, which every wave
+            // finished before the barrier that ended that step.
+            if (kt + 1 < nk) lds_store(cur ^ 1, r0);
+            __syncthreads();
+        }
+    } else {
+        // Two staging buffers. At the top of an even step kt, r0 is free and r1
+        // holds step kt + 1; the loads for step kt + 2 go to r0. Step kt + 1's
+        // data, requested a whole K-step earlier, is written to the other LDS
+        // stage halfway through step kt's MFMAs (that stage was last read in step
+        // kt - 1, before the barrier that ended it), so a K-step ends with just
+        // the barrier. The loop is unrolled by two so that each buffer is a fixed
+        // set of registers.
+        if (nk > 0) {
+            global_load(0, r0);
+            lds_store(0, r0);
+        }
+        if (nk > 1) global_load(1, r1);
         __syncthreads();
+        int kt = 0;
+        for (; kt + 1 < nk; kt += 2) {
+            if (kt + 2 < nk) global_load(kt + 2, r0);
+            multiply(0, [&] { lds_store(1, r1); });
+            __syncthreads();
+            if (kt + 3 < nk) global_load(kt + 3, r1);
+            multiply(1, [&] {
+                if (kt + 2 < nk) lds_store(0, r0);
+            });
+            __syncthreads();
+        }
+        if (kt < nk) multiply(0, nothing);  // odd number of K-steps: the last one is in stage 0
     }
-    for (int kt = 0; kt < nk; ++kt) {
-        const int cur = kt & 1;
-        if (kt + 1 < nk) global_load(kt + 1);
-        multiply(cur);
-        // The other stage was last read in step kt - 1, which every wave finished
-        // before the barrier that ended that step.
-        if (kt + 1 < nk) lds_store(cur ^ 1);
+
+    if constexpr (T::KS > 1) {
+        // Waves of shares 1..KS-1 park their sums in LDS (reused: every wave is past
+        // its last LDS read after this barrier); share 0 adds them in share order.
+        constexpr int BLOCK = T::FM * T::FN * 16 * 64;  // floats per wave's sums
         __syncthreads();
+        if (ks > 0) {
+            float *dst = lds + ((ks - 1) * T::WAVES_MN + wmn) * BLOCK + lane;
+#pragma unroll
+            for (int i = 0; i < T::FM; ++i)
+#pragma unroll
+                for (int j = 0; j < T::FN; ++j)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) dst[((i * T::FN + j) * 16 + r) * 64] = acc[i][j][r];
+        }
+        __syncthreads();
+        if (ks > 0) return;  // no barrier follows
+#pragma unroll 1
+        for (int g = 1; g < T::KS; ++g) {
+            const float *src = lds + ((g - 1) * T::WAVES_MN + wmn) * BLOCK + lane;
+#pragma unroll
+            for (int i = 0; i < T::FM; ++i)
+#pragma unroll
+                for (int j = 0; j < T::FN; ++j)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) acc[i][j][r] += src[((i * T::FN + j) * 16 + r) * 64];
+        }
     }
 
     // Accumulator block layout of v_mfma_f32_32x32x2_f32: lane l, register r holds
@@ -280,9 +366,12 @@ hipError_t launch_tile(const GemmArgs &a, hipStream_t stream)
     return hipLaunchKernel(fn, dim3((unsigned)tiles), dim3(T::NT), args, 0, stream);
 }
 
-using TileL = Tile<256, 256, 32, 128, 64, 8>;
-using TileM = Tile<128, 128, 32, 64, 64, 8>;
-using TileS = Tile<64, 64, 32, 32, 32, 8>;
+using T256x256k32 = Tile<256, 256, 32, 128, 64, 8>;
+using T128x128k32p2 = Tile<128, 128, 32, 64, 64, 8, 2>;
+using T128x128k32s2 = Tile<128, 128, 32, 64, 64, 8, 1, 2>;
+using T64x64k64p2 = Tile<64, 64, 64, 32, 32, 8, 2>;
+using T64x64k64p2s2 = Tile<64, 64, 64, 32, 32, 8, 2, 2>;
+using T128x64k64s2 = Tile<128, 64, 64, 64, 32, 8, 1, 2>;
 
 struct ConfigEntry {
     const char *name;
@@ -290,10 +379,14 @@ struct ConfigEntry {
     int bm, bn;
 };
 
+// name: BMxBNxBK, wave tile, prefetch depth, waves per output block (K split).
 const ConfigEntry kConfigs[] = {
-    {"256x256x32 w128x64 (8 waves)", &launch_tile<TileL>, 256, 256},
-    {"128x128x32 w64x64 (4 waves)", &launch_tile<TileM>, 128, 128},
-    {"64x64x32 w32x32 (4 waves)", &launch_tile<TileS>, 64, 64},
+    {"256x256x32 w128x64 pf1 ks1 (8 waves)", &launch_tile<T256x256k32>, 256, 256},
+    {"128x128x32 w64x64 pf2 ks1 (4 waves)", &launch_tile<T128x128k32p2>, 128, 128},
+    {"128x128x32 w64x64 pf1 ks2 (8 waves)", &launch_tile<T128x128k32s2>, 128, 128},
+    {"64x64x64 w32x32 pf2 ks1 (4 waves)", &launch_tile<T64x64k64p2>, 64, 64},
+    {"64x64x64 w32x32 pf2 ks2 (8 waves)", &launch_tile<T64x64k64p2s2>, 64, 64},
+    {"128x64x64 w64x32 pf1 ks2 (8 waves)", &launch_tile<T128x64k64s2>, 128, 64},
 };
 constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
 
@@ -312,14 +405,15 @@ const char *gemm_config_name(int cfg)
     return (cfg >= 0 && cfg < kNumConfigs) ? kConfigs[cfg].name : nullptr;
 }
 
-// Largest tile that still gives every one of the 256 CUs work: a big tile reuses
+// Largest tile that still gives most of the 256 CUs a tile: a big tile reuses
 // each staged element more often, a small one fills the chip on small shapes.
+// (Thresholds from a rocprofv3-timed sweep of every config over 128^3 .. 8192^2.)
 int gemm_select_config(int64_t M, int64_t N, int64_t K)
 {
     (void)K;
-    if (tiles_for(0, M, N) >= 512) return 0;
-    if (tiles_for(1, M, N) >= 256) return 1;
-    return 2;
+    if (tiles_for(0, M, N) >= 200) return 0;
+    if (tiles_for(1, M, N) >= 200) return 1;
+    return 4;
 }
 
 hipError_t gemm_launch(int cfg, const GemmArgs &a, hipStream_t stream)
