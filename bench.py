@@ -356,6 +356,7 @@ def sweep(kind, torch, mm, dev):
         shapes = [(w.M, w.N, w.K, w.name) for w in wl.WORKLOADS.values() if w.op == "gemm"]
         shapes += [(512, 512, 512, ""), (2048, 2048, 2048, ""), (4096, 4096, 4096, ""),
                    (8192, 1792, 4096, "projection, 1/8 of N")]
+        shapes += [(4096, n, 4096, f"FC layer 4096x4096, batch of {n}") for n in (8, 16, 32, 64)]
         nc = mm.mm_gemm_f32_num_configs()
         print("# fp32 GEMM, TFLOP/s per tile configuration (back-to-back launches between two "
               "events, inputs N(0,1))")

@@ -208,3 +208,29 @@ def test_projection_spot_rows(dev, dist):
     C64, S64 = oracle.gemm(A, B, rows=rows)
     r = verify.exact(got, C64) if dist == "int4" else verify.within_tol(got, C64, S64, REL_TOL)
     assert r, str(r)
+
+
+@pytest.mark.parametrize("N", [1, 2, 3, 7, 16, 33, 64])
+def test_fc_layer_small_batch(dev, N):
+    """The 4096 x 4096 fully-connected layer applied to N input vectors at once
+    (C = A X with X of N columns): integer inputs exact, random within tolerance,
+    in the configuration mm_gemm_f32 selects."""
+    M = K = 4096
+    A = wl.random_matrix(91, M, K, "int4")
+    X = wl.random_matrix(92 + N, K, N, "int4")
+    assert_exact(gpu_gemm(A, X, dev), A, X)
+    A = wl.random_matrix(93, M, K, "u11")
+    X = wl.random_matrix(94 + N, K, N, "u11")
+    assert_tol(gpu_gemm(A, X, dev), A, X)
+
+
+def test_small_batch_columns_equal_gemv(dev):
+    """Each column of A X equals the GEMV A x_j, exactly on integers."""
+    A = wl.random_matrix(95, 1000, 777, "int4")
+    X = wl.random_matrix(96, 777, 24, "int4")
+    Ad = to_device(A, dev)
+    C = gpu_gemm(A, X, dev)
+    for j in (0, 5, 23):
+        y = mm.gemv(Ad, to_device(np.ascontiguousarray(X[:, j]), dev))
+        torch.cuda.synchronize()
+        assert np.array_equal(C[:, j], y.cpu().numpy()), j

@@ -387,6 +387,9 @@ const ConfigEntry kConfigs[] = {
     {"64x64x64 w32x32 pf2 ks1 (4 waves)", &launch_tile<T64x64k64p2>, 64, 64},
     {"64x64x64 w32x32 pf2 ks2 (8 waves)", &launch_tile<T64x64k64p2s2>, 64, 64},
     {"128x64x64 w64x32 pf1 ks2 (8 waves)", &launch_tile<T128x64k64s2>, 128, 64},
+    {"narrow 16x64 (16x16x4 MFMA), K over 8 waves, 16/NB chunks", &gemm_skinny_launch<8, 16>, 16, 64},
+    {"narrow 16x64 (16x16x4 MFMA), K over 4 waves, 16/NB chunks", &gemm_skinny_launch<4, 16>, 16, 64},
+    {"narrow 16x64 (16x16x4 MFMA), K over 16 waves, 4/NB chunks", &gemm_skinny_launch<16, 4>, 16, 64},
 };
 constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
 
@@ -411,9 +414,11 @@ const char *gemm_config_name(int cfg)
 int gemm_select_config(int64_t M, int64_t N, int64_t K)
 {
     (void)K;
+    if (N <= 64) return 8;  // a few columns: stream A once (mm_gemm_skinny.hip)
     if (tiles_for(0, M, N) >= 200) return 0;
     if (tiles_for(1, M, N) >= 200) return 1;
-    return 4;
+    if (tiles_for(4, M, N) >= 128) return 4;
+    return 6;               // few 64 x 64 tiles: 16-row tiles fill more CUs
 }
 
 hipError_t gemm_launch(int cfg, const GemmArgs &a, hipStream_t stream)

@@ -31,6 +31,12 @@ int gemm_select_config(int64_t M, int64_t N, int64_t K);
 // Enqueue config `cfg` of the GEMM (K >= 1, M >= 1, N >= 1).
 hipError_t gemm_launch(int cfg, const GemmArgs &a, hipStream_t stream);
 
+// Narrow-C GEMM (mm_gemm_skinny.hip): 16 x 64 tiles of C, K split over W waves
+// per workgroup, L / (column blocks) 16-deep chunks per wave per round. Correct for
+// any shape.
+template <int W, int L>
+hipError_t gemm_skinny_launch(const GemmArgs &a, hipStream_t stream);
+
 // Enqueue the GEMV (M >= 1, N >= 1).
 hipError_t gemv_launch(const GemvArgs &a, hipStream_t stream);
 
