@@ -111,7 +111,7 @@ def main():
                     help="target length of the oracle's timed sample")
     ap.add_argument("--only", choices=["gemm", "gemv", "copy"], default=None,
                     help="profiling helper: launch only this kernel --steps times")
-    ap.add_argument("--sweep", choices=["gemm", "gemv"], default=None,
+    ap.add_argument("--sweep", choices=["gemm", "gemv", "h16"], default=None,
                     help="print a timing table instead of the benchmark line")
     args = ap.parse_args()
 
@@ -380,6 +380,37 @@ def sweep(kind, torch, mm, dev):
                 cells.append(f"{flop / ms / 1e9:7.1f}" + ("*" if c == sel else " "))
             print(f"{M:6d} {N:6d} {K:6d}  " + " ".join(cells) + f"  {name}", flush=True)
             del A, B, C
+    elif kind == "h16":
+        shapes = [(w.M, w.N, w.K, w.name) for w in wl.WORKLOADS.values() if w.op == "gemm"]
+        shapes += [(2048, 2048, 2048, ""), (4096, 4096, 4096, ""), (8192, 8192, 8192, "")]
+        nc = mm.mm_gemm_h16_num_configs()
+        peak = rl.MI355X_16BIT_MFMA_PEAK / 1e12
+        print("# 16-bit-input GEMM (fp32 accumulate, fp32 C), TFLOP/s per tile configuration "
+              f"(back-to-back launches between two events; dense 16-bit peak {peak:.0f} TFLOP/s)")
+        for c in range(nc):
+            print(f"#   cfg {c}: {mm.mm_gemm_h16_config_name(c)}")
+        print("#   * = the configuration mm_gemm_bf16 / mm_gemm_f16 select for the shape")
+        print(f"{'M':>6s} {'N':>6s} {'K':>6s}  fmt   " +
+              " ".join(f"{'cfg' + str(c):>8s}" for c in range(nc)) + "  best % of peak  workload")
+        for M, N, K, name in shapes:
+            for fmt, dt in (("bf16", torch.bfloat16), ("f16", torch.float16)):
+                A = torch.randn(M, K, device=dev).to(dt)
+                B = (torch.randn(K, N, device=dev) / K ** 0.5).to(dt)
+                C = torch.empty(M, N, device=dev)
+                flop = rl.gemm_flops(M, N, K)
+                reps = max(3, min(200, int(2e12 / flop)))
+                sel = mm.mm_gemm_h16_select(M, N, K)
+                fn = mm.mm_gemm_bf16_config if fmt == "bf16" else mm.mm_gemm_f16_config
+                cells, best = [], 0.0
+                for c in range(nc):
+                    def launch(i, st, c=c):
+                        fn(c, M, N, K, A, K, B, N, C, N, st)
+                    tf = flop / burst_time_ms(torch, launch, reps) / 1e9
+                    best = max(best, tf)
+                    cells.append(f"{tf:7.1f}" + ("*" if c == sel else " "))
+                print(f"{M:6d} {N:6d} {K:6d}  {fmt:5s} " + " ".join(cells) +
+                      f"  {100 * best / peak:13.1f}  {name}", flush=True)
+                del A, B, C
     else:
         VN = 4096
         print("# fp32 GEMV y = A x, N = 4096: time per launch vs M (back-to-back launches "

@@ -107,6 +107,41 @@ int mm_gemm_f32_config(int cfg, int64_t M, int64_t N, int64_t K,
                        const float *B, int64_t ldb,
                        float *C, int64_t ldc, void *stream);
 
+/*
+ * mm_gemm_bf16 / mm_gemm_f16: C = A x B with 16-bit inputs and fp32 accumulation
+ * and output ("Matrix Operations", "Performance Considerations": half precision
+ * and matrix engines). A and B hold bf16 (mm_gemm_bf16) or IEEE binary16
+ * (mm_gemm_f16) bit patterns, 2 bytes per element, row-major with leading
+ * dimensions counted in elements; C is fp32. Every product of two 16-bit values is
+ * exact in fp32, so C is the fp32 GEMM of the inputs' exact values, summed on the
+ * matrix cores in fp32.
+ * Arguments, layout, ownership, stream, zero-size cases and errors as for
+ * mm_gemm_f32, except: A and B must be 2-byte aligned (16-byte-aligned rows with
+ * leading dimensions divisible by 8 for A and 4 for B take the fast loads).
+ *   mm_gemm_h16_num_configs / mm_gemm_h16_config_name / mm_gemm_h16_select: the
+ *     tile configurations of these two calls, as for the fp32 GEMM.
+ *   mm_gemm_bf16_config / mm_gemm_f16_config: the calls with config `cfg` forced.
+ */
+int mm_gemm_bf16(int64_t M, int64_t N, int64_t K,
+                 const uint16_t *A, int64_t lda,
+                 const uint16_t *B, int64_t ldb,
+                 float *C, int64_t ldc, void *stream);
+int mm_gemm_f16(int64_t M, int64_t N, int64_t K,
+                const uint16_t *A, int64_t lda,
+                const uint16_t *B, int64_t ldb,
+                float *C, int64_t ldc, void *stream);
+int mm_gemm_h16_num_configs(void);
+const char *mm_gemm_h16_config_name(int cfg);
+int mm_gemm_h16_select(int64_t M, int64_t N, int64_t K);
+int mm_gemm_bf16_config(int cfg, int64_t M, int64_t N, int64_t K,
+                        const uint16_t *A, int64_t lda,
+                        const uint16_t *B, int64_t ldb,
+                        float *C, int64_t ldc, void *stream);
+int mm_gemm_f16_config(int cfg, int64_t M, int64_t N, int64_t K,
+                       const uint16_t *A, int64_t lda,
+                       const uint16_t *B, int64_t ldb,
+                       float *C, int64_t ldc, void *stream);
+
 /* mm_status_string: static text for a status code (never NULL). */
 const char *mm_status_string(int status);
 

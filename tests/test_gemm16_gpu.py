@@ -1,0 +1,154 @@
+"""GPU parity of the 16-bit-input GEMM (bf16 and fp16 in, fp32 accumulate and out).
+
+The inputs are drawn in fp32, rounded to the 16-bit format (round to nearest even),
+and the oracle multiplies the rounded values exactly (they are exact in fp32).
+Bars as for the fp32 GEMM: integer inputs bit-exact (every product and partial
+sum is an integer below 2^24), random inputs within 1e-5 * sum_k |A_ik B_kj|.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import verify
+import tiled_gemm_gemv_amd as mm
+import workloads as wl
+from gpu_helpers import require_gpu
+
+pytestmark = pytest.mark.gpu
+
+REL_TOL = 1e-5
+FORMATS = {
+    "bf16": (wl.to_bf16_bits, wl.bf16_bits_to_f32, torch.bfloat16),
+    "f16": (wl.to_f16_bits, wl.f16_bits_to_f32, torch.float16),
+}
+
+
+@pytest.fixture(scope="module")
+def dev():
+    d = require_gpu()
+    mm.load()
+    return d
+
+
+def n16():
+    try:
+        return mm.mm_gemm_h16_num_configs()
+    except OSError:
+        return 3
+
+
+CONFIGS = list(range(n16()))
+
+
+def quantize(a, fmt):
+    to_bits, to_f32, tdtype = FORMATS[fmt]
+    bits = to_bits(a)
+    return bits, to_f32(bits)
+
+
+def on_device(bits, fmt, dev, ld=None, offset=0):
+    """uint16 bit patterns -> a device tensor of the 16-bit dtype (optionally a view
+    with row stride ld, `offset` elements into a NaN-filled buffer)."""
+    tdtype = FORMATS[fmt][2]
+    rows, cols = bits.shape
+    t = torch.from_numpy(bits.view(np.int16)).to(dev).view(tdtype)
+    if ld is None and offset == 0:
+        return t
+    ld = ld or cols
+    buf = torch.full(((rows - 1) * ld + cols + offset + 8,), float("nan"), dtype=tdtype, device=dev)
+    view = torch.as_strided(buf, (rows, cols), (ld, 1), offset)
+    view.copy_(t)
+    return view
+
+
+def run(A, B, fmt, dev, cfg=None, lda=None, ldb=None, offs=(0, 0)):
+    Ab, Af = quantize(A, fmt)
+    Bb, Bf = quantize(B, fmt)
+    C = mm.gemm16(on_device(Ab, fmt, dev, lda, offs[0]), on_device(Bb, fmt, dev, ldb, offs[1]),
+                  config=cfg)
+    torch.cuda.synchronize()
+    return C.cpu().numpy(), Af, Bf
+
+
+@pytest.mark.parametrize("fmt", list(FORMATS))
+@pytest.mark.parametrize("cfg", CONFIGS + [None])
+@pytest.mark.parametrize("name", ["gemm128", "gemm1024", "gemm_ragged"])
+def test_workloads(dev, fmt, cfg, name):
+    w = wl.WORKLOADS[name]
+    A, B = wl.gemm_inputs(w)
+    C, Af, Bf = run(A, B, fmt, dev, cfg)
+    C64, S64 = oracle.gemm(Af, Bf)
+    r = verify.within_tol(C, C64, S64, REL_TOL)
+    assert r, str(r)
+    A, B = wl.gemm_inputs(w.with_dist("int4"))
+    C, Af, Bf = run(A, B, fmt, dev, cfg)
+    C64, _ = oracle.gemm(Af, Bf)
+    r = verify.exact(C, C64)
+    assert r, str(r)
+
+
+@pytest.mark.parametrize("fmt", list(FORMATS))
+@pytest.mark.parametrize("cfg", CONFIGS)
+def test_permutation_and_edges(dev, fmt, cfg):
+    M = K = 96
+    perm = np.random.default_rng(6).permutation(K)
+    P = np.zeros((M, K), np.float32)
+    P[np.arange(M), perm] = 1
+    B = (np.arange(K * 80, dtype=np.float32).reshape(K, 80) % 251) - 125   # exact in 16 bits
+    C, _, Bf = run(P, B, fmt, dev, cfg)
+    assert np.array_equal(C, Bf[perm])
+    rng = np.random.default_rng(200 + cfg)
+    edge = [1, 2, 3, 7, 8, 9, 31, 32, 33, 63, 64, 65, 127, 128, 129, 255, 256, 257]
+    for t in range(16):
+        M, N, K = (int(v) for v in rng.choice(edge, 3))
+        A = wl.random_matrix(3000 + t, M, K, "int4")
+        B = wl.random_matrix(4000 + t, K, N, "int4")
+        C, Af, Bf = run(A, B, fmt, dev, cfg)
+        C64, _ = oracle.gemm(Af, Bf)
+        r = verify.exact(C, C64)
+        assert r, f"{(M, N, K)}: {r}"
+
+
+@pytest.mark.parametrize("fmt", list(FORMATS))
+@pytest.mark.parametrize("cfg", CONFIGS)
+@pytest.mark.parametrize("lds,offs", [((None, None), (0, 0)), ((203, 190), (1, 3)),
+                                      ((208, 188), (0, 4))])
+def test_strided_unaligned(dev, fmt, cfg, lds, offs):
+    """Odd leading dimensions and starts off 16-byte alignment (2-byte loads), and
+    aligned ones (16- and 8-byte loads); NaN around the views must not leak in."""
+    M, N, K = 150, 181, 200
+    A = wl.random_matrix(51, M, K, "int4")
+    B = wl.random_matrix(52, K, N, "int4")
+    C, Af, Bf = run(A, B, fmt, dev, cfg, lda=lds[0], ldb=lds[1], offs=offs)
+    C64, _ = oracle.gemm(Af, Bf)
+    r = verify.exact(C, C64)
+    assert r, str(r)
+
+
+def test_k_zero(dev):
+    for fmt in FORMATS:
+        tdtype = FORMATS[fmt][2]
+        out = torch.full((5, 7), float("nan"), device=dev)
+        mm.gemm16(torch.empty((5, 0), dtype=tdtype, device=dev),
+                  torch.empty((0, 7), dtype=tdtype, device=dev), out=out)
+        torch.cuda.synchronize()
+        assert (out == 0).all().item()
+
+
+@pytest.mark.parametrize("fmt", list(FORMATS))
+def test_projection_spot_rows(dev, fmt):
+    """The 8192 x 4096 x 14336 projection with 16-bit inputs: 64 sampled rows."""
+    w = wl.WORKLOADS["gemm_proj"]
+    A, B = wl.gemm_inputs(w)
+    Ab, Af = quantize(A, fmt)
+    Bb, Bf = quantize(B, fmt)
+    del A, B
+    C = mm.gemm16(on_device(Ab, fmt, dev), on_device(Bb, fmt, dev))
+    torch.cuda.synchronize()
+    rows = wl.sample_rows(w, 64)
+    got = C[torch.from_numpy(rows).to(dev)].cpu().numpy()
+    del C
+    C64, S64 = oracle.gemm(Af, Bf, rows=rows)
+    r = verify.within_tol(got, C64, S64, REL_TOL)
+    assert r, str(r)

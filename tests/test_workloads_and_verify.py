@@ -112,3 +112,18 @@ def test_tolerance_zero_magnitude_demands_zero():
 def test_checkers_reject_shape_mismatch():
     with pytest.raises(ValueError):
         verify.exact(np.zeros((2, 3), np.float32), np.zeros((3, 2)))
+
+
+def test_sixteen_bit_rounding_matches_torch():
+    """to_bf16_bits / to_f16_bits round to nearest even, as torch's CPU casts do, and
+    the bit patterns convert back to the same values exactly."""
+    import torch
+    a = np.concatenate([wl.draw(wl.rng_for(11, 0), (20000,), "normal"),
+                        np.array([1.00390625, 1.01171875, -2.5, 0.0, 65504.0, 1e-3], np.float32)])
+    t = torch.from_numpy(a)
+    bf = wl.to_bf16_bits(a)
+    assert np.array_equal(bf, t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16))
+    assert np.array_equal(wl.bf16_bits_to_f32(bf), t.to(torch.bfloat16).float().numpy())
+    h = wl.to_f16_bits(a)
+    assert np.array_equal(h, t.to(torch.float16).view(torch.int16).numpy().view(np.uint16))
+    assert np.array_equal(wl.f16_bits_to_f32(h), t.to(torch.float16).float().numpy())

@@ -67,6 +67,18 @@ def load():
     lib.mm_gemm_f32_config_name.restype = ctypes.c_char_p
     lib.mm_gemm_f32_select.argtypes = [i64, i64, i64]
     lib.mm_gemm_f32_select.restype = ci
+    for name in ("mm_gemm_bf16", "mm_gemm_f16"):
+        getattr(lib, name).argtypes = [i64, i64, i64, vp, i64, vp, i64, vp, i64, vp]
+        getattr(lib, name).restype = ci
+    for name in ("mm_gemm_bf16_config", "mm_gemm_f16_config"):
+        getattr(lib, name).argtypes = [ci, i64, i64, i64, vp, i64, vp, i64, vp, i64, vp]
+        getattr(lib, name).restype = ci
+    lib.mm_gemm_h16_num_configs.argtypes = []
+    lib.mm_gemm_h16_num_configs.restype = ci
+    lib.mm_gemm_h16_config_name.argtypes = [ci]
+    lib.mm_gemm_h16_config_name.restype = ctypes.c_char_p
+    lib.mm_gemm_h16_select.argtypes = [i64, i64, i64]
+    lib.mm_gemm_h16_select.restype = ci
     lib.mm_gemv_f32.argtypes = [i64, i64, vp, vp, vp, vp]
     lib.mm_gemv_f32.restype = ci
     lib.mm_status_string.argtypes = [ci]
@@ -122,6 +134,45 @@ def mm_gemm_f32_config(cfg, M, N, K, A, lda, B, ldb, C, ldc, stream=None):
                                   _stream(stream)), "mm_gemm_f32_config")
 
 
+def mm_gemm_bf16(M, N, K, A, lda, B, ldb, C, ldc, stream=None):
+    """C (fp32) = A x B with bf16 A and B. Raises MMError."""
+    lib = load()
+    _check(lib.mm_gemm_bf16(M, N, K, _addr(A), lda, _addr(B), ldb, _addr(C), ldc,
+                            _stream(stream)), "mm_gemm_bf16")
+
+
+def mm_gemm_f16(M, N, K, A, lda, B, ldb, C, ldc, stream=None):
+    """C (fp32) = A x B with fp16 A and B. Raises MMError."""
+    lib = load()
+    _check(lib.mm_gemm_f16(M, N, K, _addr(A), lda, _addr(B), ldb, _addr(C), ldc,
+                           _stream(stream)), "mm_gemm_f16")
+
+
+def mm_gemm_bf16_config(cfg, M, N, K, A, lda, B, ldb, C, ldc, stream=None):
+    lib = load()
+    _check(lib.mm_gemm_bf16_config(cfg, M, N, K, _addr(A), lda, _addr(B), ldb, _addr(C), ldc,
+                                   _stream(stream)), "mm_gemm_bf16_config")
+
+
+def mm_gemm_f16_config(cfg, M, N, K, A, lda, B, ldb, C, ldc, stream=None):
+    lib = load()
+    _check(lib.mm_gemm_f16_config(cfg, M, N, K, _addr(A), lda, _addr(B), ldb, _addr(C), ldc,
+                                  _stream(stream)), "mm_gemm_f16_config")
+
+
+def mm_gemm_h16_num_configs():
+    return load().mm_gemm_h16_num_configs()
+
+
+def mm_gemm_h16_config_name(cfg):
+    name = load().mm_gemm_h16_config_name(cfg)
+    return name.decode() if name is not None else None
+
+
+def mm_gemm_h16_select(M, N, K):
+    return load().mm_gemm_h16_select(M, N, K)
+
+
 def mm_gemv_f32(M, N, A, x, y, stream=None):
     """y = A x (A M x N with packed rows). Raises MMError."""
     lib = load()
@@ -151,12 +202,13 @@ def mm_last_error():
 
 # ----------------------------------------------------- torch-tensor front ends
 
-def _matrix(t, name):
+def _matrix(t, name, dtypes=None):
     import torch
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
-    if t.dtype != torch.float32:
-        raise TypeError(f"{name} must be float32, got {t.dtype}")
+    dtypes = dtypes or (torch.float32,)
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name} must be one of {dtypes}, got {t.dtype}")
     if t.device.type != "cuda":
         raise ValueError(f"{name} must be on the GPU, got {t.device}")
     if t.dim() != 2:
@@ -191,6 +243,32 @@ def gemm(A, B, out=None, config=None, stream=None):
             mm_gemm_f32(M, N, K, A, lda, B, ldb, out, ldc, stream)
         else:
             mm_gemm_f32_config(config, M, N, K, A, lda, B, ldb, out, ldc, stream)
+    return out
+
+
+def gemm16(A, B, out=None, config=None, stream=None):
+    """out (fp32) = A @ B for bf16 or fp16 GPU tensors A and B of the same dtype."""
+    import torch
+    lda = _matrix(A, "A", (torch.bfloat16, torch.float16))
+    ldb = _matrix(B, "B", (A.dtype,))
+    M, K = A.shape
+    K2, N = B.shape
+    if K2 != K:
+        raise ValueError(f"inner dimensions differ: {tuple(A.shape)} x {tuple(B.shape)}")
+    if B.device != A.device:
+        raise ValueError("A and B are on different devices")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=A.device)
+    if tuple(out.shape) != (M, N):
+        raise ValueError(f"out has shape {tuple(out.shape)}, expected {(M, N)}")
+    ldc = _matrix(out, "out")
+    bf = A.dtype == torch.bfloat16
+    with torch.cuda.device(A.device):
+        if config is None:
+            (mm_gemm_bf16 if bf else mm_gemm_f16)(M, N, K, A, lda, B, ldb, out, ldc, stream)
+        else:
+            (mm_gemm_bf16_config if bf else mm_gemm_f16_config)(config, M, N, K, A, lda, B, ldb,
+                                                                 out, ldc, stream)
     return out
 
 

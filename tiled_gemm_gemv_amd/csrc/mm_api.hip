@@ -45,8 +45,9 @@ bool extent_fits(int64_t rows, int64_t cols, int64_t ld)
     return true;
 }
 
-int check_gemm(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda, const float *B,
-               int64_t ldb, const float *C, int64_t ldc)
+// elem: bytes per element of A and B (4 for fp32, 2 for the 16-bit formats).
+int check_gemm(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, const void *B,
+               int64_t ldb, const float *C, int64_t ldc, int elem = 4)
 {
     if (M < 0 || N < 0 || K < 0) return invalid("negative size");
     if (M > kMaxDim || N > kMaxDim || K > kMaxDim) return invalid("size above 2^31 - 1");
@@ -56,6 +57,8 @@ int check_gemm(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda, con
     if (M > 0 && K > 0 && !A) return invalid("A is NULL");
     if (K > 0 && N > 0 && !B) return invalid("B is NULL");
     if (M > 0 && N > 0 && !C) return invalid("C is NULL");
+    if ((uintptr_t)A % elem || (uintptr_t)B % elem || (uintptr_t)C % 4)
+        return invalid("pointer not aligned to its element size");
     if (M > 0 && K > 0 && !extent_fits(M, K, lda)) return invalid("A extent overflows");
     if (K > 0 && N > 0 && !extent_fits(K, N, ldb)) return invalid("B extent overflows");
     if (M > 0 && N > 0 && !extent_fits(M, N, ldc)) return invalid("C extent overflows");
@@ -82,6 +85,19 @@ int run_gemm(int cfg, int64_t M, int64_t N, int64_t K, const float *A, int64_t l
     a.K = (int)K;
     if (cfg < 0) cfg = mm::gemm_select_config(M, N, K);
     return from_hip("gemm launch", mm::gemm_launch(cfg, a, s));
+}
+
+int run_gemm16(int cfg, bool bf16, int64_t M, int64_t N, int64_t K, const uint16_t *A,
+               int64_t lda, const uint16_t *B, int64_t ldb, float *C, int64_t ldc, void *stream)
+{
+    const int st = check_gemm(M, N, K, A, lda, B, ldb, C, ldc, 2);
+    if (st != MM_OK) return st;
+    if (M == 0 || N == 0) return MM_OK;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (K == 0) return from_hip("zero fill launch", mm::zero_fill_launch(C, M, N, ldc, s));
+    if (cfg < 0) cfg = mm::gemm16_select_config(M, N, K);
+    return from_hip("gemm16 launch", mm::gemm16_launch(cfg, bf16, A, lda, B, ldb, C, ldc, (int)M,
+                                                       (int)N, (int)K, s));
 }
 
 }  // namespace
@@ -111,6 +127,42 @@ int mm_gemm_f32_select(int64_t M, int64_t N, int64_t K)
     return mm::gemm_select_config(M, N, K);
 }
 
+int mm_gemm_bf16(int64_t M, int64_t N, int64_t K, const uint16_t *A, int64_t lda,
+                 const uint16_t *B, int64_t ldb, float *C, int64_t ldc, void *stream)
+{
+    return run_gemm16(-1, true, M, N, K, A, lda, B, ldb, C, ldc, stream);
+}
+
+int mm_gemm_f16(int64_t M, int64_t N, int64_t K, const uint16_t *A, int64_t lda,
+                const uint16_t *B, int64_t ldb, float *C, int64_t ldc, void *stream)
+{
+    return run_gemm16(-1, false, M, N, K, A, lda, B, ldb, C, ldc, stream);
+}
+
+int mm_gemm_bf16_config(int cfg, int64_t M, int64_t N, int64_t K, const uint16_t *A, int64_t lda,
+                        const uint16_t *B, int64_t ldb, float *C, int64_t ldc, void *stream)
+{
+    if (cfg < 0 || cfg >= mm::gemm16_num_configs()) return invalid("config index out of range");
+    return run_gemm16(cfg, true, M, N, K, A, lda, B, ldb, C, ldc, stream);
+}
+
+int mm_gemm_f16_config(int cfg, int64_t M, int64_t N, int64_t K, const uint16_t *A, int64_t lda,
+                       const uint16_t *B, int64_t ldb, float *C, int64_t ldc, void *stream)
+{
+    if (cfg < 0 || cfg >= mm::gemm16_num_configs()) return invalid("config index out of range");
+    return run_gemm16(cfg, false, M, N, K, A, lda, B, ldb, C, ldc, stream);
+}
+
+int mm_gemm_h16_num_configs(void) { return mm::gemm16_num_configs(); }
+
+const char *mm_gemm_h16_config_name(int cfg) { return mm::gemm16_config_name(cfg); }
+
+int mm_gemm_h16_select(int64_t M, int64_t N, int64_t K)
+{
+    if (M < 0 || N < 0 || K < 0) return 0;
+    return mm::gemm16_select_config(M, N, K);
+}
+
 int mm_gemv_f32(int64_t M, int64_t N, const float *A, const float *x, float *y, void *stream)
 {
     if (M < 0 || N < 0) return invalid("negative size");
@@ -118,6 +170,8 @@ int mm_gemv_f32(int64_t M, int64_t N, const float *A, const float *x, float *y, 
     if (M > 0 && N > 0 && !A) return invalid("A is NULL");
     if (N > 0 && !x) return invalid("x is NULL");
     if (M > 0 && !y) return invalid("y is NULL");
+    if ((uintptr_t)A % 4 || (uintptr_t)x % 4 || (uintptr_t)y % 4)
+        return invalid("pointer not aligned to its element size");
     if (M > 0 && N > 0 && !extent_fits(M, N, N)) return invalid("A extent overflows");
     if (M == 0) return MM_OK;
     hipStream_t s = static_cast<hipStream_t>(stream);

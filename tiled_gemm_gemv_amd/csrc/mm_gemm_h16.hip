@@ -1,0 +1,352 @@
+// mm_gemm_h16.hip -- GEMM with 16-bit inputs (bf16 or fp16) and fp32 accumulation:
+// C = A x B with A and B in a 16-bit format and C in fp32.
+//
+// "Matrix Operations" (docs.vulkan.org ML-inference tutorial, "Performance
+// Considerations / Data Types") notes that half precision can run twice as fast as
+// fp32 where the hardware supports it, and ("Specialized Hardware") that matrix
+// engines go further. On gfx950 the dense 16-bit matrix rate is 16 times the fp32
+// one. The products of two 16-bit values are exact in fp32 (at most 22 significant
+// bits), so C is the same sum as the fp32 GEMM of the inputs' exact values, summed
+// in fp32 in a different order.
+//
+// Same scheme as the fp32 kernel (mm_gemm.hip): one workgroup per BM x BN tile of
+// C, two LDS stages, HBM loads for the next K-step in flight during the current
+// step's MFMAs, one barrier per K-step, masked loads at the edges, XCD-aware tile
+// order. Differences:
+//   * v_mfma_f32_32x32x16_{bf16,f16}: lane l supplies A[l % 32][8 (l / 32) + e] and
+//     B[8 (l / 32) + e][l % 32] for e = 0..7, i.e. one 16-byte LDS read per operand;
+//     MFMA step s of a K-step covers k = 16 s .. 16 s + 15;
+//   * BK = 64 elements (128 bytes) per K-step; LDS rows are padded by 8 elements;
+//   * B is transposed into k-contiguous LDS rows as 8 x 4 blocks of 16-bit values
+//     (each thread loads 8 rows of 4 columns, 8 bytes each, and regroups them into 4
+//     LDS rows of 8 k-values).
+#include "mm_internal.h"
+
+namespace mm {
+namespace {
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+
+constexpr int kXcds = 8;
+
+template <int BM_, int BN_, int WM_, int WN_>
+struct Tile16 {
+    static constexpr int BM = BM_, BN = BN_, BK = 64, WM = WM_, WN = WN_;
+    static constexpr int WAVES_M = BM / WM, WAVES_N = BN / WN;
+    static constexpr int NT = WAVES_M * WAVES_N * 64;
+    static constexpr int FM = WM / 32, FN = WN / 32;
+    static constexpr int PITCH = BK + 8;            // elements (144 bytes)
+    static constexpr int A_TILE = BM * PITCH;       // elements
+    static constexpr int STAGE = (BM + BN) * PITCH;
+    static constexpr int KG = BK / 8;               // 16-byte groups along k
+    static constexpr int A_CHUNKS = BM * KG;
+    static constexpr int A_PER_T = (A_CHUNKS + NT - 1) / NT;
+    static constexpr int B_BLOCKS = KG * (BN / 4);  // 8 x 4 blocks of a B panel
+    static constexpr int B_PER_T = (B_BLOCKS + NT - 1) / NT;
+    static_assert(2 * STAGE * 2 <= 160 * 1024, "two stages must fit the 160 KB LDS");
+};
+
+// 8 consecutive 16-bit values at p (in range) as 16 bytes.
+template <bool VEC>
+__device__ __forceinline__ u32x4 load8(const unsigned short *p)
+{
+    if constexpr (VEC) {
+        return *reinterpret_cast<const u32x4 *>(p);
+    } else {
+        u32x4 v;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) v[q] = (unsigned)p[2 * q] | ((unsigned)p[2 * q + 1] << 16);
+        return v;
+    }
+}
+
+// 4 consecutive 16-bit values at p (in range) as 8 bytes.
+template <bool VEC>
+__device__ __forceinline__ u32x2 load4h(const unsigned short *p)
+{
+    if constexpr (VEC) {
+        return *reinterpret_cast<const u32x2 *>(p);
+    } else {
+        return u32x2{(unsigned)p[0] | ((unsigned)p[1] << 16), (unsigned)p[2] | ((unsigned)p[3] << 16)};
+    }
+}
+
+template <bool VEC>
+__device__ __forceinline__ u32x2 load4h_masked(const unsigned short *p, int valid)
+{
+    if (valid >= 4) return load4h<VEC>(p);
+    u32x2 v = {0u, 0u};
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+        if (e < valid) v[e >> 1] |= (unsigned)p[e] << (16 * (e & 1));
+    return v;
+}
+
+// The first `valid` of 8 consecutive values at p, zeros after; nothing past them is read.
+template <bool VEC>
+__device__ __forceinline__ u32x4 load8_masked(const unsigned short *p, int valid)
+{
+    if (valid >= 8) return load8<VEC>(p);
+    u32x4 v = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+        if (e < valid) v[e >> 1] |= (unsigned)p[e] << (16 * (e & 1));
+    return v;
+}
+
+__device__ __forceinline__ void tile_of_block16(int bid, int nblocks, int tiles_m, int tiles_n,
+                                                int &tm, int &tn)
+{
+    const int q = nblocks / kXcds, r = nblocks % kXcds;
+    const int xcd = bid % kXcds, slot = bid / kXcds;
+    const int logical = (xcd < r) ? xcd * (q + 1) + slot : r * (q + 1) + (xcd - r) * q + slot;
+    constexpr int group_m = 8;
+    const int per_group = group_m * tiles_n;
+    const int g = logical / per_group;
+    const int first_m = g * group_m;
+    const int gm = min(tiles_m - first_m, group_m);
+    const int in_g = logical - g * per_group;
+    tm = first_m + in_g % gm;
+    tn = in_g / gm;
+}
+
+template <bool BF16>
+__device__ __forceinline__ f32x16 mfma16(u32x4 a, u32x4 b, f32x16 c)
+{
+    if constexpr (BF16) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                       __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+    } else {
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                      __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+    }
+}
+
+struct Gemm16Args {
+    const unsigned short *A;
+    const unsigned short *B;
+    float *C;
+    int64_t lda, ldb, ldc;
+    int M, N, K;
+};
+
+template <class T, bool BF16, bool VEC_A, bool VEC_B>
+__global__ __launch_bounds__(T::NT) void gemm_h16_kernel(Gemm16Args p)
+{
+    __shared__ __attribute__((aligned(16))) unsigned short lds[2 * T::STAGE];
+
+    const int tiles_m = (p.M + T::BM - 1) / T::BM;
+    const int tiles_n = (p.N + T::BN - 1) / T::BN;
+    int tm, tn;
+    tile_of_block16(blockIdx.x, gridDim.x, tiles_m, tiles_n, tm, tn);
+    const int m0 = tm * T::BM, n0 = tn * T::BN;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int wm0 = (wave / T::WAVES_N) * T::WM;
+    const int wn0 = (wave % T::WAVES_N) * T::WN;
+    const bool inner_mn = (m0 + T::BM <= p.M) && (n0 + T::BN <= p.N);
+    const int nk = (p.K + T::BK - 1) / T::BK;
+
+    f32x16 acc[T::FM][T::FN];
+#pragma unroll
+    for (int i = 0; i < T::FM; ++i)
+#pragma unroll
+        for (int j = 0; j < T::FN; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+    u32x4 ra[T::A_PER_T];
+    u32x2 rb[T::B_PER_T][8];  // 8 k-rows x 4 columns each
+
+    auto global_load = [&](int kt) {
+        const int k0 = kt * T::BK;
+        const bool full = inner_mn && (k0 + T::BK <= p.K);
+#pragma unroll
+        for (int c = 0; c < T::A_PER_T; ++c) {
+            const int idx = tid + c * T::NT;
+            if (T::A_CHUNKS % T::NT == 0 || idx < T::A_CHUNKS) {
+                const int row = idx / T::KG, kg = idx % T::KG;
+                const int gm = m0 + row, gk = k0 + 8 * kg;
+                const unsigned short *src = p.A + (int64_t)gm * p.lda + gk;
+                ra[c] = full ? load8<VEC_A>(src) : load8_masked<VEC_A>(src, gm < p.M ? p.K - gk : 0);
+            }
+        }
+#pragma unroll
+        for (int c = 0; c < T::B_PER_T; ++c) {
+            const int idx = tid + c * T::NT;
+            if (T::B_BLOCKS % T::NT == 0 || idx < T::B_BLOCKS) {
+                const int kg = idx % T::KG, ng = idx / T::KG;
+                const int gn = n0 + 4 * ng;
+#pragma unroll
+                for (int r = 0; r < 8; ++r) {
+                    const int gk = k0 + 8 * kg + r;
+                    const unsigned short *src = p.B + (int64_t)gk * p.ldb + gn;
+                    rb[c][r] = full ? load4h<VEC_B>(src)
+                                    : load4h_masked<VEC_B>(src, gk < p.K ? p.N - gn : 0);
+                }
+            }
+        }
+    };
+
+    auto lds_store = [&](int buf) {
+        unsigned short *As = lds + buf * T::STAGE;
+        unsigned short *Bs = As + T::A_TILE;
+#pragma unroll
+        for (int c = 0; c < T::A_PER_T; ++c) {
+            const int idx = tid + c * T::NT;
+            if (T::A_CHUNKS % T::NT == 0 || idx < T::A_CHUNKS) {
+                const int row = idx / T::KG, kg = idx % T::KG;
+                *reinterpret_cast<u32x4 *>(As + row * T::PITCH + 8 * kg) = ra[c];
+            }
+        }
+#pragma unroll
+        for (int c = 0; c < T::B_PER_T; ++c) {
+            const int idx = tid + c * T::NT;
+            if (T::B_BLOCKS % T::NT == 0 || idx < T::B_BLOCKS) {
+                const int kg = idx % T::KG, ng = idx / T::KG;
+                // rb[c][r] holds 4 columns of B's k-row r of the block (two values per
+                // word); column col of the block becomes one k-contiguous LDS row.
+#pragma unroll
+                for (int col = 0; col < 4; ++col) {
+                    const int w = col >> 1;
+                    const int sh = 16 * (col & 1);
+                    u32x4 v;
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const unsigned lo = (rb[c][2 * q][w] >> sh) & 0xffffu;
+                        const unsigned hi = (rb[c][2 * q + 1][w] >> sh) & 0xffffu;
+                        v[q] = lo | (hi << 16);
+                    }
+                    *reinterpret_cast<u32x4 *>(Bs + (4 * ng + col) * T::PITCH + 8 * kg) = v;
+                }
+            }
+        }
+    };
+
+    auto multiply = [&](int buf) {
+        const int koff = (lane >> 5) * 8;
+        const unsigned short *As = lds + buf * T::STAGE + (wm0 + (lane & 31)) * T::PITCH + koff;
+        const unsigned short *Bs =
+            lds + buf * T::STAGE + T::A_TILE + (wn0 + (lane & 31)) * T::PITCH + koff;
+        u32x4 a[2][T::FM], b[2][T::FN];
+        auto read_frags = [&](int s, u32x4 (&fa)[T::FM], u32x4 (&fb)[T::FN]) {
+#pragma unroll
+            for (int i = 0; i < T::FM; ++i)
+                fa[i] = *reinterpret_cast<const u32x4 *>(As + i * 32 * T::PITCH + 16 * s);
+#pragma unroll
+            for (int j = 0; j < T::FN; ++j)
+                fb[j] = *reinterpret_cast<const u32x4 *>(Bs + j * 32 * T::PITCH + 16 * s);
+        };
+        read_frags(0, a[0], b[0]);
+#pragma unroll
+        for (int s = 0; s < T::BK / 16; ++s) {
+            if (s + 1 < T::BK / 16) read_frags(s + 1, a[(s + 1) & 1], b[(s + 1) & 1]);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int i = 0; i < T::FM; ++i)
+#pragma unroll
+                for (int j = 0; j < T::FN; ++j)
+                    acc[i][j] = mfma16<BF16>(a[s & 1][i], b[s & 1][j], acc[i][j]);
+        }
+    };
+
+    if (nk > 0) {
+        global_load(0);
+        lds_store(0);
+        __syncthreads();
+    }
+    for (int kt = 0; kt < nk; ++kt) {
+        const int cur = kt & 1;
+        if (kt + 1 < nk) global_load(kt + 1);
+        multiply(cur);
+        // the other stage was last read in step kt - 1, before the barrier ending it
+        if (kt + 1 < nk) lds_store(cur ^ 1);
+        __syncthreads();
+    }
+
+    // accumulator layout as for the fp32 32x32 blocks
+    const int col_l = lane & 31;
+    const int row_l = 4 * (lane >> 5);
+#pragma unroll
+    for (int i = 0; i < T::FM; ++i)
+#pragma unroll
+        for (int j = 0; j < T::FN; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int gm = m0 + wm0 + i * 32 + 8 * (r >> 2) + row_l + (r & 3);
+                const int gn = n0 + wn0 + j * 32 + col_l;
+                if (inner_mn || (gm < p.M && gn < p.N))
+                    p.C[(int64_t)gm * p.ldc + gn] = acc[i][j][r];
+            }
+}
+
+template <class T, bool BF16>
+hipError_t launch16(const Gemm16Args &a, hipStream_t stream)
+{
+    const int64_t tiles = (int64_t)((a.M + T::BM - 1) / T::BM) * ((a.N + T::BN - 1) / T::BN);
+    if (tiles > 0x7fffffff) return hipErrorInvalidConfiguration;
+    const bool va = (a.lda % 8 == 0) && ((uintptr_t)a.A % 16 == 0);
+    const bool vb = (a.ldb % 4 == 0) && ((uintptr_t)a.B % 8 == 0);
+    const void *fn;
+    if (va && vb)
+        fn = reinterpret_cast<const void *>(&gemm_h16_kernel<T, BF16, true, true>);
+    else if (va)
+        fn = reinterpret_cast<const void *>(&gemm_h16_kernel<T, BF16, true, false>);
+    else if (vb)
+        fn = reinterpret_cast<const void *>(&gemm_h16_kernel<T, BF16, false, true>);
+    else
+        fn = reinterpret_cast<const void *>(&gemm_h16_kernel<T, BF16, false, false>);
+    Gemm16Args arg = a;
+    void *args[] = {&arg};
+    return hipLaunchKernel(fn, dim3((unsigned)tiles), dim3(T::NT), args, 0, stream);
+}
+
+using T16L = Tile16<256, 256, 128, 64>;
+using T16M = Tile16<128, 128, 64, 64>;
+using T16S = Tile16<64, 64, 32, 32>;
+
+}  // namespace
+
+int gemm16_num_configs() { return 3; }
+
+const char *gemm16_config_name(int cfg)
+{
+    static const char *names[] = {"256x256x64 w128x64 (8 waves)", "128x128x64 w64x64 (4 waves)",
+                                  "64x64x64 w32x32 (4 waves)"};
+    return (cfg >= 0 && cfg < 3) ? names[cfg] : nullptr;
+}
+
+int gemm16_select_config(int64_t M, int64_t N, int64_t K)
+{
+    (void)K;
+    if (((M + 255) / 256) * ((N + 255) / 256) >= 200) return 0;
+    if (((M + 127) / 128) * ((N + 127) / 128) >= 200) return 1;
+    return 2;
+}
+
+hipError_t gemm16_launch(int cfg, bool bf16, const void *A, int64_t lda, const void *B, int64_t ldb,
+                         float *C, int64_t ldc, int M, int N, int K, hipStream_t stream)
+{
+    Gemm16Args a;
+    a.A = static_cast<const unsigned short *>(A);
+    a.B = static_cast<const unsigned short *>(B);
+    a.C = C;
+    a.lda = lda;
+    a.ldb = ldb;
+    a.ldc = ldc;
+    a.M = M;
+    a.N = N;
+    a.K = K;
+    switch (cfg) {
+    case 0: return bf16 ? launch16<T16L, true>(a, stream) : launch16<T16L, false>(a, stream);
+    case 1: return bf16 ? launch16<T16M, true>(a, stream) : launch16<T16M, false>(a, stream);
+    default: return bf16 ? launch16<T16S, true>(a, stream) : launch16<T16S, false>(a, stream);
+    }
+}
+
+}  // namespace mm

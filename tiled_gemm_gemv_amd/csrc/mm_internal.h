@@ -37,6 +37,14 @@ hipError_t gemm_launch(int cfg, const GemmArgs &a, hipStream_t stream);
 template <int W, int L>
 hipError_t gemm_skinny_launch(const GemmArgs &a, hipStream_t stream);
 
+// GEMM with 16-bit inputs (mm_gemm_h16.hip); A and B hold bf16 (bf16 = true) or
+// binary16 bit patterns, C is fp32. M, N, K >= 1.
+int gemm16_num_configs();
+const char *gemm16_config_name(int cfg);
+int gemm16_select_config(int64_t M, int64_t N, int64_t K);
+hipError_t gemm16_launch(int cfg, bool bf16, const void *A, int64_t lda, const void *B, int64_t ldb,
+                         float *C, int64_t ldc, int M, int N, int K, hipStream_t stream);
+
 // Enqueue the GEMV (M >= 1, N >= 1).
 hipError_t gemv_launch(const GemvArgs &a, hipStream_t stream);
 

@@ -26,6 +26,7 @@ Peaks are AMD's published MI355X figures (not from the pages).
 FP32 = 4
 
 MI355X_FP32_MFMA_PEAK = 157.3e12      # FLOP/s, dense fp32 matrix
+MI355X_16BIT_MFMA_PEAK = 2.5e15       # FLOP/s, dense bf16 / fp16 matrix
 MI355X_HBM_PEAK = 8.0e12              # bytes/s, HBM3E
 MI355X_CUS = 256
 MI355X_PEAK_SCLK_HZ = 2.4e9

@@ -121,6 +121,28 @@ def random_matrix(seed: int, rows: int, cols: int, dist: str = "u11", std: float
     return draw(rng_for(seed, OPERAND_A), (rows, cols), dist, std)
 
 
+def to_bf16_bits(a: np.ndarray) -> np.ndarray:
+    """float32 -> bf16 bit patterns (uint16), rounding to nearest, ties to even."""
+    u = np.ascontiguousarray(a, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    rounded = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    return rounded.astype(np.uint16)
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns -> the same values as float32 (exact)."""
+    return (np.asarray(b, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def to_f16_bits(a: np.ndarray) -> np.ndarray:
+    """float32 -> IEEE binary16 bit patterns (uint16), rounding to nearest even."""
+    return np.ascontiguousarray(a, dtype=np.float32).astype(np.float16).view(np.uint16)
+
+
+def f16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    """binary16 bit patterns -> the same values as float32 (exact)."""
+    return np.asarray(b, dtype=np.uint16).view(np.float16).astype(np.float32)
+
+
 def embed(a: np.ndarray, ld: int, fill=np.nan, extra_rows: int = 0):
     """Place a (rows x cols) in a buffer with row stride ld >= cols.
 
