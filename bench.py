@@ -380,6 +380,28 @@ def sweep(kind, torch, mm, dev):
                 cells.append(f"{flop / ms / 1e9:7.1f}" + ("*" if c == sel else " "))
             print(f"{M:6d} {N:6d} {K:6d}  " + " ".join(cells) + f"  {name}", flush=True)
             del A, B, C
+        print("# strided batched GEMM (one mm_gemm_f32_batched launch) vs the same problems as "
+              "separate mm_gemm_f32 calls, TFLOP/s")
+        print(f"{'batch':>6s} {'M':>6s} {'N':>6s} {'K':>6s} {'batched':>9s} {'separate':>9s}")
+        for batch, M, N, K in ((64, 512, 512, 512), (16, 1024, 1024, 1024), (256, 256, 256, 256),
+                               (32, 128, 4096, 128)):
+            A = torch.randn(batch, M, K, device=dev)
+            B = torch.randn(batch, K, N, device=dev)
+            C = torch.empty(batch, M, N, device=dev)
+            flop = batch * rl.gemm_flops(M, N, K)
+            reps = max(3, min(100, int(2e11 / flop)))
+
+            def batched(i, st):
+                mm.mm_gemm_f32_batched(batch, M, N, K, A, K, M * K, B, N, K * N, C, N, M * N, st)
+
+            def separate(i, st):
+                for b in range(batch):
+                    mm.mm_gemm_f32(M, N, K, A[b], K, B[b], N, C[b], N, st)
+            tb = burst_time_ms(torch, batched, reps)
+            ts = burst_time_ms(torch, separate, max(1, reps // 4))
+            print(f"{batch:6d} {M:6d} {N:6d} {K:6d} {flop / tb / 1e9:9.1f} {flop / ts / 1e9:9.1f}",
+                  flush=True)
+            del A, B, C
     elif kind == "h16":
         shapes = [(w.M, w.N, w.K, w.name) for w in wl.WORKLOADS.values() if w.op == "gemm"]
         shapes += [(2048, 2048, 2048, ""), (4096, 4096, 4096, ""), (8192, 8192, 8192, "")]

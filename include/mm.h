@@ -108,6 +108,24 @@ int mm_gemm_f32_config(int cfg, int64_t M, int64_t N, int64_t K,
                        float *C, int64_t ldc, void *stream);
 
 /*
+ * mm_gemm_f32_batched: `batch` independent fp32 GEMMs C_b = A_b x B_b in one launch
+ * ("Matrix Operations", "Performance Considerations": processing several matrix
+ * products in parallel fills the GPU better). Problem b (0 <= b < batch) uses
+ * A + b * stride_a, B + b * stride_b and C + b * stride_c (strides in elements,
+ * >= 0; a stride of 0 shares that operand between problems). Each problem has the
+ * sizes and leading dimensions of mm_gemm_f32 and the same semantics.
+ *   batch     0 <= batch <= 65535; batch == 0 enqueues nothing (pointers may then
+ *             be NULL; sizes and leading dimensions are still checked).
+ * The C_b must not overlap each other or any input (undefined, not checked).
+ * Errors: as for mm_gemm_f32, plus MM_ERR_INVALID_ARG for a negative stride, a
+ * batch out of range, or batch offsets that overflow.
+ */
+int mm_gemm_f32_batched(int64_t batch, int64_t M, int64_t N, int64_t K,
+                        const float *A, int64_t lda, int64_t stride_a,
+                        const float *B, int64_t ldb, int64_t stride_b,
+                        float *C, int64_t ldc, int64_t stride_c, void *stream);
+
+/*
  * mm_gemm_bf16 / mm_gemm_f16: C = A x B with 16-bit inputs and fp32 accumulation
  * and output ("Matrix Operations", "Performance Considerations": half precision
  * and matrix engines). A and B hold bf16 (mm_gemm_bf16) or IEEE binary16

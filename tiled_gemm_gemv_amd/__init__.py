@@ -67,6 +67,9 @@ def load():
     lib.mm_gemm_f32_config_name.restype = ctypes.c_char_p
     lib.mm_gemm_f32_select.argtypes = [i64, i64, i64]
     lib.mm_gemm_f32_select.restype = ci
+    lib.mm_gemm_f32_batched.argtypes = [i64, i64, i64, i64, vp, i64, i64, vp, i64, i64, vp, i64,
+                                        i64, vp]
+    lib.mm_gemm_f32_batched.restype = ci
     for name in ("mm_gemm_bf16", "mm_gemm_f16"):
         getattr(lib, name).argtypes = [i64, i64, i64, vp, i64, vp, i64, vp, i64, vp]
         getattr(lib, name).restype = ci
@@ -132,6 +135,15 @@ def mm_gemm_f32_config(cfg, M, N, K, A, lda, B, ldb, C, ldc, stream=None):
     lib = load()
     _check(lib.mm_gemm_f32_config(cfg, M, N, K, _addr(A), lda, _addr(B), ldb, _addr(C), ldc,
                                   _stream(stream)), "mm_gemm_f32_config")
+
+
+def mm_gemm_f32_batched(batch, M, N, K, A, lda, stride_a, B, ldb, stride_b, C, ldc, stride_c,
+                        stream=None):
+    """C_b = A_b x B_b for b < batch, operands offset by b * stride. Raises MMError."""
+    lib = load()
+    _check(lib.mm_gemm_f32_batched(batch, M, N, K, _addr(A), lda, stride_a, _addr(B), ldb,
+                                   stride_b, _addr(C), ldc, stride_c, _stream(stream)),
+           "mm_gemm_f32_batched")
 
 
 def mm_gemm_bf16(M, N, K, A, lda, B, ldb, C, ldc, stream=None):
@@ -243,6 +255,30 @@ def gemm(A, B, out=None, config=None, stream=None):
             mm_gemm_f32(M, N, K, A, lda, B, ldb, out, ldc, stream)
         else:
             mm_gemm_f32_config(config, M, N, K, A, lda, B, ldb, out, ldc, stream)
+    return out
+
+
+def gemm_batched(A, B, out=None, stream=None):
+    """out[b] = A[b] @ B[b] for 3-D fp32 GPU tensors (batch, rows, cols) whose last
+    dimension has unit stride; a batch stride of 0 (e.g. from expand) shares an operand."""
+    import torch
+    for t, name in ((A, "A"), (B, "B")):
+        if not isinstance(t, torch.Tensor) or t.dtype != torch.float32 or t.dim() != 3:
+            raise TypeError(f"{name} must be a 3-D float32 tensor")
+        if t.device.type != "cuda":
+            raise ValueError(f"{name} must be on the GPU")
+    batch, M, K = A.shape
+    batch2, K2, N = B.shape
+    if batch2 != batch or K2 != K:
+        raise ValueError(f"shapes differ: {tuple(A.shape)} x {tuple(B.shape)}")
+    if out is None:
+        out = torch.empty((batch, M, N), dtype=torch.float32, device=A.device)
+    lda = _matrix(A[0] if batch else A.new_empty((M, K)), "A")
+    ldb = _matrix(B[0] if batch else B.new_empty((K, N)), "B")
+    ldc = _matrix(out[0] if batch else out.new_empty((M, N)), "out")
+    with torch.cuda.device(A.device):
+        mm_gemm_f32_batched(batch, M, N, K, A, lda, A.stride(0), B, ldb, B.stride(0), out, ldc,
+                            out.stride(0), stream)
     return out
 
 

@@ -45,15 +45,22 @@ bool extent_fits(int64_t rows, int64_t cols, int64_t ld)
     return true;
 }
 
-// elem: bytes per element of A and B (4 for fp32, 2 for the 16-bit formats).
-int check_gemm(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, const void *B,
-               int64_t ldb, const float *C, int64_t ldc, int elem = 4)
+int check_gemm_dims(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldc)
 {
     if (M < 0 || N < 0 || K < 0) return invalid("negative size");
     if (M > kMaxDim || N > kMaxDim || K > kMaxDim) return invalid("size above 2^31 - 1");
     if (lda < (K > 1 ? K : 1)) return invalid("lda < max(1, K)");
     if (ldb < (N > 1 ? N : 1)) return invalid("ldb < max(1, N)");
     if (ldc < (N > 1 ? N : 1)) return invalid("ldc < max(1, N)");
+    return MM_OK;
+}
+
+// elem: bytes per element of A and B (4 for fp32, 2 for the 16-bit formats).
+int check_gemm(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, const void *B,
+               int64_t ldb, const float *C, int64_t ldc, int elem = 4)
+{
+    const int d = check_gemm_dims(M, N, K, lda, ldb, ldc);
+    if (d != MM_OK) return d;
     if (M > 0 && K > 0 && !A) return invalid("A is NULL");
     if (K > 0 && N > 0 && !B) return invalid("B is NULL");
     if (M > 0 && N > 0 && !C) return invalid("C is NULL");
@@ -85,6 +92,48 @@ int run_gemm(int cfg, int64_t M, int64_t N, int64_t K, const float *A, int64_t l
     a.K = (int)K;
     if (cfg < 0) cfg = mm::gemm_select_config(M, N, K);
     return from_hip("gemm launch", mm::gemm_launch(cfg, a, s));
+}
+
+// Batched: every problem's extent and its offset b * stride must fit, strides >= 0.
+int run_gemm_batched(int64_t batch, int64_t M, int64_t N, int64_t K, const float *A, int64_t lda,
+                     int64_t sa, const float *B, int64_t ldb, int64_t sb, float *C, int64_t ldc,
+                     int64_t sc, void *stream)
+{
+    if (batch < 0) return invalid("negative batch");
+    if (batch > 65535) return invalid("batch above 65535");
+    if (sa < 0 || sb < 0 || sc < 0) return invalid("negative batch stride");
+    if (batch == 0) return check_gemm_dims(M, N, K, lda, ldb, ldc);  // pointers may be NULL
+    const int st = check_gemm(M, N, K, A, lda, B, ldb, C, ldc);
+    if (st != MM_OK) return st;
+    if (M == 0 || N == 0) return MM_OK;
+    const int64_t limit = INT64_MAX / 8;
+    if ((batch - 1) > 0 && (sa > limit / (batch - 1) || sb > limit / (batch - 1) ||
+                            sc > limit / (batch - 1)))
+        return invalid("batch offset overflows");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (K == 0) {
+        for (int64_t b = 0; b < batch; ++b) {
+            const int r = from_hip("zero fill launch", mm::zero_fill_launch(C + b * sc, M, N, ldc, s));
+            if (r != MM_OK) return r;
+        }
+        return MM_OK;
+    }
+    mm::GemmArgs a;
+    a.A = A;
+    a.B = B;
+    a.C = C;
+    a.lda = lda;
+    a.ldb = ldb;
+    a.ldc = ldc;
+    a.M = (int)M;
+    a.N = (int)N;
+    a.K = (int)K;
+    a.batch = (int)batch;
+    a.sa = sa;
+    a.sb = sb;
+    a.sc = sc;
+    return from_hip("batched gemm launch",
+                    mm::gemm_launch(mm::gemm_select_config(M, N, K, batch), a, s));
 }
 
 int run_gemm16(int cfg, bool bf16, int64_t M, int64_t N, int64_t K, const uint16_t *A,
@@ -125,6 +174,14 @@ int mm_gemm_f32_select(int64_t M, int64_t N, int64_t K)
 {
     if (M < 0 || N < 0 || K < 0) return 0;
     return mm::gemm_select_config(M, N, K);
+}
+
+int mm_gemm_f32_batched(int64_t batch, int64_t M, int64_t N, int64_t K, const float *A,
+                        int64_t lda, int64_t stride_a, const float *B, int64_t ldb,
+                        int64_t stride_b, float *C, int64_t ldc, int64_t stride_c, void *stream)
+{
+    return run_gemm_batched(batch, M, N, K, A, lda, stride_a, B, ldb, stride_b, C, ldc, stride_c,
+                            stream);
 }
 
 int mm_gemm_bf16(int64_t M, int64_t N, int64_t K, const uint16_t *A, int64_t lda,

@@ -127,6 +127,11 @@ __global__ __launch_bounds__(T::NT) void gemm_f32_kernel(GemmArgs p)
 {
     __shared__ __attribute__((aligned(16))) float lds[2 * T::STAGE];
 
+    // problem of a strided batch: grid row blockIdx.y
+    p.A += blockIdx.y * p.sa;
+    p.B += blockIdx.y * p.sb;
+    p.C += blockIdx.y * p.sc;
+
     const int tiles_m = (p.M + T::BM - 1) / T::BM;
     const int tiles_n = (p.N + T::BN - 1) / T::BN;
     int tm, tn;
@@ -363,7 +368,7 @@ hipError_t launch_tile(const GemmArgs &a, hipStream_t stream)
         fn = reinterpret_cast<const void *>(&gemm_f32_kernel<T, false, false>);
     GemmArgs arg = a;
     void *args[] = {&arg};
-    return hipLaunchKernel(fn, dim3((unsigned)tiles), dim3(T::NT), args, 0, stream);
+    return hipLaunchKernel(fn, dim3((unsigned)tiles, (unsigned)a.batch), dim3(T::NT), args, 0, stream);
 }
 
 using T256x256k32 = Tile<256, 256, 32, 128, 64, 8>;
@@ -411,13 +416,13 @@ const char *gemm_config_name(int cfg)
 // Largest tile that still gives most of the 256 CUs a tile: a big tile reuses
 // each staged element more often, a small one fills the chip on small shapes.
 // (Thresholds from a rocprofv3-timed sweep of every config over 128^3 .. 8192^2.)
-int gemm_select_config(int64_t M, int64_t N, int64_t K)
+int gemm_select_config(int64_t M, int64_t N, int64_t K, int64_t batch)
 {
     (void)K;
     if (N <= 64) return 8;  // a few columns: stream A once (mm_gemm_skinny.hip)
-    if (tiles_for(0, M, N) >= 200) return 0;
-    if (tiles_for(1, M, N) >= 200) return 1;
-    if (tiles_for(4, M, N) >= 128) return 4;
+    if (batch * tiles_for(0, M, N) >= 200) return 0;
+    if (batch * tiles_for(1, M, N) >= 200) return 1;
+    if (batch * tiles_for(4, M, N) >= 128) return 4;
     return 6;               // few 64 x 64 tiles: 16-row tiles fill more CUs
 }
 

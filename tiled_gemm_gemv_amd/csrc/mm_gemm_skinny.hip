@@ -50,6 +50,10 @@ template <int NB, int W, int U, bool VEC_A>
 __global__ __launch_bounds__(W * 64) void gemm_skinny_kernel(GemmArgs p)
 {
     __shared__ f32x4 partial[(W > 1 ? W - 1 : 1) * NB * 64];
+    // problem of a strided batch: grid layer blockIdx.z
+    p.A += blockIdx.z * p.sa;
+    p.B += blockIdx.z * p.sb;
+    p.C += blockIdx.z * p.sc;
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int g = lane >> 4, c16 = lane & 15;
     const int m0 = blockIdx.x * kSkinnyRows;
@@ -128,7 +132,8 @@ hipError_t launch_nb(const GemmArgs &a, bool vec, hipStream_t stream)
                          : reinterpret_cast<const void *>(&gemm_skinny_kernel<NB, W, U, false>);
     GemmArgs arg = a;
     void *args[] = {&arg};
-    return hipLaunchKernel(fn, dim3((unsigned)gx, (unsigned)gy), dim3(W * 64), args, 0, stream);
+    return hipLaunchKernel(fn, dim3((unsigned)gx, (unsigned)gy, (unsigned)a.batch), dim3(W * 64), args,
+                           0, stream);
 }
 
 }  // namespace

@@ -14,6 +14,9 @@ struct GemmArgs {
     float *C;
     int64_t lda, ldb, ldc;
     int M, N, K;
+    // strided batch: problem b uses A + b * sa, B + b * sb, C + b * sc (elements)
+    int batch = 1;
+    int64_t sa = 0, sb = 0, sc = 0;
 };
 
 // Arguments of one GEMV launch (A has packed rows: leading dimension N).
@@ -27,7 +30,8 @@ struct GemvArgs {
 // GEMM tile configurations, in the order of the public config index.
 int gemm_num_configs();
 const char *gemm_config_name(int cfg);
-int gemm_select_config(int64_t M, int64_t N, int64_t K);
+// batch: number of independent problems launched together (tiles are counted over all).
+int gemm_select_config(int64_t M, int64_t N, int64_t K, int64_t batch = 1);
 // Enqueue config `cfg` of the GEMM (K >= 1, M >= 1, N >= 1).
 hipError_t gemm_launch(int cfg, const GemmArgs &a, hipStream_t stream);
 
