@@ -89,6 +89,20 @@ int mm_gemv_f32(int64_t M, int64_t N, const float *A, const float *x, float *y,
                 void *stream);
 
 /*
+ * mm_gemv_t_f32: y = A^T x in fp32, y[j] = sum over i in [0, M) of A[i][j] * x[i]:
+ * the GEMV of the same row-major matrix applied to its transpose (a column of A
+ * dotted with x per output).
+ *   M, N      sizes, 0 <= M, N <= 2^31 - 1.
+ *   A         M x N with packed rows (leading dimension N).
+ *   x         M entries, contiguous. May be NULL when M == 0.
+ *   y         N entries, contiguous. May be NULL when N == 0.
+ * N == 0: nothing is enqueued. M == 0: y is filled with zeros. The summation order
+ * is fixed, so results are deterministic. Errors: as for mm_gemv_f32.
+ */
+int mm_gemv_t_f32(int64_t M, int64_t N, const float *A, const float *x, float *y,
+                  void *stream);
+
+/*
  * Tile configurations of the GEMM. mm_gemm_f32 picks one per shape; the calls
  * below expose the choice and let a caller (tests, tuning) run a given one.
  *   mm_gemm_f32_num_configs: number of configurations, >= 1.

@@ -1,0 +1,76 @@
+"""GPU parity of the transposed GEMV y = A^T x against the oracle (which computes
+A^T x as the GEMM x^T A: the same sums, y[j] = sum_i x_i A[i][j])."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import verify
+import tiled_gemm_gemv_amd as mm
+import workloads as wl
+from gpu_helpers import require_gpu, to_device
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dev():
+    d = require_gpu()
+    mm.load()
+    return d
+
+
+def run(A, x, dev, a_offset=0):
+    M, N = A.shape
+    abuf = to_device(np.concatenate([np.full(a_offset, np.nan, np.float32), A.ravel()]), dev)
+    Ad = abuf[a_offset:].view(M, N)
+    y = torch.full((N + 1,), float("nan"), device=dev)
+    mm.gemv_t(Ad, to_device(x, dev), out=y[:N])
+    torch.cuda.synchronize()
+    h = y.cpu().numpy()
+    assert np.isnan(h[N]), "wrote past the end of y"
+    return h[:N]
+
+
+def reference(A, x):
+    C64, S64 = oracle.gemm(x.reshape(1, -1), A)
+    return C64[0], S64[0]
+
+
+@pytest.mark.parametrize("M,N", [(4096, 4096), (1, 1), (3, 5), (1000, 1531), (4097, 17),
+                                 (20000, 64), (17, 4100), (333, 4095)])
+@pytest.mark.parametrize("a_offset", [0, 1])
+def test_shapes(dev, M, N, a_offset):
+    A = wl.random_matrix(500 + M, M, N, "int4")
+    x = wl.random_matrix(600 + N, 1, M, "int4")[0]
+    y64, _ = reference(A, x)
+    r = verify.exact(run(A, x, dev, a_offset), y64)
+    assert r, f"{(M, N)}: {r}"
+    A = wl.random_matrix(700 + M, M, N, "u11")
+    x = wl.random_matrix(800 + N, 1, M, "u11")[0]
+    y64, s64 = reference(A, x)
+    r = verify.within_tol(run(A, x, dev, a_offset), y64, s64, 1e-5)
+    assert r, f"{(M, N)}: {r}"
+
+
+def test_matches_gemv_of_transpose(dev):
+    """A^T x equals the row GEMV of the explicitly transposed matrix, exactly on integers."""
+    A = wl.random_matrix(91, 777, 1531, "int4")
+    x = wl.random_matrix(92, 1, 777, "int4")[0]
+    y = run(A, x, dev)
+    yr = mm.gemv(to_device(np.ascontiguousarray(A.T), dev), to_device(x, dev))
+    torch.cuda.synchronize()
+    assert np.array_equal(y, yr.cpu().numpy())
+
+
+def test_deterministic_and_m_zero(dev):
+    A = to_device(wl.random_matrix(93, 4096, 4096, "u11"), dev)
+    x = to_device(wl.random_matrix(94, 1, 4096, "u11")[0], dev)
+    y1 = mm.gemv_t(A, x)
+    y2 = mm.gemv_t(A, x)
+    torch.cuda.synchronize()
+    assert torch.equal(y1.view(torch.int32), y2.view(torch.int32))
+    y = torch.full((9,), float("nan"), device=dev)
+    mm.gemv_t(torch.empty((0, 8), device=dev), torch.empty(0, device=dev), out=y[:8])
+    torch.cuda.synchronize()
+    assert (y[:8] == 0).all().item() and torch.isnan(y[8]).item()

@@ -83,6 +83,8 @@ def load():
     lib.mm_gemm_h16_select.argtypes = [i64, i64, i64]
     lib.mm_gemm_h16_select.restype = ci
     lib.mm_gemv_f32.argtypes = [i64, i64, vp, vp, vp, vp]
+    lib.mm_gemv_t_f32.argtypes = [i64, i64, vp, vp, vp, vp]
+    lib.mm_gemv_t_f32.restype = ci
     lib.mm_gemv_f32.restype = ci
     lib.mm_status_string.argtypes = [ci]
     lib.mm_status_string.restype = ctypes.c_char_p
@@ -189,6 +191,13 @@ def mm_gemv_f32(M, N, A, x, y, stream=None):
     """y = A x (A M x N with packed rows). Raises MMError."""
     lib = load()
     _check(lib.mm_gemv_f32(M, N, _addr(A), _addr(x), _addr(y), _stream(stream)), "mm_gemv_f32")
+
+
+def mm_gemv_t_f32(M, N, A, x, y, stream=None):
+    """y = A^T x (A M x N with packed rows, x of M, y of N). Raises MMError."""
+    lib = load()
+    _check(lib.mm_gemv_t_f32(M, N, _addr(A), _addr(x), _addr(y), _stream(stream)),
+           "mm_gemv_t_f32")
 
 
 def mm_gemm_f32_num_configs():
@@ -325,4 +334,22 @@ def gemv(A, x, out=None, stream=None):
         raise ValueError(f"out must be a contiguous float32 vector of {M} entries")
     with torch.cuda.device(A.device):
         mm_gemv_f32(M, N, A, x, out, stream)
+    return out
+
+
+def gemv_t(A, x, out=None, stream=None):
+    """out = A.T @ x for an fp32 GPU matrix with packed rows and a contiguous vector."""
+    import torch
+    _matrix(A, "A")
+    M, N = A.shape
+    if not A.is_contiguous():
+        raise ValueError("A must have packed rows (contiguous)")
+    if x.dtype != torch.float32 or x.dim() != 1 or x.shape[0] != M or not x.is_contiguous():
+        raise ValueError(f"x must be a contiguous float32 vector of {M} entries")
+    if out is None:
+        out = torch.empty(N, dtype=torch.float32, device=A.device)
+    if out.dtype != torch.float32 or tuple(out.shape) != (N,) or not out.is_contiguous():
+        raise ValueError(f"out must be a contiguous float32 vector of {N} entries")
+    with torch.cuda.device(A.device):
+        mm_gemv_t_f32(M, N, A, x, out, stream)
     return out

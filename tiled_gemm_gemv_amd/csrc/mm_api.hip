@@ -242,6 +242,28 @@ int mm_gemv_f32(int64_t M, int64_t N, const float *A, const float *x, float *y, 
     return from_hip("gemv launch", mm::gemv_launch(a, s));
 }
 
+int mm_gemv_t_f32(int64_t M, int64_t N, const float *A, const float *x, float *y, void *stream)
+{
+    if (M < 0 || N < 0) return invalid("negative size");
+    if (M > kMaxDim || N > kMaxDim) return invalid("size above 2^31 - 1");
+    if (M > 0 && N > 0 && !A) return invalid("A is NULL");
+    if (M > 0 && !x) return invalid("x is NULL");
+    if (N > 0 && !y) return invalid("y is NULL");
+    if ((uintptr_t)A % 4 || (uintptr_t)x % 4 || (uintptr_t)y % 4)
+        return invalid("pointer not aligned to its element size");
+    if (M > 0 && N > 0 && !extent_fits(M, N, N)) return invalid("A extent overflows");
+    if (N == 0) return MM_OK;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (M == 0) return from_hip("zero fill launch", mm::zero_fill_launch(y, 1, N, N, s));
+    mm::GemvArgs a;
+    a.A = A;
+    a.x = x;
+    a.y = y;
+    a.M = (int)M;
+    a.N = (int)N;
+    return from_hip("gemv_t launch", mm::gemv_t_launch(a, s));
+}
+
 const char *mm_status_string(int status)
 {
     switch (status) {

@@ -1,0 +1,111 @@
+// mm_gemv_t.hip -- transposed fp32 GEMV y = A^T x, y[j] = sum over i of A[i][j] * x[i],
+// for a row-major M x N matrix A (x has M entries, y has N).
+//
+// The plain definition is the GEMV of "Matrix Operations" (docs.vulkan.org
+// ML-inference tutorial, "Matrix-Vector Multiplication") applied to the transpose:
+// each output is a column of A dotted with x. Reading A column-wise would stride
+// by a whole row per element, so the kernel still streams A along its rows and
+// gives each workgroup a strip of 16 columns over all M rows:
+//   * a wave reads 16 rows x 64 bytes per instruction (lane l: row l / 4 of the
+//     group, 4 columns at 4 * (l % 4)), 16-byte loads, up to 16 instructions in
+//     flight; the 4 waves take interleaved groups of 16 rows;
+//   * each lane keeps 4 column sums; at the end the 16 lanes that share columns
+//     are combined with a butterfly, then the 4 waves in LDS in wave order, so the
+//     summation order is fixed and results are deterministic;
+//   * N / 16 strips give one workgroup per CU at N = 4096; consecutive strips go
+//     to the same XCD (the launch order is renumbered as in the GEMM), so the two
+//     halves of a 128-byte line are read through one L2.
+// Rows that are not 16-byte aligned (N % 4 != 0 or an unaligned A) use 4-byte loads.
+#include "mm_internal.h"
+
+namespace mm {
+namespace {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kStrip = 16;        // columns per workgroup
+constexpr int kWaves = 4;         // waves per workgroup
+constexpr int kRowsPerLoad = 16;  // rows one wave instruction covers
+constexpr int kDepth = 16;        // row groups in flight per wave
+
+__device__ __forceinline__ int strip_of_block(int bid, int nblocks)
+{
+    const int q = nblocks / 8, r = nblocks % 8;
+    const int xcd = bid % 8, slot = bid / 8;
+    return (xcd < r) ? xcd * (q + 1) + slot : r * (q + 1) + (xcd - r) * q + slot;
+}
+
+template <bool VEC>
+__global__ __launch_bounds__(kWaves * 64) void gemv_t_kernel(GemvArgs p)
+{
+    __shared__ f32x4 partial[(kWaves - 1) * 64];
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int strip = strip_of_block(blockIdx.x, gridDim.x);
+    const int j0 = strip * kStrip + 4 * (lane & 3);   // this lane's first column
+    const int rsub = lane >> 2;                         // row within a 16-row group
+    const int ncols = p.N - j0;                         // columns left from j0 (may be <= 0)
+
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    // row groups g = w, w + 4, w + 8, ...; a round takes kDepth of them
+    const int groups = (p.M + kRowsPerLoad - 1) / kRowsPerLoad;
+    for (int g0 = w; g0 < groups; g0 += kWaves * kDepth) {
+        f32x4 va[kDepth];
+        float vx[kDepth];
+#pragma unroll
+        for (int d = 0; d < kDepth; ++d) {
+            const int i = (g0 + d * kWaves) * kRowsPerLoad + rsub;
+            const bool row_ok = i < p.M;
+            const float *src = p.A + (int64_t)(row_ok ? i : 0) * p.N + j0;
+            f32x4 v = {0.f, 0.f, 0.f, 0.f};
+            if (row_ok) {
+                if (VEC && ncols >= 4) {
+                    v = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(src));
+                } else {
+                    if (ncols > 0) v[0] = src[0];
+                    if (ncols > 1) v[1] = src[1];
+                    if (ncols > 2) v[2] = src[2];
+                    if (ncols > 3) v[3] = src[3];
+                }
+            }
+            va[d] = v;
+            vx[d] = row_ok ? p.x[i] : 0.f;
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int d = 0; d < kDepth; ++d) {
+            acc[0] += va[d][0] * vx[d];
+            acc[1] += va[d][1] * vx[d];
+            acc[2] += va[d][2] * vx[d];
+            acc[3] += va[d][3] * vx[d];
+        }
+    }
+    // lanes l, l ^ 4, l ^ 8, ... (same l % 4) hold the same 4 columns
+#pragma unroll
+    for (int off = 4; off < 64; off <<= 1)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) acc[c] += __shfl_xor(acc[c], off, 64);
+    if (w > 0 && lane < 4) partial[(w - 1) * 64 + lane] = acc;
+    __syncthreads();
+    if (w > 0 || lane >= 4) return;  // no barrier follows
+#pragma unroll 1
+    for (int v = 1; v < kWaves; ++v) acc += partial[(v - 1) * 64 + lane];
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+        if (c < ncols) p.y[j0 + c] = acc[c];
+}
+
+}  // namespace
+
+hipError_t gemv_t_launch(const GemvArgs &a, hipStream_t stream)
+{
+    const bool vec = (a.N % 4 == 0) && ((uintptr_t)a.A % 16 == 0);
+    const int64_t strips = ((int64_t)a.N + kStrip - 1) / kStrip;
+    if (strips > 0x7fffffff) return hipErrorInvalidConfiguration;
+    GemvArgs arg = a;
+    void *args[] = {&arg};
+    const void *fn = vec ? reinterpret_cast<const void *>(&gemv_t_kernel<true>)
+                         : reinterpret_cast<const void *>(&gemv_t_kernel<false>);
+    return hipLaunchKernel(fn, dim3((unsigned)strips), dim3(kWaves * 64), args, 0, stream);
+}
+
+}  // namespace mm

@@ -52,6 +52,10 @@ hipError_t gemm16_launch(int cfg, bool bf16, const void *A, int64_t lda, const v
 // Enqueue the GEMV (M >= 1, N >= 1).
 hipError_t gemv_launch(const GemvArgs &a, hipStream_t stream);
 
+// Enqueue the transposed GEMV y = A^T x (mm_gemv_t.hip); x has M entries, y has N.
+// M >= 1, N >= 1.
+hipError_t gemv_t_launch(const GemvArgs &a, hipStream_t stream);
+
 // Enqueue a fill of the rows x cols matrix at p (row stride ld) with zeros.
 hipError_t zero_fill_launch(float *p, int64_t rows, int64_t cols, int64_t ld, hipStream_t stream);
 
