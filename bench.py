@@ -17,9 +17,10 @@ Infinity Cache) gives the GEMV's HBM rate. Results are then verified against the
 CPU oracle (64+ sampled GEMM rows in full, every GEMV output) and the oracle's
 own time on a bounded sample of the same work is reported as `cpu_baseline`.
 
-Profiling helpers (same script, for rocprofv3 runs): --only gemm | gemv | copy
+Profiling helpers (same script, for rocprofv3 runs): --only gemm | gemv | copy | h16
 runs just that kernel `--steps` times with no oracle; `copy` is a plain
-device-to-device copy of known size used to calibrate HBM counters.
+device-to-device copy of known size used to calibrate HBM counters; `h16` is the
+bf16-input GEMM at the projection shape.
 
 Sweeps (tables, not the benchmark line): --sweep gemm times every GEMM tile
 configuration on the workload shapes and a few others; --sweep gemv times the GEMV
@@ -109,7 +110,7 @@ def main():
     ap.add_argument("--gemv-reps", type=int, default=400)
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="target length of the oracle's timed sample")
-    ap.add_argument("--only", choices=["gemm", "gemv", "copy"], default=None,
+    ap.add_argument("--only", choices=["gemm", "gemv", "copy", "h16"], default=None,
                     help="profiling helper: launch only this kernel --steps times")
     ap.add_argument("--sweep", choices=["gemm", "gemv", "h16"], default=None,
                     help="print a timing table instead of the benchmark line")
@@ -147,6 +148,17 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         log(f"copy: {args.steps} x {src.numel() * 4} bytes")
+        return
+
+    if args.only == "h16":
+        # bf16 inputs at the projection shape (values from the same distributions)
+        A16 = (torch.randn(M, K, device=dev)).to(torch.bfloat16)
+        B16 = (torch.randn(K, N, device=dev) / 64.0).to(torch.bfloat16)
+        C = torch.empty((M, N), dtype=torch.float32, device=dev)
+        for _ in range(args.steps):
+            mm.mm_gemm_bf16(M, N, K, A16, K, B16, N, C, N, stream)
+        torch.cuda.synchronize()
+        log(f"h16: {args.steps} bf16 launches")
         return
 
     log(f"generating inputs: {wg.describe()}, {wv.describe()}")

@@ -33,9 +33,12 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 
 constexpr int kXcds = 8;
 
-template <int BM_, int BN_, int WM_, int WN_>
+// PF_: K-steps of HBM loads in flight (1 or 2, as in the fp32 kernel). At 16-bit
+// rates a K-step of MFMAs is shorter than a load's latency, so the second set of
+// staging registers matters more here.
+template <int BM_, int BN_, int WM_, int WN_, int PF_ = 1>
 struct Tile16 {
-    static constexpr int BM = BM_, BN = BN_, BK = 64, WM = WM_, WN = WN_;
+    static constexpr int BM = BM_, BN = BN_, BK = 64, WM = WM_, WN = WN_, PF = PF_;
     static constexpr int WAVES_M = BM / WM, WAVES_N = BN / WN;
     static constexpr int NT = WAVES_M * WAVES_N * 64;
     static constexpr int FM = WM / 32, FN = WN / 32;
@@ -48,6 +51,10 @@ struct Tile16 {
     static constexpr int B_BLOCKS = KG * (BN / 4);  // 8 x 4 blocks of a B panel
     static constexpr int B_PER_T = (B_BLOCKS + NT - 1) / NT;
     static_assert(2 * STAGE * 2 <= 160 * 1024, "two stages must fit the 160 KB LDS");
+    struct Staged {
+        u32x4 a[A_PER_T];
+        u32x2 b[B_PER_T][8];  // 8 k-rows x 4 columns each
+    };
 };
 
 // 8 consecutive 16-bit values at p (in range) as 16 bytes.
@@ -160,10 +167,9 @@ __global__ __launch_bounds__(T::NT) void gemm_h16_kernel(Gemm16Args p)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-    u32x4 ra[T::A_PER_T];
-    u32x2 rb[T::B_PER_T][8];  // 8 k-rows x 4 columns each
+    typename T::Staged r0, r1;
 
-    auto global_load = [&](int kt) {
+    auto global_load = [&](int kt, typename T::Staged &st) {
         const int k0 = kt * T::BK;
         const bool full = inner_mn && (k0 + T::BK <= p.K);
 #pragma unroll
@@ -173,7 +179,8 @@ __global__ __launch_bounds__(T::NT) void gemm_h16_kernel(Gemm16Args p)
                 const int row = idx / T::KG, kg = idx % T::KG;
                 const int gm = m0 + row, gk = k0 + 8 * kg;
                 const unsigned short *src = p.A + (int64_t)gm * p.lda + gk;
-                ra[c] = full ? load8<VEC_A>(src) : load8_masked<VEC_A>(src, gm < p.M ? p.K - gk : 0);
+                st.a[c] = full ? load8<VEC_A>(src)
+                               : load8_masked<VEC_A>(src, gm < p.M ? p.K - gk : 0);
             }
         }
 #pragma unroll
@@ -186,14 +193,14 @@ __global__ __launch_bounds__(T::NT) void gemm_h16_kernel(Gemm16Args p)
                 for (int r = 0; r < 8; ++r) {
                     const int gk = k0 + 8 * kg + r;
                     const unsigned short *src = p.B + (int64_t)gk * p.ldb + gn;
-                    rb[c][r] = full ? load4h<VEC_B>(src)
-                                    : load4h_masked<VEC_B>(src, gk < p.K ? p.N - gn : 0);
+                    st.b[c][r] = full ? load4h<VEC_B>(src)
+                                      : load4h_masked<VEC_B>(src, gk < p.K ? p.N - gn : 0);
                 }
             }
         }
     };
 
-    auto lds_store = [&](int buf) {
+    auto lds_store = [&](int buf, const typename T::Staged &st) {
         unsigned short *As = lds + buf * T::STAGE;
         unsigned short *Bs = As + T::A_TILE;
 #pragma unroll
@@ -201,7 +208,7 @@ __global__ __launch_bounds__(T::NT) void gemm_h16_kernel(Gemm16Args p)
             const int idx = tid + c * T::NT;
             if (T::A_CHUNKS % T::NT == 0 || idx < T::A_CHUNKS) {
                 const int row = idx / T::KG, kg = idx % T::KG;
-                *reinterpret_cast<u32x4 *>(As + row * T::PITCH + 8 * kg) = ra[c];
+                *reinterpret_cast<u32x4 *>(As + row * T::PITCH + 8 * kg) = st.a[c];
             }
         }
 #pragma unroll
@@ -209,7 +216,7 @@ __global__ __launch_bounds__(T::NT) void gemm_h16_kernel(Gemm16Args p)
             const int idx = tid + c * T::NT;
             if (T::B_BLOCKS % T::NT == 0 || idx < T::B_BLOCKS) {
                 const int kg = idx % T::KG, ng = idx / T::KG;
-                // rb[c][r] holds 4 columns of B's k-row r of the block (two values per
+                // st.b[c][r] holds 4 columns of B's k-row r of the block (two values per
                 // word); column col of the block becomes one k-contiguous LDS row.
 #pragma unroll
                 for (int col = 0; col < 4; ++col) {
@@ -218,8 +225,8 @@ __global__ __launch_bounds__(T::NT) void gemm_h16_kernel(Gemm16Args p)
                     u32x4 v;
 #pragma unroll
                     for (int q = 0; q < 4; ++q) {
-                        const unsigned lo = (rb[c][2 * q][w] >> sh) & 0xffffu;
-                        const unsigned hi = (rb[c][2 * q + 1][w] >> sh) & 0xffffu;
+                        const unsigned lo = (st.b[c][2 * q][w] >> sh) & 0xffffu;
+                        const unsigned hi = (st.b[c][2 * q + 1][w] >> sh) & 0xffffu;
                         v[q] = lo | (hi << 16);
                     }
                     *reinterpret_cast<u32x4 *>(Bs + (4 * ng + col) * T::PITCH + 8 * kg) = v;
@@ -228,7 +235,7 @@ __global__ __launch_bounds__(T::NT) void gemm_h16_kernel(Gemm16Args p)
         }
     };
 
-    auto multiply = [&](int buf) {
+    auto multiply = [&](int buf, auto &&mid) {
         const int koff = (lane >> 5) * 8;
         const unsigned short *As = lds + buf * T::STAGE + (wm0 + (lane & 31)) * T::PITCH + koff;
         const unsigned short *Bs =
@@ -246,6 +253,7 @@ __global__ __launch_bounds__(T::NT) void gemm_h16_kernel(Gemm16Args p)
 #pragma unroll
         for (int s = 0; s < T::BK / 16; ++s) {
             if (s + 1 < T::BK / 16) read_frags(s + 1, a[(s + 1) & 1], b[(s + 1) & 1]);
+            if (s == T::BK / 32) mid();
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int i = 0; i < T::FM; ++i)
@@ -255,18 +263,43 @@ __global__ __launch_bounds__(T::NT) void gemm_h16_kernel(Gemm16Args p)
         }
     };
 
-    if (nk > 0) {
-        global_load(0);
-        lds_store(0);
+    auto nothing = [] {};
+    if constexpr (T::PF == 1) {
+        if (nk > 0) {
+            global_load(0, r0);
+            lds_store(0, r0);
+            __syncthreads();
+        }
+        for (int kt = 0; kt < nk; ++kt) {
+            const int cur = kt & 1;
+            if (kt + 1 < nk) global_load(kt + 1, r0);
+            multiply(cur, nothing);
+            // the other stage was last read in step kt - 1, before the barrier ending it
+            if (kt + 1 < nk) lds_store(cur ^ 1, r0);
+            __syncthreads();
+        }
+    } else {
+        // Two staging buffers, loop unrolled by two (see the fp32 kernel): the loads
+        // for step kt + 2 are issued at the top of step kt; step kt + 1's data is
+        // written to the other stage halfway through step kt's MFMAs.
+        if (nk > 0) {
+            global_load(0, r0);
+            lds_store(0, r0);
+        }
+        if (nk > 1) global_load(1, r1);
         __syncthreads();
-    }
-    for (int kt = 0; kt < nk; ++kt) {
-        const int cur = kt & 1;
-        if (kt + 1 < nk) global_load(kt + 1);
-        multiply(cur);
-        // the other stage was last read in step kt - 1, before the barrier ending it
-        if (kt + 1 < nk) lds_store(cur ^ 1);
-        __syncthreads();
+        int kt = 0;
+        for (; kt + 1 < nk; kt += 2) {
+            if (kt + 2 < nk) global_load(kt + 2, r0);
+            multiply(0, [&] { lds_store(1, r1); });
+            __syncthreads();
+            if (kt + 3 < nk) global_load(kt + 3, r1);
+            multiply(1, [&] {
+                if (kt + 2 < nk) lds_store(0, r0);
+            });
+            __syncthreads();
+        }
+        if (kt < nk) multiply(0, nothing);
     }
 
     // accumulator layout as for the fp32 32x32 blocks
@@ -309,24 +342,27 @@ hipError_t launch16(const Gemm16Args &a, hipStream_t stream)
 using T16L = Tile16<256, 256, 128, 64>;
 using T16M = Tile16<128, 128, 64, 64>;
 using T16S = Tile16<64, 64, 32, 32>;
+using T16Mp2 = Tile16<128, 128, 64, 64, 2>;
+using T16Sp2 = Tile16<64, 64, 32, 32, 2>;
 
 }  // namespace
 
-int gemm16_num_configs() { return 3; }
+int gemm16_num_configs() { return 5; }
 
 const char *gemm16_config_name(int cfg)
 {
-    static const char *names[] = {"256x256x64 w128x64 (8 waves)", "128x128x64 w64x64 (4 waves)",
-                                  "64x64x64 w32x32 (4 waves)"};
-    return (cfg >= 0 && cfg < 3) ? names[cfg] : nullptr;
+    static const char *names[] = {"256x256x64 w128x64 pf1 (8 waves)", "128x128x64 w64x64 pf1 (4 waves)",
+                                  "64x64x64 w32x32 pf1 (4 waves)", "128x128x64 w64x64 pf2 (4 waves)",
+                                  "64x64x64 w32x32 pf2 (4 waves)"};
+    return (cfg >= 0 && cfg < 5) ? names[cfg] : nullptr;
 }
 
 int gemm16_select_config(int64_t M, int64_t N, int64_t K)
 {
     (void)K;
     if (((M + 255) / 256) * ((N + 255) / 256) >= 200) return 0;
-    if (((M + 127) / 128) * ((N + 127) / 128) >= 200) return 1;
-    return 2;
+    if (((M + 127) / 128) * ((N + 127) / 128) >= 200) return 3;
+    return 4;
 }
 
 hipError_t gemm16_launch(int cfg, bool bf16, const void *A, int64_t lda, const void *B, int64_t ldb,
@@ -345,7 +381,9 @@ hipError_t gemm16_launch(int cfg, bool bf16, const void *A, int64_t lda, const v
     switch (cfg) {
     case 0: return bf16 ? launch16<T16L, true>(a, stream) : launch16<T16L, false>(a, stream);
     case 1: return bf16 ? launch16<T16M, true>(a, stream) : launch16<T16M, false>(a, stream);
-    default: return bf16 ? launch16<T16S, true>(a, stream) : launch16<T16S, false>(a, stream);
+    case 2: return bf16 ? launch16<T16S, true>(a, stream) : launch16<T16S, false>(a, stream);
+    case 3: return bf16 ? launch16<T16Mp2, true>(a, stream) : launch16<T16Mp2, false>(a, stream);
+    default: return bf16 ? launch16<T16Sp2, true>(a, stream) : launch16<T16Sp2, false>(a, stream);
     }
 }
 
