@@ -14,6 +14,9 @@ The arithmetic lives in oracle.c; this module only marshals numpy arrays:
 * gemv(A, x, threads=None) -> (y64, s64)
     y64[i] = sum_j A[i, j] * x[j] in fp64, ascending j; s64 = sum_j |A[i, j] * x[j]|.
     Definition: same page, section "Matrix-Vector Multiplication".
+* conv2d(x, w, stride, pad, dilation) -> (y64, s64)
+    The 2-D convolution of a convolutional layer from its usual definition (see
+    oracle.c; the pages only say it can be recast as a matrix product).
 
 Inputs must be float32, 2-D row-major with unit column stride (any row stride).
 """
@@ -62,6 +65,8 @@ class Oracle:
         lib.oracle_gemm_f64.restype = ctypes.c_int
         lib.oracle_gemv_f64.argtypes = [i64, i64, vp, i64, vp, vp, vp, ctypes.c_int]
         lib.oracle_gemv_f64.restype = ctypes.c_int
+        lib.oracle_conv2d_f64.argtypes = [i64] * 13 + [vp, vp, vp, vp, ctypes.c_int]
+        lib.oracle_conv2d_f64.restype = ctypes.c_int
         self.lib = lib
         self.path = libpath
 
@@ -106,6 +111,33 @@ class Oracle:
         return y, s
 
 
+    def conv2d(self, x, w, stride=(1, 1), pad=(0, 0), dilation=(1, 1), threads=None):
+        """fp64 reference of the 2-D convolution: x is N x C x H x W, w is K x C x R x S
+        (float32, packed); returns (y64, s64), each N x K x P x Q."""
+        x = np.ascontiguousarray(np.asarray(x))
+        w = np.ascontiguousarray(np.asarray(w))
+        if x.dtype != np.float32 or w.dtype != np.float32 or x.ndim != 4 or w.ndim != 4:
+            raise TypeError("x and w must be 4-D float32 arrays")
+        N, C, H, W = x.shape
+        K, C2, R, S = w.shape
+        if C2 != C:
+            raise ValueError(f"channel counts differ: x has {C}, w has {C2}")
+        sh, sw = stride
+        ph, pw = pad
+        dh, dw = dilation
+        P = (H + 2 * ph - dh * (R - 1) - 1) // sh + 1
+        Q = (W + 2 * pw - dw * (S - 1) - 1) // sw + 1
+        if P < 1 or Q < 1:
+            raise ValueError("the filter does not fit the padded input")
+        y = np.full((N, K, P, Q), np.nan)
+        s = np.full((N, K, P, Q), np.nan)
+        rc = self.lib.oracle_conv2d_f64(N, C, H, W, K, R, S, sh, sw, ph, pw, dh, dw, _ptr(x),
+                                        _ptr(w), _ptr(y), _ptr(s), threads or default_threads())
+        if rc != 0:
+            raise RuntimeError(f"oracle_conv2d_f64 failed with status {rc}")
+        return y, s
+
+
 _default = None
 
 
@@ -125,3 +157,7 @@ def gemm(A, B, rows=None, threads=None):
 
 def gemv(A, x, threads=None):
     return load().gemv(A, x, threads=threads)
+
+
+def conv2d(x, w, stride=(1, 1), pad=(0, 0), dilation=(1, 1), threads=None):
+    return load().conv2d(x, w, stride, pad, dilation, threads=threads)

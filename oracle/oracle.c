@@ -19,6 +19,10 @@
  *         A is M x N row-major, x has N entries, y has M entries.
  *         ("Matrix Operations", section "Matrix-Vector Multiplication".)
  *
+ *   CONV  the 2-D convolution of a convolutional layer, from its usual definition
+ *         (see oracle_conv2d_f64 below; the pages only say it can be recast as a
+ *         matrix product).
+ *
  * Arithmetic. Every input is an fp32 value widened to fp64. The product of two
  * fp32 values has at most 48 significant bits, so it is exact in fp64; only the
  * additions round (round-to-nearest-even). Each output is summed in ascending
@@ -207,6 +211,109 @@ int oracle_gemv_f64(int64_t M, int64_t N, const float *A, int64_t lda,
         started = t;
     }
     if (rc == ORACLE_OK) gemv_rows(&jobs[0]);
+    for (int t = 1; t <= started; ++t) pthread_join(tid[t], NULL);
+    free(jobs);
+    free(tid);
+    return rc;
+}
+
+/* ------------------------------------------------------------- convolution --- */
+
+/*
+ * oracle_conv2d_f64: the 2-D convolution (cross-correlation) that a convolutional
+ * layer computes, written out from its definition. The pages only say that the core
+ * of a convolutional layer can be recast as a matrix product ("Matrix Operations",
+ * Introduction; "GPU Matrix Multiplication: Tiling and Shared Memory", closing
+ * preview of im2col); the definition used is the usual one:
+ *
+ *   y[n][k][p][q] = sum over c < C, r < R, s < S of
+ *                   x[n][c][p*sh + r*dh - ph][q*sw + s*dw - pw] * w[k][c][r][s]
+ *
+ * with x taken as 0 outside 0 <= h < H, 0 <= w < W, and P = (H + 2 ph - dh (R - 1) - 1)
+ * / sh + 1, Q likewise (integer division; P, Q >= 1 here). Layouts, all packed:
+ * x is N x C x H x W, w is K x C x R x S, y and s_out are N x K x P x Q. Each output
+ * is summed in fp64 in ascending (c, r, s) order; s_out gets the sum of |products|.
+ */
+struct conv_job {
+    int64_t C, H, W, K, R, S, sh, sw, ph, pw, dh, dw, P, Q;
+    const float *x, *w;
+    double *y, *s;
+    int64_t nk0, nk1; /* this job's (image, filter) pairs, n * K + k in [nk0, nk1) */
+};
+
+static void conv_pairs(const struct conv_job *jb)
+{
+    for (int64_t nk = jb->nk0; nk < jb->nk1; ++nk) {
+        const int64_t n = nk / jb->K, k = nk % jb->K;
+        const float *xn = jb->x + n * jb->C * jb->H * jb->W;
+        const float *wk = jb->w + k * jb->C * jb->R * jb->S;
+        double *yo = jb->y + nk * jb->P * jb->Q;
+        double *so = jb->s ? jb->s + nk * jb->P * jb->Q : NULL;
+        for (int64_t p = 0; p < jb->P; ++p)
+            for (int64_t q = 0; q < jb->Q; ++q) {
+                double acc = 0.0; /* the output, in fp64 */
+                double mag = 0.0; /* sum of |products| */
+                for (int64_t c = 0; c < jb->C; ++c)
+                    for (int64_t r = 0; r < jb->R; ++r)
+                        for (int64_t s = 0; s < jb->S; ++s) {
+                            const int64_t h = p * jb->sh + r * jb->dh - jb->ph;
+                            const int64_t v = q * jb->sw + s * jb->dw - jb->pw;
+                            if (h < 0 || h >= jb->H || v < 0 || v >= jb->W) continue;
+                            const double prod = (double)xn[(c * jb->H + h) * jb->W + v] *
+                                                (double)wk[(c * jb->R + r) * jb->S + s];
+                            acc += prod;
+                            mag += fabs(prod);
+                        }
+                yo[p * jb->Q + q] = acc;
+                if (so) so[p * jb->Q + q] = mag;
+            }
+    }
+}
+
+static void *conv_thread(void *arg)
+{
+    conv_pairs((const struct conv_job *)arg);
+    return NULL;
+}
+
+int oracle_conv2d_f64(int64_t N, int64_t C, int64_t H, int64_t W, int64_t K, int64_t R,
+                      int64_t S, int64_t sh, int64_t sw, int64_t ph, int64_t pw, int64_t dh,
+                      int64_t dw, const float *x, const float *w, double *y, double *s,
+                      int threads)
+{
+    if (N < 0 || C < 0 || H < 0 || W < 0 || K < 0 || R < 1 || S < 1 || sh < 1 || sw < 1 ||
+        ph < 0 || pw < 0 || dh < 1 || dw < 1)
+        return ORACLE_BAD_ARG;
+    const int64_t P = (H + 2 * ph - dh * (R - 1) - 1) / sh + 1;
+    const int64_t Q = (W + 2 * pw - dw * (S - 1) - 1) / sw + 1;
+    if (H + 2 * ph - dh * (R - 1) - 1 < 0 || W + 2 * pw - dw * (S - 1) - 1 < 0) return ORACLE_BAD_ARG;
+    const int64_t pairs = N * K;
+    if (pairs == 0 || P * Q == 0) return ORACLE_OK;
+    if (!y || (C > 0 && (!x || !w))) return ORACLE_BAD_ARG;
+    if (threads < 1) threads = 1;
+    if (threads > pairs) threads = (int)pairs;
+
+    struct conv_job *jobs = calloc((size_t)threads, sizeof *jobs);
+    pthread_t *tid = calloc((size_t)threads, sizeof *tid);
+    if (!jobs || !tid) {
+        free(jobs);
+        free(tid);
+        return ORACLE_THREAD_FAIL;
+    }
+    for (int t = 0; t < threads; ++t) {
+        struct conv_job jb = {C, H, W, K, R, S, sh, sw, ph, pw, dh, dw, P, Q, x, w, y, s,
+                              pairs * t / threads, pairs * (t + 1) / threads};
+        jobs[t] = jb;
+    }
+    int started = 0, rc = ORACLE_OK;
+    for (int t = 1; t < threads; ++t) {
+        if (pthread_create(&tid[t], NULL, conv_thread, &jobs[t]) != 0) {
+            rc = ORACLE_THREAD_FAIL;
+            break;
+        }
+        started = t;
+    }
+    if (rc == ORACLE_OK) conv_pairs(&jobs[0]);
     for (int t = 1; t <= started; ++t) pthread_join(tid[t], NULL);
     free(jobs);
     free(tid);

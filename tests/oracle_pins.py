@@ -321,5 +321,110 @@ def pin_page_operation_counts(orc):
     assert int(C.sum()) == sq["value"]
 
 
+
+
+# ---------------------------------------------------------------- convolution
+
+def _brute_int_conv(x, w, stride, pad, dil):
+    """Exact Python-int convolution from the definition (independent of the C code)."""
+    N, C, H, W = x.shape
+    K, _, R, S = w.shape
+    sh, sw = stride
+    ph, pw = pad
+    dh, dw = dil
+    P = (H + 2 * ph - dh * (R - 1) - 1) // sh + 1
+    Q = (W + 2 * pw - dw * (S - 1) - 1) // sw + 1
+    xi = x.astype(np.int64).tolist()
+    wi = w.astype(np.int64).tolist()
+    y = np.zeros((N, K, P, Q))
+    s = np.zeros((N, K, P, Q))
+    for n in range(N):
+        for k in range(K):
+            for p in range(P):
+                for q in range(Q):
+                    acc = mag = 0
+                    for c in range(C):
+                        for r in range(R):
+                            for t in range(S):
+                                h, v = p * sh + r * dh - ph, q * sw + t * dw - pw
+                                if 0 <= h < H and 0 <= v < W:
+                                    prod = xi[n][c][h][v] * wi[k][c][r][t]
+                                    acc += prod
+                                    mag += abs(prod)
+                    y[n, k, p, q] = acc
+                    s[n, k, p, q] = mag
+    return y, s
+
+
+def pin_conv_golden(orc):
+    """Hand-worked convolutions (tests/golden/conv_examples.json) are reproduced exactly."""
+    for case in _golden("conv_examples.json")["cases"]:
+        y, _ = orc.conv2d(np.array(case["x"], np.float32), np.array(case["w"], np.float32),
+                          case["stride"], case["pad"], case["dilation"], threads=1)
+        assert np.array_equal(y, np.array(case["y"], np.float64)), case["name"]
+
+
+def pin_conv_bruteforce_int(orc):
+    """Integer convolutions over strides, paddings and dilations equal an exact loop."""
+    cases = [((2, 3, 7, 6), (4, 3, 3, 3), (1, 1), (1, 1), (1, 1)),
+             ((1, 2, 9, 8), (3, 2, 3, 2), (2, 3), (1, 0), (1, 1)),
+             ((2, 1, 8, 8), (2, 1, 3, 3), (1, 2), (2, 2), (2, 3)),
+             ((1, 4, 5, 5), (2, 4, 1, 1), (1, 1), (0, 0), (1, 1)),
+             ((1, 2, 4, 6), (1, 2, 4, 6), (1, 1), (0, 0), (1, 1))]
+    for t, (xs, ws, st, pd, dl) in enumerate(cases):
+        x = _ints(300 + t, xs)
+        w = _ints(400 + t, ws)
+        y, s = orc.conv2d(x, w, st, pd, dl, threads=3)
+        yw, sw = _brute_int_conv(x, w, st, pd, dl)
+        assert np.array_equal(y, yw) and np.array_equal(s, sw), (xs, ws, st, pd, dl)
+
+
+def pin_conv_1x1_is_gemm(orc):
+    """A 1x1 convolution with stride 1 and no padding is, per image, the GEMM
+    W (K x C) times the image as a C x (H W) matrix."""
+    x = _floats(501, (2, 5, 6, 7))
+    w = _floats(502, (4, 5, 1, 1))
+    y, _ = orc.conv2d(x, w)
+    for n in range(2):
+        C64, _ = orc.gemm(w.reshape(4, 5), x[n].reshape(5, 42))
+        assert np.array_equal(y[n].reshape(4, 42), C64)
+
+
+def pin_conv_identity_and_delta(orc):
+    """A centred delta filter (w[k][c] = delta_kc at the centre, padding 1) returns the
+    input; a one-hot input returns the filter, mirrored into place."""
+    x = _floats(503, (1, 3, 6, 5))
+    w = np.zeros((3, 3, 3, 3), np.float32)
+    for c in range(3):
+        w[c, c, 1, 1] = 1
+    y, _ = orc.conv2d(x, w, pad=(1, 1))
+    assert np.array_equal(y, x.astype(np.float64))
+    xs = np.zeros((1, 1, 7, 7), np.float32)
+    xs[0, 0, 3, 3] = 1
+    wf = _floats(504, (1, 1, 3, 3))
+    y, _ = orc.conv2d(xs, wf)   # P = Q = 5; output (p,q) sees tap (3-p, 3-q)
+    want = np.zeros((5, 5))
+    for p in range(5):
+        for q in range(5):
+            r, t = 3 - p, 3 - q
+            if 0 <= r < 3 and 0 <= t < 3:
+                want[p, q] = wf[0, 0, r, t]
+    assert np.array_equal(y[0, 0], want)
+
+
+def pin_conv_all_ones_counts_taps(orc):
+    """All-ones input and filter: each output counts the filter taps that land inside
+    the padded image, C * (rows inside) * (columns inside)."""
+    C, H, W, R, S = 3, 6, 5, 3, 4
+    y, s = orc.conv2d(np.ones((1, C, H, W), np.float32), np.ones((2, C, R, S), np.float32),
+                      stride=(2, 1), pad=(1, 2))
+    P, Q = y.shape[2:]
+    for p in range(P):
+        rows = sum(1 for r in range(R) if 0 <= p * 2 + r - 1 < H)
+        for q in range(Q):
+            cols = sum(1 for t in range(S) if 0 <= q + t - 2 < W)
+            assert y[0, 0, p, q] == C * rows * cols == s[0, 1, p, q]
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]
 CHEAP_PINS = [p for p in ALL_PINS if p is not pin_page_operation_counts]

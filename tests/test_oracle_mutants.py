@@ -49,6 +49,17 @@ MUTANTS = [
     ("gemv_row_stride_n", "const float *arow = jb->A + i * jb->lda;",
      "const float *arow = jb->A + i * jb->N;"),
     ("gemv_subtracts", "acc += p;", "acc -= p;"),
+    ("conv_no_low_padding_check", "if (h < 0 || h >= jb->H || v < 0 || v >= jb->W) continue;",
+     "if (h >= jb->H || v >= jb->W || h < 0) continue;"),
+    ("conv_ignores_stride", "const int64_t h = p * jb->sh + r * jb->dh - jb->ph;",
+     "const int64_t h = p + r * jb->dh - jb->ph;"),
+    ("conv_ignores_dilation", "const int64_t v = q * jb->sw + s * jb->dw - jb->pw;",
+     "const int64_t v = q * jb->sw + s - jb->pw;"),
+    ("conv_swaps_filter_axes", "(double)wk[(c * jb->R + r) * jb->S + s];",
+     "(double)wk[(c * jb->S + s) * jb->R + r];"),
+    ("conv_fp32_accumulator", "double acc = 0.0; /* the output, in fp64 */", "float acc = 0.0f;"),
+    ("conv_drops_last_channel", "for (int64_t c = 0; c < jb->C; ++c)\n                    for (int64_t r",
+     "for (int64_t c = 0; c < jb->C - 1; ++c)\n                    for (int64_t r"),
 ]
 
 CHILD = r"""
