@@ -17,12 +17,14 @@ Infinity Cache) gives the GEMV's HBM rate. Results are then verified against the
 CPU oracle (64+ sampled GEMM rows in full, every GEMV output) and the oracle's
 own time on a bounded sample of the same work is reported as `cpu_baseline`.
 
-Profiling helpers (same script, for rocprofv3 runs): --only gemm | gemv | copy | h16
-runs just that kernel `--steps` times with no oracle; `copy` is a plain
+Profiling helpers (same script, for rocprofv3 runs): --only gemm | gemv | copy | h16 |
+conv runs just that kernel `--steps` times with no oracle; `copy` is a plain
 device-to-device copy of known size used to calibrate HBM counters; `h16` is the
-bf16-input GEMM at the projection shape.
+bf16-input GEMM at the projection shape; `conv` the 3x3 convolution layer
+(N=32, C=K=128, 28x28).
 
-Sweeps (tables, not the benchmark line): --sweep gemm times every GEMM tile
+Sweeps (tables, not the benchmark line): --sweep conv times every convolution tile
+configuration on the layer workloads; --sweep gemm times every GEMM tile
 configuration on the workload shapes and a few others; --sweep gemv times the GEMV
 at N = 4096 for growing M, which separates its per-launch fixed cost from its
 streaming rate. Both time a run of back-to-back launches between two events on
@@ -49,17 +51,23 @@ from tiled_gemm_gemv_amd import roofline as rl  # noqa: E402
 METRIC = "fp32 GEMM TFLOP/s & % MFMA peak; GEMV GB/s & % HBM peak (1 MI355X)"
 GEMV_SETS = 8
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
-GEMM_SRC = os.path.join(ROOT, "tiled_gemm_gemv_amd", "csrc", "mm_gemm.hip")
-GEMV_SRC = os.path.join(ROOT, "tiled_gemm_gemv_amd", "csrc", "mm_gemv.hip")
+CSRC = os.path.join(ROOT, "tiled_gemm_gemv_amd", "csrc")
+# the sources of each kernel whose HBM traffic profiles/hbm_traffic.txt records
+GEMM_SRC = [os.path.join(CSRC, "mm_gemm.hip"), os.path.join(CSRC, "mm_gemm_tile.h")]
+GEMV_SRC = [os.path.join(CSRC, "mm_gemv.hip")]
 
 
 def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-def source_digest(path):
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+def source_digest(paths):
+    """First 16 hex digits of the sha256 of the files' bytes, concatenated in order."""
+    h = hashlib.sha256()
+    for path in paths:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def read_traffic():
@@ -110,9 +118,9 @@ def main():
     ap.add_argument("--gemv-reps", type=int, default=400)
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="target length of the oracle's timed sample")
-    ap.add_argument("--only", choices=["gemm", "gemv", "copy", "h16"], default=None,
+    ap.add_argument("--only", choices=["gemm", "gemv", "copy", "h16", "conv"], default=None,
                     help="profiling helper: launch only this kernel --steps times")
-    ap.add_argument("--sweep", choices=["gemm", "gemv", "h16"], default=None,
+    ap.add_argument("--sweep", choices=["gemm", "gemv", "h16", "conv"], default=None,
                     help="print a timing table instead of the benchmark line")
     args = ap.parse_args()
 
@@ -159,6 +167,16 @@ def main():
             mm.mm_gemm_bf16(M, N, K, A16, K, B16, N, C, N, stream)
         torch.cuda.synchronize()
         log(f"h16: {args.steps} bf16 launches")
+        return
+
+    if args.only == "conv":
+        # the 3x3 middle layer, in the configuration mm_conv2d_f32 chooses
+        cw = wl.CONV_WORKLOADS["conv3x3"]
+        x, f, y = conv_tensors(torch, cw, dev)
+        for _ in range(args.steps):
+            launch_conv(mm, cw, x, f, y, stream)
+        torch.cuda.synchronize()
+        log(f"conv: {args.steps} launches of {cw.describe()}")
         return
 
     log(f"generating inputs: {wg.describe()}, {wv.describe()}")
@@ -363,8 +381,76 @@ def burst_time_ms(torch, launch, reps):
     return e0.elapsed_time(e1) / reps
 
 
+def conv_tensors(torch, cw, dev):
+    """Device x, filters, y for a convolution workload (values from its distributions)."""
+    x_h, f_h = wl.conv_inputs(cw)
+    P, Q = cw.out_hw()
+    x = torch.from_numpy(x_h).to(dev)
+    f = torch.from_numpy(f_h).to(dev)
+    y = torch.empty((cw.N, cw.K, P, Q), dtype=torch.float32, device=dev)
+    return x, f, y
+
+
+def launch_conv(mm, cw, x, f, y, stream, cfg=None):
+    geo = (cw.N, cw.C, cw.H, cw.W, cw.K, cw.R, cw.S, *cw.stride, *cw.pad, *cw.dilation)
+    if cfg is None:
+        mm.mm_conv2d_f32(*geo, x, f, y, stream)
+    else:
+        mm.mm_conv2d_f32_config(cfg, *geo, x, f, y, stream)
+
+
+def sweep_conv(torch, mm, dev):
+    nc = mm.mm_conv2d_f32_num_configs()
+    peak = rl.MI355X_FP32_MFMA_PEAK
+    print("# fp32 convolution (implicit GEMM), TFLOP/s per tile configuration (back-to-back "
+          "launches between two events)")
+    for c in range(nc):
+        print(f"#   cfg {c}: {mm.mm_conv2d_f32_config_name(c)}")
+    print("#   default = mm_conv2d_f32's own choice (* marks that tile among the configs; "
+          "1x1 layers on large maps go to the batched GEMM and its own choice)")
+    print("#   dense = mm_gemm_f32 on the same M x N x K with the im2col matrix already in "
+          "memory (what the gather costs, not counting writing that matrix)")
+    print("#   bound = min(fp32 MFMA peak, algorithmic FLOP/byte x 8 TB/s); % = default / bound")
+    print(f"{'workload':>12s} {'GEMM M':>7s} {'GEMM N':>8s} {'GEMM K':>7s} {'GFLOP':>7s}  " +
+          " ".join(f"{'cfg' + str(c):>7s}" for c in range(nc)) +
+          f" {'default':>8s} {'dense':>7s} {'bound':>7s} {'%':>6s}")
+    for cw in wl.CONV_WORKLOADS.values():
+        x, f, y = conv_tensors(torch, cw, dev)
+        P, Q = cw.out_hw()
+        flop = rl.conv_flops(cw.N, cw.C, cw.K, cw.R, cw.S, P, Q)
+        by = rl.conv_algorithmic_bytes(cw.N, cw.C, cw.H, cw.W, cw.K, cw.R, cw.S, P, Q)
+        bound = min(peak, flop / by * rl.MI355X_HBM_PEAK)
+        reps = max(3, min(200, int(2e11 / flop)))
+        sel = mm.mm_conv2d_f32_select(cw.K, cw.N * P * Q)
+        cells = []
+        for c in range(nc):
+            def launch(i, st, c=c):
+                launch_conv(mm, cw, x, f, y, st, c)
+            tf = flop / burst_time_ms(torch, launch, reps) / 1e9
+            cells.append(f"{tf:6.1f}" + ("*" if c == sel else " "))
+
+        def launch_default(i, st):
+            launch_conv(mm, cw, x, f, y, st)
+        td = flop / burst_time_ms(torch, launch_default, reps) / 1e9
+        del x, y
+        GM, GN, GK = cw.K, cw.N * P * Q, cw.C * cw.R * cw.S
+        Bd = torch.randn(GK, GN, device=dev)
+        Cd = torch.empty(GM, GN, device=dev)
+
+        def launch_dense(i, st):
+            mm.mm_gemm_f32(GM, GN, GK, f, GK, Bd, GN, Cd, GN, st)
+        tdense = flop / burst_time_ms(torch, launch_dense, reps) / 1e9
+        print(f"{cw.name:>12s} {GM:7d} {GN:8d} {GK:7d} "
+              f"{flop / 1e9:7.2f}  " + " ".join(cells) +
+              f" {td:8.1f} {tdense:7.1f} {bound / 1e12:7.1f} {100 * td * 1e12 / bound:6.1f}",
+              flush=True)
+        del f, Bd, Cd
+
+
 def sweep(kind, torch, mm, dev):
-    if kind == "gemm":
+    if kind == "conv":
+        sweep_conv(torch, mm, dev)
+    elif kind == "gemm":
         shapes = [(w.M, w.N, w.K, w.name) for w in wl.WORKLOADS.values() if w.op == "gemm"]
         shapes += [(512, 512, 512, ""), (2048, 2048, 2048, ""), (4096, 4096, 4096, ""),
                    (8192, 1792, 4096, "projection, 1/8 of N")]

@@ -16,6 +16,8 @@
  *         A is M x N, x has N entries, y has M entries.
  *         ("Matrix Operations", section "Matrix-Vector Multiplication".)
  *
+ *   CONV  2-D convolution through the GEMM (mm_conv2d_f32 below).
+ *
  * Conventions shared by every entry point:
  *   - Layout: row-major. Element (i, k) of A lives at A[i * lda + k], (k, j) of B
  *     at B[k * ldb + j], (i, j) of C at C[i * ldc + j]. The pages lay matrices out
@@ -173,6 +175,66 @@ int mm_gemm_f16_config(int cfg, int64_t M, int64_t N, int64_t K,
                        const uint16_t *A, int64_t lda,
                        const uint16_t *B, int64_t ldb,
                        float *C, int64_t ldc, void *stream);
+
+/*
+ * mm_conv2d_f32: 2-D convolution (cross-correlation, as in neural networks) in fp32,
+ * lowered to the GEMM by im2col ("Matrix Operations", Introduction: a convolutional
+ * layer's core recast as a matrix product; "GPU Matrix Multiplication: Tiling and
+ * Shared Memory", closing preview of im2col). The pages give no formula; the one
+ * computed is the usual definition
+ *
+ *   y[n][k][p][q] = sum over c < C, r < R, s < S of
+ *                   w[k][c][r][s] * x[n][c][p*sh + r*dh - ph][q*sw + s*dw - pw]
+ *
+ * with x read as 0 at rows outside [0, H) and columns outside [0, W) (zero padding),
+ * and the output size P = (H + 2 ph - dh (R - 1) - 1) / sh + 1, Q = (W + 2 pw -
+ * dw (S - 1) - 1) / sw + 1 (integer division; see mm_conv2d_out_dim).
+ *   N, C, H, W     images, channels, input height, width; >= 0.
+ *   K, R, S        filters, filter height, width; K >= 0, R, S >= 1.
+ *   sh, sw         strides >= 1; ph, pw: zero padding >= 0; dh, dw: dilation >= 1.
+ *   x              N x C x H x W, packed (NCHW). May be NULL if it has no elements.
+ *   w              K x C x R x S, packed. May be NULL if it has no elements.
+ *   y              N x K x P x Q, packed, written. May be NULL if it has no elements.
+ * Products are fp32, accumulated in fp32 on the matrix cores in an order of the
+ * kernel's choosing; the im2col matrix is gathered on the fly, never stored, so no
+ * workspace is used. C == 0: y is filled with zeros. No output elements: nothing is
+ * enqueued.
+ * Errors: MM_ERR_INVALID_ARG for a negative size, a stride, dilation or filter size
+ * below 1, negative padding, a filter that does not fit the padded input (P or Q
+ * would be below 1), a NULL or unaligned pointer that is used, or sizes beyond the
+ * limits: one image (C H W), C R S and P Q at most 2^31 - 1; H + 2 ph, W + 2 pw,
+ * dh (R - 1), dw (S - 1) below 2^29. Other errors as for mm_gemm_f32.
+ */
+int mm_conv2d_f32(int64_t N, int64_t C, int64_t H, int64_t W,
+                  int64_t K, int64_t R, int64_t S,
+                  int64_t sh, int64_t sw, int64_t ph, int64_t pw, int64_t dh, int64_t dw,
+                  const float *x, const float *w, float *y, void *stream);
+
+/*
+ * mm_conv2d_out_dim: the output extent along one axis, (in + 2 pad - dil (filter - 1)
+ * - 1) / stride + 1, or -1 if an argument is out of range (in < 0, filter < 1,
+ * stride < 1, pad < 0, dil < 1, or any above 2^29) or the dilated filter is longer
+ * than the padded input.
+ */
+int64_t mm_conv2d_out_dim(int64_t in, int64_t filter, int64_t stride, int64_t pad,
+                          int64_t dil);
+
+/*
+ * Tile configurations of the convolution (tile shapes of the GEMM, with an im2col
+ * gather in place of the B loads), as for the GEMM:
+ *   mm_conv2d_f32_num_configs, mm_conv2d_f32_config_name(cfg): count and names;
+ *   mm_conv2d_f32_select: the config mm_conv2d_f32 would use for the product of K
+ *     filters by N * P * Q output positions;
+ *   mm_conv2d_f32_config: mm_conv2d_f32 forced to config `cfg` (MM_ERR_INVALID_ARG
+ *     if out of range). Every config is correct for every shape.
+ */
+int mm_conv2d_f32_num_configs(void);
+const char *mm_conv2d_f32_config_name(int cfg);
+int mm_conv2d_f32_select(int64_t K, int64_t NPQ);
+int mm_conv2d_f32_config(int cfg, int64_t N, int64_t C, int64_t H, int64_t W,
+                         int64_t K, int64_t R, int64_t S,
+                         int64_t sh, int64_t sw, int64_t ph, int64_t pw, int64_t dh, int64_t dw,
+                         const float *x, const float *w, float *y, void *stream);
 
 /* mm_status_string: static text for a status code (never NULL). */
 const char *mm_status_string(int status);

@@ -154,3 +154,95 @@ def test_workload_accounting():
     assert abs(rl.gemm_bound_time(8192, 14336, 4096) - 6.116e-3) < 1e-5
     assert abs(rl.gemv_bound_time(4096, 4096) - 8.393e-6) < 1e-8
     assert abs(rl.MI355X_CUS * 256 * rl.MI355X_PEAK_SCLK_HZ - rl.MI355X_FP32_MFMA_PEAK) < 0.1e12
+
+
+# ------------------------------------------------------------------ convolution
+
+def _out_dim(i, f, st, p, d):
+    return (i + 2 * p - d * (f - 1) - 1) // st + 1
+
+
+def test_conv_out_dim(lib):
+    for i, f, st, p, d in [(28, 3, 1, 1, 1), (56, 3, 2, 1, 1), (224, 7, 2, 3, 1), (64, 3, 1, 2, 2),
+                           (5, 5, 1, 0, 1), (1, 1, 1, 0, 1), (7, 3, 3, 0, 2), (0, 1, 1, 1, 1),
+                           (10, 4, 3, 5, 3)]:
+        assert mm.mm_conv2d_out_dim(i, f, st, p, d) == _out_dim(i, f, st, p, d) >= 1
+    # the dilated filter longer than the padded input, and arguments out of range
+    for args in [(4, 5, 1, 0, 1), (4, 3, 1, 0, 2), (0, 1, 1, 0, 1), (0, 3, 1, 1, 1), (-1, 1, 1, 0, 1), (4, 0, 1, 0, 1),
+                 (4, 1, 0, 0, 1), (4, 1, 1, -1, 1), (4, 1, 1, 0, 0), (1 << 29, 1, 1, 0, 1),
+                 (8, 3, 1, 1 << 28, 1), (8, 1 << 29, 1, 0, 1)]:
+        assert mm.mm_conv2d_out_dim(*args) == -1, args
+
+
+def test_conv_config_table(lib):
+    n = mm.mm_conv2d_f32_num_configs()
+    assert n >= 1
+    names = [mm.mm_conv2d_f32_config_name(i) for i in range(n)]
+    assert all(names) and len(set(names)) == n
+    gemm_names = [mm.mm_gemm_f32_config_name(i) for i in range(mm.mm_gemm_f32_num_configs())]
+    assert all(name in gemm_names for name in names)   # tile shapes of the GEMM
+    assert mm.mm_conv2d_f32_config_name(n) is None
+    for K, NPQ in [(1, 1), (64, 401408), (128, 25088), (256, 25088), (7, 286), (4096, 1 << 30)]:
+        assert 0 <= mm.mm_conv2d_f32_select(K, NPQ) < n
+
+
+# N, C, H, W, K, R, S, sh, sw, ph, pw, dh, dw
+GOOD = (2, 3, 8, 8, 4, 3, 3, 1, 1, 1, 1, 1, 1)
+
+
+def _conv(lib, geo, x=FAKE, w=FAKE, y=FAKE, cfg=None):
+    if cfg is None:
+        return lib.mm_conv2d_f32(*geo, x, w, y, None)
+    return lib.mm_conv2d_f32_config(cfg, *geo, x, w, y, None)
+
+
+@pytest.mark.parametrize("change,why", [
+    ({0: -1}, "negative size"), ({1: -1}, "negative size"), ({4: -3}, "negative size"),
+    ({5: 0}, "filter size"), ({6: 0}, "filter size"),
+    ({7: 0}, "stride"), ({8: -1}, "stride"),
+    ({9: -1}, "padding"), ({10: -2}, "padding"),
+    ({11: 0}, "dilation"), ({12: 0}, "dilation"),
+    ({5: 9, 9: 0}, "does not fit"), ({6: 5, 10: 0, 12: 3}, "does not fit"),
+    ({2: 1 << 29}, "2^29"), ({9: 1 << 28}, "2^29"), ({5: 3, 11: 1 << 28, 2: 1 << 28}, "2^29"),
+    ({1: 1 << 16, 2: 256, 3: 128}, "C * H * W"),
+    ({1: 1 << 25, 2: 7, 3: 7, 5: 9, 6: 9}, "C * R * S"),
+    ({2: 50000, 3: 50000, 9: 0, 10: 0, 5: 1, 6: 1}, "P * Q"),
+])
+def test_conv_rejects_invalid_arguments(lib, change, why):
+    geo = list(GOOD)
+    for k, v in change.items():
+        geo[k] = v
+    assert _conv(lib, geo) == mm.MM_ERR_INVALID_ARG
+    assert why in mm.mm_last_error(), mm.mm_last_error()
+
+
+def test_conv_rejects_bad_pointers_and_config(lib):
+    for kw, why in [({"x": None}, "x is NULL"), ({"w": None}, "w is NULL"),
+                    ({"y": None}, "y is NULL"), ({"x": FAKE + 2}, "aligned")]:
+        assert _conv(lib, GOOD, **kw) == mm.MM_ERR_INVALID_ARG
+        assert why in mm.mm_last_error()
+    n = mm.mm_conv2d_f32_num_configs()
+    for cfg in (-1, n):
+        assert _conv(lib, GOOD, cfg=cfg) == mm.MM_ERR_INVALID_ARG
+    with pytest.raises(mm.MMError):
+        mm.mm_conv2d_f32(*GOOD[:7], 0, 1, 1, 1, 1, 1, FAKE, FAKE, FAKE, stream=1)
+
+
+def test_conv_without_outputs_enqueues_nothing(lib):
+    # N == 0 or K == 0: no output element, so no HIP call, even with NULL pointers
+    geo = list(GOOD)
+    geo[0] = 0
+    assert _conv(lib, geo, x=None, y=None) == mm.MM_OK
+    geo = list(GOOD)
+    geo[4] = 0
+    assert _conv(lib, geo, w=None, y=None) == mm.MM_OK
+
+
+def test_conv_accounting():
+    P, Q = rl.conv_out_hw(224, 224, 7, 7, (2, 2), (3, 3))
+    assert (P, Q) == (112, 112)
+    assert rl.conv_flops(32, 3, 64, 7, 7, P, Q) == 2 * 64 * (32 * 112 * 112) * 147
+    assert rl.conv_algorithmic_bytes(1, 2, 5, 5, 3, 3, 3, 3, 3) == 4 * (50 + 54 + 27)
+    assert rl.im2col_matrix_bytes(1, 2, 3, 3, 3, 3) == 4 * 18 * 9
+    # a 1x1 convolution of one image is the GEMM of its filters with its C x HW matrix
+    assert rl.conv_flops(1, 256, 64, 1, 1, 56, 56) == rl.gemm_flops(64, 56 * 56, 256)

@@ -6,7 +6,7 @@ the library's HIP kernels. Pointer arguments accept a device address (int) or a
 torch tensor on the GPU; `stream` accepts a hipStream_t address (int), a
 torch.cuda.Stream, or None for torch's current stream on the current device.
 
-gemm(A, B, out=None) and gemv(A, x, out=None) are conveniences for torch tensors:
+gemm(A, B, out=None), gemv(A, x, out=None), conv2d(x, w, ...) etc. are conveniences for torch tensors:
 they check dtypes, devices and strides, allocate the output with torch when none
 is given, and call the C entry points. PyTorch only provides device memory and
 streams here.
@@ -86,6 +86,19 @@ def load():
     lib.mm_gemv_t_f32.argtypes = [i64, i64, vp, vp, vp, vp]
     lib.mm_gemv_t_f32.restype = ci
     lib.mm_gemv_f32.restype = ci
+    conv_args = [i64] * 13 + [vp, vp, vp, vp]
+    lib.mm_conv2d_f32.argtypes = conv_args
+    lib.mm_conv2d_f32.restype = ci
+    lib.mm_conv2d_f32_config.argtypes = [ci] + conv_args
+    lib.mm_conv2d_f32_config.restype = ci
+    lib.mm_conv2d_out_dim.argtypes = [i64] * 5
+    lib.mm_conv2d_out_dim.restype = i64
+    lib.mm_conv2d_f32_num_configs.argtypes = []
+    lib.mm_conv2d_f32_num_configs.restype = ci
+    lib.mm_conv2d_f32_config_name.argtypes = [ci]
+    lib.mm_conv2d_f32_config_name.restype = ctypes.c_char_p
+    lib.mm_conv2d_f32_select.argtypes = [i64, i64]
+    lib.mm_conv2d_f32_select.restype = ci
     lib.mm_status_string.argtypes = [ci]
     lib.mm_status_string.restype = ctypes.c_char_p
     lib.mm_last_error.argtypes = []
@@ -211,6 +224,37 @@ def mm_gemm_f32_config_name(cfg):
 
 def mm_gemm_f32_select(M, N, K):
     return load().mm_gemm_f32_select(M, N, K)
+
+
+def mm_conv2d_f32(N, C, H, W, K, R, S, sh, sw, ph, pw, dh, dw, x, w, y, stream=None):
+    """2-D convolution, x N x C x H x W, w K x C x R x S, y N x K x P x Q (packed).
+    Raises MMError."""
+    lib = load()
+    _check(lib.mm_conv2d_f32(N, C, H, W, K, R, S, sh, sw, ph, pw, dh, dw, _addr(x), _addr(w),
+                             _addr(y), _stream(stream)), "mm_conv2d_f32")
+
+
+def mm_conv2d_f32_config(cfg, N, C, H, W, K, R, S, sh, sw, ph, pw, dh, dw, x, w, y, stream=None):
+    lib = load()
+    _check(lib.mm_conv2d_f32_config(cfg, N, C, H, W, K, R, S, sh, sw, ph, pw, dh, dw, _addr(x),
+                                    _addr(w), _addr(y), _stream(stream)), "mm_conv2d_f32_config")
+
+
+def mm_conv2d_out_dim(in_, filter_, stride, pad, dil):
+    return load().mm_conv2d_out_dim(in_, filter_, stride, pad, dil)
+
+
+def mm_conv2d_f32_num_configs():
+    return load().mm_conv2d_f32_num_configs()
+
+
+def mm_conv2d_f32_config_name(cfg):
+    name = load().mm_conv2d_f32_config_name(cfg)
+    return name.decode() if name is not None else None
+
+
+def mm_conv2d_f32_select(K, NPQ):
+    return load().mm_conv2d_f32_select(K, NPQ)
 
 
 def mm_status_string(status):
@@ -352,4 +396,38 @@ def gemv_t(A, x, out=None, stream=None):
         raise ValueError(f"out must be a contiguous float32 vector of {N} entries")
     with torch.cuda.device(A.device):
         mm_gemv_t_f32(M, N, A, x, out, stream)
+    return out
+
+
+def conv2d(x, w, stride=(1, 1), pad=(0, 0), dilation=(1, 1), out=None, config=None, stream=None):
+    """out = the 2-D convolution of x (N x C x H x W) with w (K x C x R x S), both
+    contiguous fp32 GPU tensors; out is N x K x P x Q (allocated if not given)."""
+    import torch
+    for t, name in ((x, "x"), (w, "w")):
+        if not isinstance(t, torch.Tensor) or t.dtype != torch.float32 or t.dim() != 4:
+            raise TypeError(f"{name} must be a 4-D float32 tensor")
+        if t.device.type != "cuda" or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous GPU tensor")
+    if w.device != x.device:
+        raise ValueError("x and w are on different devices")
+    N, C, H, W = x.shape
+    K, C2, R, S = w.shape
+    if C2 != C:
+        raise ValueError(f"channel counts differ: x has {C}, w has {C2}")
+    (sh, sw), (ph, pw), (dh, dw) = stride, pad, dilation
+    P = mm_conv2d_out_dim(H, R, sh, ph, dh)
+    Q = mm_conv2d_out_dim(W, S, sw, pw, dw)
+    if P < 1 or Q < 1:
+        raise ValueError("invalid convolution geometry (the filter must fit the padded input)")
+    if out is None:
+        out = torch.empty((N, K, P, Q), dtype=torch.float32, device=x.device)
+    if (out.dtype != torch.float32 or tuple(out.shape) != (N, K, P, Q) or not out.is_contiguous()
+            or out.device != x.device):
+        raise ValueError(f"out must be a contiguous float32 tensor of shape {(N, K, P, Q)}")
+    with torch.cuda.device(x.device):
+        if config is None:
+            mm_conv2d_f32(N, C, H, W, K, R, S, sh, sw, ph, pw, dh, dw, x, w, out, stream)
+        else:
+            mm_conv2d_f32_config(config, N, C, H, W, K, R, S, sh, sw, ph, pw, dh, dw, x, w, out,
+                                 stream)
     return out

@@ -149,6 +149,78 @@ int run_gemm16(int cfg, bool bf16, int64_t M, int64_t N, int64_t K, const uint16
                                                        (int)N, (int)K, s));
 }
 
+constexpr int64_t kConvMaxGeom = int64_t(1) << 29;
+
+// Output extent along one axis, or -1 (arguments as for mm_conv2d_out_dim).
+int64_t conv_out_dim(int64_t in, int64_t filter, int64_t stride, int64_t pad, int64_t dil)
+{
+    if (in < 0 || filter < 1 || stride < 1 || pad < 0 || dil < 1) return -1;
+    if (in >= kConvMaxGeom || filter >= kConvMaxGeom || stride >= kConvMaxGeom ||
+        pad >= kConvMaxGeom || dil >= kConvMaxGeom)
+        return -1;
+    const int64_t span = dil * (filter - 1);  // < 2^58
+    const int64_t padded = in + 2 * pad;
+    if (span >= kConvMaxGeom || padded >= kConvMaxGeom) return -1;
+    if (padded - span - 1 < 0) return -1;
+    return (padded - span - 1) / stride + 1;
+}
+
+int run_conv(int cfg, int64_t N, int64_t C, int64_t H, int64_t W, int64_t K, int64_t R,
+             int64_t S, int64_t sh, int64_t sw, int64_t ph, int64_t pw, int64_t dh, int64_t dw,
+             const float *x, const float *w, float *y, void *stream)
+{
+    if (N < 0 || C < 0 || H < 0 || W < 0 || K < 0) return invalid("negative size");
+    if (R < 1 || S < 1) return invalid("filter size below 1");
+    if (sh < 1 || sw < 1) return invalid("stride below 1");
+    if (ph < 0 || pw < 0) return invalid("negative padding");
+    if (dh < 1 || dw < 1) return invalid("dilation below 1");
+    const int64_t P = conv_out_dim(H, R, sh, ph, dh), Q = conv_out_dim(W, S, sw, pw, dw);
+    if (P < 0 || Q < 0) {
+        if (H + 2 * ph >= kConvMaxGeom || W + 2 * pw >= kConvMaxGeom || R >= kConvMaxGeom ||
+            S >= kConvMaxGeom || dh >= kConvMaxGeom || dw >= kConvMaxGeom ||
+            sh >= kConvMaxGeom || sw >= kConvMaxGeom || dh * (R - 1) >= kConvMaxGeom ||
+            dw * (S - 1) >= kConvMaxGeom)
+            return invalid("convolution geometry above 2^29");
+        return invalid("filter does not fit the padded input");
+    }
+    if (K > kMaxDim || N > kMaxDim || C > kMaxDim) return invalid("size above 2^31 - 1");
+    const int64_t HW = H * W, PQ = P * Q;  // each below 2^58
+    if (PQ > kMaxDim) return invalid("P * Q above 2^31 - 1");
+    if (C > 0 && HW > kMaxDim / C) return invalid("C * H * W above 2^31 - 1");
+    if (C > 0 && R * S > kMaxDim / C) return invalid("C * R * S above 2^31 - 1");
+    const int64_t limit = INT64_MAX / 4;
+    const int64_t CHW = C * HW, CRS = C * R * S;
+    if (N > 0 && CHW > limit / N) return invalid("x extent overflows");
+    if (K > 0 && PQ > 0 && N > limit / K / PQ) return invalid("y extent overflows");
+    const bool has_x = N > 0 && CHW > 0, has_w = K > 0 && CRS > 0, has_y = N > 0 && K > 0;
+    if (has_x && !x) return invalid("x is NULL");
+    if (has_w && !w) return invalid("w is NULL");
+    if (has_y && !y) return invalid("y is NULL");
+    if ((uintptr_t)x % 4 || (uintptr_t)w % 4 || (uintptr_t)y % 4)
+        return invalid("pointer not aligned to its element size");
+    if (!has_y) return MM_OK;  // P, Q >= 1 here, so no output means N or K is 0
+    mm::ConvArgs a;
+    a.N = N;
+    a.C = C;
+    a.H = H;
+    a.W = W;
+    a.K = K;
+    a.R = R;
+    a.S = S;
+    a.sh = sh;
+    a.sw = sw;
+    a.ph = ph;
+    a.pw = pw;
+    a.dh = dh;
+    a.dw = dw;
+    a.P = P;
+    a.Q = Q;
+    a.x = x;
+    a.w = w;
+    a.y = y;
+    return from_hip("conv2d launch", mm::conv_launch(cfg, a, static_cast<hipStream_t>(stream)));
+}
+
 }  // namespace
 
 extern "C" {
@@ -262,6 +334,37 @@ int mm_gemv_t_f32(int64_t M, int64_t N, const float *A, const float *x, float *y
     a.M = (int)M;
     a.N = (int)N;
     return from_hip("gemv_t launch", mm::gemv_t_launch(a, s));
+}
+
+int mm_conv2d_f32(int64_t N, int64_t C, int64_t H, int64_t W, int64_t K, int64_t R, int64_t S,
+                  int64_t sh, int64_t sw, int64_t ph, int64_t pw, int64_t dh, int64_t dw,
+                  const float *x, const float *w, float *y, void *stream)
+{
+    return run_conv(-1, N, C, H, W, K, R, S, sh, sw, ph, pw, dh, dw, x, w, y, stream);
+}
+
+int mm_conv2d_f32_config(int cfg, int64_t N, int64_t C, int64_t H, int64_t W, int64_t K,
+                         int64_t R, int64_t S, int64_t sh, int64_t sw, int64_t ph, int64_t pw,
+                         int64_t dh, int64_t dw, const float *x, const float *w, float *y,
+                         void *stream)
+{
+    if (cfg < 0 || cfg >= mm::conv_num_configs()) return invalid("config index out of range");
+    return run_conv(cfg, N, C, H, W, K, R, S, sh, sw, ph, pw, dh, dw, x, w, y, stream);
+}
+
+int64_t mm_conv2d_out_dim(int64_t in, int64_t filter, int64_t stride, int64_t pad, int64_t dil)
+{
+    return conv_out_dim(in, filter, stride, pad, dil);
+}
+
+int mm_conv2d_f32_num_configs(void) { return mm::conv_num_configs(); }
+
+const char *mm_conv2d_f32_config_name(int cfg) { return mm::conv_config_name(cfg); }
+
+int mm_conv2d_f32_select(int64_t K, int64_t NPQ)
+{
+    if (K < 0 || NPQ < 0) return 0;
+    return mm::conv_select_config(K, NPQ);
 }
 
 const char *mm_status_string(int status)

@@ -148,8 +148,11 @@ __global__ __launch_bounds__(T::NT) void gemm_h16_kernel(Gemm16Args p)
 
     const int tiles_m = (p.M + T::BM - 1) / T::BM;
     const int tiles_n = (p.N + T::BN - 1) / T::BN;
+    const int64_t tiles = (int64_t)tiles_m * tiles_n;
+    const int64_t bid = linear_block();
+    if (bid >= tiles) return;  // padding of a 2-D grid (whole workgroup, before any barrier)
     int tm, tn;
-    tile_of_block16(blockIdx.x, gridDim.x, tiles_m, tiles_n, tm, tn);
+    tile_of_block16((int)bid, (int)tiles, tiles_m, tiles_n, tm, tn);
     const int m0 = tm * T::BM, n0 = tn * T::BN;
 
     const int tid = threadIdx.x;
@@ -334,9 +337,11 @@ hipError_t launch16(const Gemm16Args &a, hipStream_t stream)
         fn = reinterpret_cast<const void *>(&gemm_h16_kernel<T, BF16, false, true>);
     else
         fn = reinterpret_cast<const void *>(&gemm_h16_kernel<T, BF16, false, false>);
+    unsigned gx, gy;
+    if (!grid_for(tiles, gx, gy)) return hipErrorInvalidConfiguration;
     Gemm16Args arg = a;
     void *args[] = {&arg};
-    return hipLaunchKernel(fn, dim3((unsigned)tiles), dim3(T::NT), args, 0, stream);
+    return hipLaunchKernel(fn, dim3(gx, gy), dim3(T::NT), args, 0, stream);
 }
 
 using T16L = Tile16<256, 256, 128, 64>;

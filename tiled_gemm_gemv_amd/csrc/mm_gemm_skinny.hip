@@ -50,14 +50,19 @@ template <int NB, int W, int U, bool VEC_A>
 __global__ __launch_bounds__(W * 64) void gemm_skinny_kernel(GemmArgs p)
 {
     __shared__ f32x4 partial[(W > 1 ? W - 1 : 1) * NB * 64];
+    // workgroup -> (row block, column block): row blocks vary fastest
+    const int64_t tiles_m = (p.M + kSkinnyRows - 1) / kSkinnyRows;
+    const int64_t tiles = tiles_m * ((p.N + kSkinnyCols - 1) / kSkinnyCols);
+    const int64_t bid = linear_block();
+    if (bid >= tiles) return;  // padding of a 2-D grid (whole workgroup, before any barrier)
     // problem of a strided batch: grid layer blockIdx.z
     p.A += blockIdx.z * p.sa;
     p.B += blockIdx.z * p.sb;
     p.C += blockIdx.z * p.sc;
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int g = lane >> 4, c16 = lane & 15;
-    const int m0 = blockIdx.x * kSkinnyRows;
-    const int n0 = blockIdx.y * kSkinnyCols;
+    const int m0 = (int)(bid % tiles_m) * kSkinnyRows;
+    const int n0 = (int)(bid / tiles_m) * kSkinnyCols;
     const int row = m0 + c16;
     const bool row_ok = row < p.M;
     const float *arow = p.A + (int64_t)(row_ok ? row : m0) * p.lda;
@@ -125,15 +130,14 @@ __global__ __launch_bounds__(W * 64) void gemm_skinny_kernel(GemmArgs p)
 template <int NB, int W, int U>
 hipError_t launch_nb(const GemmArgs &a, bool vec, hipStream_t stream)
 {
-    const int64_t gx = (a.M + kSkinnyRows - 1) / kSkinnyRows;
-    const int64_t gy = (a.N + kSkinnyCols - 1) / kSkinnyCols;
-    if (gx > 0x7fffffff || gy > 65535) return hipErrorInvalidConfiguration;
+    const int64_t tiles = ((a.M + kSkinnyRows - 1) / kSkinnyRows) * ((a.N + kSkinnyCols - 1) / kSkinnyCols);
+    unsigned gx, gy;
+    if (!grid_for(tiles, gx, gy)) return hipErrorInvalidConfiguration;
     const void *fn = vec ? reinterpret_cast<const void *>(&gemm_skinny_kernel<NB, W, U, true>)
                          : reinterpret_cast<const void *>(&gemm_skinny_kernel<NB, W, U, false>);
     GemmArgs arg = a;
     void *args[] = {&arg};
-    return hipLaunchKernel(fn, dim3((unsigned)gx, (unsigned)gy, (unsigned)a.batch), dim3(W * 64), args,
-                           0, stream);
+    return hipLaunchKernel(fn, dim3(gx, gy, (unsigned)a.batch), dim3(W * 64), args, 0, stream);
 }
 
 }  // namespace

@@ -43,8 +43,10 @@ __device__ __forceinline__ float wave_sum(float v)
 template <bool VEC>
 __global__ __launch_bounds__(64) void gemv_f32_kernel(GemvArgs p)
 {
+    const int64_t bid = linear_block();
+    if (bid >= p.M) return;  // padding of a 2-D grid
     const int lane = threadIdx.x;
-    const int row = blockIdx.x;
+    const int row = (int)bid;
     const int rot = row & (kPieces - 1);
     float acc = 0.f;
     if constexpr (VEC) {
@@ -141,7 +143,9 @@ hipError_t gemv_launch(const GemvArgs &a, hipStream_t stream)
     void *args[] = {&arg};
     const void *fn = vec ? reinterpret_cast<const void *>(&gemv_f32_kernel<true>)
                          : reinterpret_cast<const void *>(&gemv_f32_kernel<false>);
-    return hipLaunchKernel(fn, dim3((unsigned)a.M), dim3(64), args, 0, stream);
+    unsigned gx, gy;
+    if (!grid_for(a.M, gx, gy)) return hipErrorInvalidConfiguration;
+    return hipLaunchKernel(fn, dim3(gx, gy), dim3(64), args, 0, stream);
 }
 
 hipError_t zero_fill_launch(float *ptr, int64_t rows, int64_t cols, int64_t ld, hipStream_t stream)

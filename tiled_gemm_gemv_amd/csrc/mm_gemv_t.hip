@@ -39,8 +39,11 @@ template <bool VEC>
 __global__ __launch_bounds__(kWaves * 64) void gemv_t_kernel(GemvArgs p)
 {
     __shared__ f32x4 partial[(kWaves - 1) * 64];
+    const int64_t strips = ((int64_t)p.N + kStrip - 1) / kStrip;
+    const int64_t bid = linear_block();
+    if (bid >= strips) return;  // padding of a 2-D grid (whole workgroup, before any barrier)
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    const int strip = strip_of_block(blockIdx.x, gridDim.x);
+    const int strip = strip_of_block((int)bid, (int)strips);
     const int j0 = strip * kStrip + 4 * (lane & 3);   // this lane's first column
     const int rsub = lane >> 2;                         // row within a 16-row group
     const int ncols = p.N - j0;                         // columns left from j0 (may be <= 0)
@@ -100,12 +103,13 @@ hipError_t gemv_t_launch(const GemvArgs &a, hipStream_t stream)
 {
     const bool vec = (a.N % 4 == 0) && ((uintptr_t)a.A % 16 == 0);
     const int64_t strips = ((int64_t)a.N + kStrip - 1) / kStrip;
-    if (strips > 0x7fffffff) return hipErrorInvalidConfiguration;
+    unsigned gx, gy;
+    if (!grid_for(strips, gx, gy)) return hipErrorInvalidConfiguration;
     GemvArgs arg = a;
     void *args[] = {&arg};
     const void *fn = vec ? reinterpret_cast<const void *>(&gemv_t_kernel<true>)
                          : reinterpret_cast<const void *>(&gemv_t_kernel<false>);
-    return hipLaunchKernel(fn, dim3((unsigned)strips), dim3(kWaves * 64), args, 0, stream);
+    return hipLaunchKernel(fn, dim3(gx, gy), dim3(kWaves * 64), args, 0, stream);
 }
 
 }  // namespace mm

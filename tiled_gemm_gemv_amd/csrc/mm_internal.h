@@ -6,6 +6,35 @@
 
 namespace mm {
 
+// Launch grids. HIP's dispatch packet holds each grid dimension in work-items, in
+// 32 bits, so a 1-D grid stops at 2^32 / (threads per workgroup) workgroups. A
+// launch of more workgroups uses a 2-D grid: kMaxGridX workgroups along x (a
+// multiple of 8, so x % 8 is still the XCD a workgroup lands on) times as many rows
+// as needed along y. Kernels number workgroups linear_block() = y * gridDim.x + x;
+// those at `count` or beyond return at once. Up to kMaxGridX workgroups the grid is
+// the plain 1-D one.
+constexpr int64_t kMaxGridX = (int64_t(1) << 22) - 8;  // * 1024 threads < 2^32
+
+// Grid of `count` >= 1 workgroups; false if it needs more than 65535 rows.
+inline bool grid_for(int64_t count, unsigned &gx, unsigned &gy)
+{
+    if (count <= kMaxGridX) {
+        gx = (unsigned)count;
+        gy = 1;
+        return true;
+    }
+    const int64_t rows = (count + kMaxGridX - 1) / kMaxGridX;
+    if (rows > 65535) return false;
+    gx = (unsigned)kMaxGridX;
+    gy = (unsigned)rows;
+    return true;
+}
+
+__device__ __forceinline__ int64_t linear_block()
+{
+    return (int64_t)blockIdx.y * gridDim.x + blockIdx.x;
+}
+
 // Arguments of one GEMM launch, already validated on the host. Sizes fit in
 // int32; offsets are formed in int64.
 struct GemmArgs {
@@ -48,6 +77,25 @@ const char *gemm16_config_name(int cfg);
 int gemm16_select_config(int64_t M, int64_t N, int64_t K);
 hipError_t gemm16_launch(int cfg, bool bf16, const void *A, int64_t lda, const void *B, int64_t ldb,
                          float *C, int64_t ldc, int M, int N, int K, hipStream_t stream);
+
+// A 2-D convolution (mm_conv.hip): x is N x C x H x W, w is K x C x R x S, y is
+// N x K x P x Q, all packed; strides sh, sw, padding ph, pw, dilation dh, dw.
+struct ConvArgs {
+    int64_t N, C, H, W, K, R, S, sh, sw, ph, pw, dh, dw, P, Q;
+    const float *x;
+    const float *w;
+    float *y;
+};
+
+// Convolution configurations: tile shapes of the GEMM (names as there).
+int conv_num_configs();
+const char *conv_config_name(int cfg);
+// Choice for a product of M filters by N = images * P * Q output positions.
+int conv_select_config(int64_t M, int64_t N);
+// Enqueue the convolution (cfg < 0: choose). The caller has checked the shape:
+// N, K, P, Q >= 1, C >= 0, one image of x below 2^31 elements, C R S and P Q below
+// 2^31, H + 2 ph, W + 2 pw, dh (R - 1), dw (S - 1) below 2^29.
+hipError_t conv_launch(int cfg, const ConvArgs &a, hipStream_t stream);
 
 // Enqueue the GEMV (M >= 1, N >= 1).
 hipError_t gemv_launch(const GemvArgs &a, hipStream_t stream);

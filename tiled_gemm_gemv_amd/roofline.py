@@ -103,6 +103,27 @@ def output_tile_reads_tiled(B, N):
     return (N // B) * 2 * B * B
 
 
+def conv_out_hw(H, W, R, S, stride=(1, 1), pad=(0, 0), dil=(1, 1)):
+    P = (H + 2 * pad[0] - dil[0] * (R - 1) - 1) // stride[0] + 1
+    Q = (W + 2 * pad[1] - dil[1] * (S - 1) - 1) // stride[1] + 1
+    return P, Q
+
+
+def conv_flops(N, C, K, R, S, P, Q):
+    """2 FLOP per multiply-add of the implicit GEMM: K x (N P Q) outputs, C R S terms each."""
+    return 2 * N * K * P * Q * C * R * S
+
+
+def conv_algorithmic_bytes(N, C, H, W, K, R, S, P, Q):
+    """x and the filters read once, y written once (the im2col matrix is never stored)."""
+    return FP32 * (N * C * H * W + K * C * R * S + N * K * P * Q)
+
+
+def im2col_matrix_bytes(N, C, R, S, P, Q):
+    """What an explicit im2col matrix (C R S x N P Q) would take, written and read back."""
+    return FP32 * C * R * S * N * P * Q
+
+
 # ----------------------------------------------------------------- roofline use
 
 def gemm_bound_time(M, N, K):

@@ -16,6 +16,20 @@ Matter / Computational Intensity"):
   gemm_ragged  C = A B, M = 1000, K = 777, N = 1531, A, B ~ N(0, 1)
   gemm_proj    C = A B, M = 8192, K = 4096, N = 14336, A ~ N(0, 1), B ~ N(0, 1/K)
 
+Convolution workloads (x N x C x H x W, filters K x C x R x S; the pages name im2col
+as the way a convolution maps onto the GEMM but give no layer sizes, so these are
+the usual shapes of an image network's layers):
+
+  conv_small   N=2  C=5   13x11  K=7   3x3 stride 1 pad 1        (oracle-sized, ragged)
+  conv3x3      N=32 C=128 28x28  K=128 3x3 stride 1 pad 1        (a middle layer)
+  conv3x3_s2   N=32 C=128 56x56  K=256 3x3 stride 2 pad 1        (a downsampling layer)
+  conv7x7_s2   N=32 C=3   224x224 K=64 7x7 stride 2 pad 3        (the input layer)
+  conv1x1      N=32 C=256 56x56  K=64  1x1                       (a pointwise layer)
+  conv3x3_d2   N=8  C=64  64x64  K=64  3x3 stride 1 pad 2 dil 2  (a dilated layer)
+
+x ~ U[-1, 1) (operand id 0); w ~ N(0, 1/(C R S)) (operand id 1), the usual scale of
+an initialised filter bank; same generator as below.
+
 Every operand comes from numpy's PCG64 seeded with [workload seed, operand id];
 operand ids: A = 0, B = 1, x = 2, row sample = 3. Readings where the workload
 text is silent: U[-1, 1) is half-open and drawn as 2u - 1 with u a float32 in
@@ -68,6 +82,74 @@ WORKLOADS = {
                           b_std=1.0 / 64.0, spot_rows=64,
                           note="transformer projection: 8192 tokens, 4096 -> 14336"),
 }
+
+
+@dataclass(frozen=True)
+class ConvWorkload:
+    name: str
+    N: int
+    C: int
+    H: int
+    W: int
+    K: int
+    R: int
+    S: int
+    stride: tuple = (1, 1)
+    pad: tuple = (0, 0)
+    dilation: tuple = (1, 1)
+    seed: int = 0
+    dist_x: str = "u11"
+    dist_w: str = "normal"    # N(0, 1/(C R S)) for "normal"
+    sample_images: int = 0    # >0: verify this many sampled images instead of all
+    note: str = field(default="", compare=False)
+
+    def out_hw(self):
+        P = (self.H + 2 * self.pad[0] - self.dilation[0] * (self.R - 1) - 1) // self.stride[0] + 1
+        Q = (self.W + 2 * self.pad[1] - self.dilation[1] * (self.S - 1) - 1) // self.stride[1] + 1
+        return P, Q
+
+    def with_dist(self, dist: str) -> "ConvWorkload":
+        return ConvWorkload(self.name + "_" + dist, self.N, self.C, self.H, self.W, self.K, self.R,
+                            self.S, self.stride, self.pad, self.dilation, self.seed, dist, dist,
+                            self.sample_images, self.note)
+
+    def describe(self) -> str:
+        return (f"conv2d fp32 N={self.N} C={self.C} H={self.H} W={self.W} K={self.K} "
+                f"{self.R}x{self.S} stride={self.stride} pad={self.pad} dil={self.dilation}")
+
+
+CONV_WORKLOADS = {
+    "conv_small": ConvWorkload("conv_small", 2, 5, 13, 11, 7, 3, 3, (1, 1), (1, 1), (1, 1), 1101,
+                               note="oracle-sized, ragged everywhere"),
+    "conv3x3": ConvWorkload("conv3x3", 32, 128, 28, 28, 128, 3, 3, (1, 1), (1, 1), (1, 1), 1102,
+                            sample_images=2, note="3x3 middle layer of an image network"),
+    "conv3x3_s2": ConvWorkload("conv3x3_s2", 32, 128, 56, 56, 256, 3, 3, (2, 2), (1, 1), (1, 1),
+                               1103, sample_images=2, note="3x3 stride-2 downsampling layer"),
+    "conv7x7_s2": ConvWorkload("conv7x7_s2", 32, 3, 224, 224, 64, 7, 7, (2, 2), (3, 3), (1, 1),
+                               1104, sample_images=2, note="7x7 stride-2 input layer"),
+    "conv1x1": ConvWorkload("conv1x1", 32, 256, 56, 56, 64, 1, 1, (1, 1), (0, 0), (1, 1), 1105,
+                            sample_images=2, note="pointwise layer"),
+    "conv3x3_d2": ConvWorkload("conv3x3_d2", 8, 64, 64, 64, 64, 3, 3, (1, 1), (2, 2), (2, 2), 1106,
+                               sample_images=2, note="3x3 dilated layer"),
+}
+
+
+def conv_inputs(w: ConvWorkload):
+    """(x, filters): N x C x H x W and K x C x R x S, C-contiguous float32."""
+    x = draw(rng_for(w.seed, OPERAND_A), (w.N, w.C, w.H, w.W), w.dist_x)
+    std = 1.0 / np.sqrt(max(1, w.C * w.R * w.S)) if w.dist_w == "normal" else 1.0
+    f = draw(rng_for(w.seed, OPERAND_B), (w.K, w.C, w.R, w.S), w.dist_w, std)
+    return x, f
+
+
+def sample_images(w: ConvWorkload, n: int = 0) -> np.ndarray:
+    """n distinct image indices in [0, N), always with the first and the last."""
+    n = n or w.sample_images or w.N
+    if n >= w.N:
+        return np.arange(w.N, dtype=np.int64)
+    mid = rng_for(w.seed, OPERAND_ROWS).choice(np.arange(1, w.N - 1), size=max(0, n - 2),
+                                               replace=False)
+    return np.sort(np.concatenate([[0, w.N - 1], mid]).astype(np.int64))
 
 
 def rng_for(seed: int, operand: int) -> np.random.Generator:
