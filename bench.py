@@ -125,9 +125,9 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
-              "(the GEMM and GEMV here need no exchange between GPUs; see DESIGN.md for how "
-              "the work would be split).", file=sys.stderr)
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported. "
+              "Across GPUs the GEMM would split B and C by columns (A replicated) and the GEMV "
+              "A by rows (x broadcast), with no exchange of results.", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -392,7 +392,7 @@ def conv_tensors(torch, cw, dev):
 
 
 def launch_conv(mm, cw, x, f, y, stream, cfg=None):
-    geo = (cw.N, cw.C, cw.H, cw.W, cw.K, cw.R, cw.S, *cw.stride, *cw.pad, *cw.dilation)
+    geo = cw.geometry()
     if cfg is None:
         mm.mm_conv2d_f32(*geo, x, f, y, stream)
     else:
@@ -406,8 +406,8 @@ def sweep_conv(torch, mm, dev):
           "launches between two events)")
     for c in range(nc):
         print(f"#   cfg {c}: {mm.mm_conv2d_f32_config_name(c)}")
-    print("#   default = mm_conv2d_f32's own choice (* marks that tile among the configs; "
-          "1x1 layers on large maps go to the batched GEMM and its own choice)")
+    print("#   default = mm_conv2d_f32's own choice (* marks it among the configs; 1x1 layers on "
+          "large maps run the batched GEMM with that tile)")
     print("#   dense = mm_gemm_f32 on the same M x N x K with the im2col matrix already in "
           "memory (what the gather costs, not counting writing that matrix)")
     print("#   bound = min(fp32 MFMA peak, algorithmic FLOP/byte x 8 TB/s); % = default / bound")
@@ -421,7 +421,7 @@ def sweep_conv(torch, mm, dev):
         by = rl.conv_algorithmic_bytes(cw.N, cw.C, cw.H, cw.W, cw.K, cw.R, cw.S, P, Q)
         bound = min(peak, flop / by * rl.MI355X_HBM_PEAK)
         reps = max(3, min(200, int(2e11 / flop)))
-        sel = mm.mm_conv2d_f32_select(cw.K, cw.N * P * Q)
+        sel = mm.mm_conv2d_f32_select(*cw.geometry())
         cells = []
         for c in range(nc):
             def launch(i, st, c=c):

@@ -202,8 +202,9 @@ int mm_gemm_f16_config(int cfg, int64_t M, int64_t N, int64_t K,
  * Errors: MM_ERR_INVALID_ARG for a negative size, a stride, dilation or filter size
  * below 1, negative padding, a filter that does not fit the padded input (P or Q
  * would be below 1), a NULL or unaligned pointer that is used, or sizes beyond the
- * limits: one image (C H W), C R S and P Q at most 2^31 - 1; H + 2 ph, W + 2 pw,
- * dh (R - 1), dw (S - 1) below 2^29. Other errors as for mm_gemm_f32.
+ * limits: one image (C H W) and the padded plane (H + 2 ph)(W + 2 pw) at most
+ * 2^30 - 1 elements; C R S and P Q at most 2^31 - 1; H + 2 ph, W + 2 pw, dh (R - 1),
+ * dw (S - 1) below 2^29. Other errors as for mm_gemm_f32.
  */
 int mm_conv2d_f32(int64_t N, int64_t C, int64_t H, int64_t W,
                   int64_t K, int64_t R, int64_t S,
@@ -223,14 +224,16 @@ int64_t mm_conv2d_out_dim(int64_t in, int64_t filter, int64_t stride, int64_t pa
  * Tile configurations of the convolution (tile shapes of the GEMM, with an im2col
  * gather in place of the B loads), as for the GEMM:
  *   mm_conv2d_f32_num_configs, mm_conv2d_f32_config_name(cfg): count and names;
- *   mm_conv2d_f32_select: the config mm_conv2d_f32 would use for the product of K
- *     filters by N * P * Q output positions;
+ *   mm_conv2d_f32_select: the config mm_conv2d_f32 uses for the geometry (same
+ *     arguments without the pointers and stream), or -1 if it is invalid;
  *   mm_conv2d_f32_config: mm_conv2d_f32 forced to config `cfg` (MM_ERR_INVALID_ARG
  *     if out of range). Every config is correct for every shape.
  */
 int mm_conv2d_f32_num_configs(void);
 const char *mm_conv2d_f32_config_name(int cfg);
-int mm_conv2d_f32_select(int64_t K, int64_t NPQ);
+int mm_conv2d_f32_select(int64_t N, int64_t C, int64_t H, int64_t W,
+                         int64_t K, int64_t R, int64_t S,
+                         int64_t sh, int64_t sw, int64_t ph, int64_t pw, int64_t dh, int64_t dw);
 int mm_conv2d_f32_config(int cfg, int64_t N, int64_t C, int64_t H, int64_t W,
                          int64_t K, int64_t R, int64_t S,
                          int64_t sh, int64_t sw, int64_t ph, int64_t pw, int64_t dh, int64_t dw,

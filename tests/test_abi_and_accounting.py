@@ -182,8 +182,12 @@ def test_conv_config_table(lib):
     gemm_names = [mm.mm_gemm_f32_config_name(i) for i in range(mm.mm_gemm_f32_num_configs())]
     assert all(name in gemm_names for name in names)   # tile shapes of the GEMM
     assert mm.mm_conv2d_f32_config_name(n) is None
-    for K, NPQ in [(1, 1), (64, 401408), (128, 25088), (256, 25088), (7, 286), (4096, 1 << 30)]:
-        assert 0 <= mm.mm_conv2d_f32_select(K, NPQ) < n
+    for geo in [(1, 1, 1, 1, 1, 1, 1, 1, 1, 0, 0, 1, 1), (32, 3, 224, 224, 64, 7, 7, 2, 2, 3, 3, 1, 1),
+                (32, 128, 28, 28, 128, 3, 3, 1, 1, 1, 1, 1, 1), (32, 256, 56, 56, 64, 1, 1, 1, 1, 0, 0, 1, 1),
+                (2, 5, 13, 11, 7, 3, 3, 1, 1, 1, 1, 1, 1), (1, 1, 30000, 30000, 4096, 1, 1, 1, 1, 0, 0, 1, 1)]:
+        assert 0 <= mm.mm_conv2d_f32_select(*geo) < n
+    assert mm.mm_conv2d_f32_select(1, 1, 4, 4, 1, 5, 5, 1, 1, 0, 0, 1, 1) == -1   # does not fit
+    assert mm.mm_conv2d_f32_select(-1, 1, 4, 4, 1, 1, 1, 1, 1, 0, 0, 1, 1) == -1
 
 
 # N, C, H, W, K, R, S, sh, sw, ph, pw, dh, dw
@@ -204,9 +208,9 @@ def _conv(lib, geo, x=FAKE, w=FAKE, y=FAKE, cfg=None):
     ({11: 0}, "dilation"), ({12: 0}, "dilation"),
     ({5: 9, 9: 0}, "does not fit"), ({6: 5, 10: 0, 12: 3}, "does not fit"),
     ({2: 1 << 29}, "2^29"), ({9: 1 << 28}, "2^29"), ({5: 3, 11: 1 << 28, 2: 1 << 28}, "2^29"),
-    ({1: 1 << 16, 2: 256, 3: 128}, "C * H * W"),
-    ({1: 1 << 25, 2: 7, 3: 7, 5: 9, 6: 9}, "C * R * S"),
-    ({2: 50000, 3: 50000, 9: 0, 10: 0, 5: 1, 6: 1}, "P * Q"),
+    ({1: 1 << 16, 2: 256, 3: 64}, "C * H * W"),
+    ({1: 1 << 25, 2: 1, 3: 1, 5: 9, 6: 9, 9: 4, 10: 4}, "C * R * S"),
+    ({1: 1, 2: 30000, 3: 30000, 9: 2000, 10: 2000, 5: 1, 6: 1}, "padded plane"),
 ])
 def test_conv_rejects_invalid_arguments(lib, change, why):
     geo = list(GOOD)

@@ -128,11 +128,20 @@ def test_default_choice_small_workload(dev):
 def test_full_size_workloads_sampled_images(dev, name):
     """The layer shapes at full size, in the configuration mm_conv2d_f32 chooses; the
     oracle recomputes the sampled images (each image's outputs depend on it alone)."""
-    cw = wl.CONV_WORKLOADS[name]
+    _full_size_check(dev, wl.CONV_WORKLOADS[name], None)
+
+
+@pytest.mark.parametrize("cfg", CONFIGS)
+@pytest.mark.parametrize("name", ["conv3x3", "conv7x7_s2"])
+def test_full_size_every_config(dev, name, cfg):
+    _full_size_check(dev, wl.CONV_WORKLOADS[name], cfg)
+
+
+def _full_size_check(dev, cw, cfg):
     x, w = wl.conv_inputs(cw)
-    P, Q = cw.out_hw()
-    print(f"\n{cw.describe()}: config {mm.mm_conv2d_f32_select(cw.K, cw.N * P * Q)}", flush=True)
-    y = mm.conv2d(to_device(x, dev), to_device(w, dev), cw.stride, cw.pad, cw.dilation)
+    used = mm.mm_conv2d_f32_select(*cw.geometry()) if cfg is None else cfg
+    print(f"\n{cw.describe()}: config {used}", flush=True)
+    y = mm.conv2d(to_device(x, dev), to_device(w, dev), cw.stride, cw.pad, cw.dilation, config=cfg)
     torch.cuda.synchronize()
     imgs = wl.sample_images(cw)
     got = y[torch.from_numpy(imgs).to(dev)].cpu().numpy()

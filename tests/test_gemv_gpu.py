@@ -58,7 +58,7 @@ def test_fc_layer_integer_exact(dev):
 
 
 SHAPES = [(1, 1), (3, 5), (7, 4093), (100, 4097), (64, 1), (5, 1024), (33, 8191), (4097, 4100),
-          (2, 65536 + 12), (9, 20000), (1000, 64), (513, 257)]
+          (2, 65536 + 12), (9, 20000), (1000, 64), (513, 257), (6, 12288), (4095, 4096)]
 
 
 @pytest.mark.parametrize("M,N", SHAPES)

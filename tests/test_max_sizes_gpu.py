@@ -5,7 +5,7 @@ start more than 2^31 elements (8 GiB) into NaN-filled buffers.
 GEMV: a packed 65539 x 32772 matrix (2.15e9 elements, 8.6 GB) whose rows repeat a
 block of 64 seeded rows (built on the device by copying, no arithmetic), so every
 one of the 65539 outputs can be checked exactly against the oracle's 64 rows.
-Convolution: a batch of three 27000 x 27000 images, split by the library into runs
+Convolution: a batch of four 27000 x 27000 images, split by the library into runs
 whose 32-bit offsets fit.
 Grids: launches of more workgroups than a 1-D grid can hold, for every kernel.
 """
@@ -89,13 +89,13 @@ def test_gemv_offsets_beyond_2_31(dev):
 
 
 def test_conv_batch_split_beyond_2_31(dev):
-    """Convolution over 3 images of 27000 x 27000 (x: 2.19e9 elements, y: 4.37e9): the
-    library splits the batch into runs whose offsets fit in 32 bits (2 images, then 1),
-    so the second run starts beyond element 2^31 of x and y. Image n repeats a block of
+    """Convolution over 4 images of 27000 x 27000 (x: 2.92e9 elements, y: 5.83e9): the
+    library splits the batch into runs of one image (a run of x stays below 2^30
+    elements), so the last run starts beyond element 2^31 of x and y. Image n repeats a block of
     64 seeded integer rows starting at row 7 n (built on the device by indexing, no
     arithmetic on values), so images differ; sampled outputs are checked exactly against
     the oracle applied to their receptive field, zero-padded on the host."""
-    N, C, H, W, K, R = 3, 1, 27000, 27000, 2, 3
+    N, C, H, W, K, R = 4, 1, 27000, 27000, 2, 3
     assert N * C * H * W > BIG and N * K * H * W > BIG
     rows = 64
     block = wl.random_matrix(91, rows, W, "int4")
@@ -207,10 +207,11 @@ def test_narrow_gemm_grid_beyond_2_32_work_items(dev, cfg):
     torch.cuda.empty_cache()
 
 
-def test_gemv_grid_beyond_2_32_work_items(dev):
-    N, blk = 8, 1024
-    M = 4_500_480                                  # one 64-lane workgroup per row
-    assert M >= TWO_D
+@pytest.mark.parametrize("N,M", [(8, 17_000_448),     # 16-byte rows: 4 rows per workgroup
+                                 (3, 4_500_480)])     # 4-byte rows: one row per workgroup
+def test_gemv_grid_beyond_2_32_work_items(dev, N, M):
+    blk = 1024
+    assert -(-M // (4 if N % 4 == 0 else 1)) >= TWO_D
     Ab = wl.random_matrix(107, blk, N, "int4")
     x = wl.random_matrix(108, 1, N, "int4")[0]
     A = to_device(Ab, dev).repeat(M // blk, 1)

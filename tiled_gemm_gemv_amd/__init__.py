@@ -97,7 +97,7 @@ def load():
     lib.mm_conv2d_f32_num_configs.restype = ci
     lib.mm_conv2d_f32_config_name.argtypes = [ci]
     lib.mm_conv2d_f32_config_name.restype = ctypes.c_char_p
-    lib.mm_conv2d_f32_select.argtypes = [i64, i64]
+    lib.mm_conv2d_f32_select.argtypes = [i64] * 13
     lib.mm_conv2d_f32_select.restype = ci
     lib.mm_status_string.argtypes = [ci]
     lib.mm_status_string.restype = ctypes.c_char_p
@@ -253,8 +253,8 @@ def mm_conv2d_f32_config_name(cfg):
     return name.decode() if name is not None else None
 
 
-def mm_conv2d_f32_select(K, NPQ):
-    return load().mm_conv2d_f32_select(K, NPQ)
+def mm_conv2d_f32_select(N, C, H, W, K, R, S, sh, sw, ph, pw, dh, dw):
+    return load().mm_conv2d_f32_select(N, C, H, W, K, R, S, sh, sw, ph, pw, dh, dw)
 
 
 def mm_status_string(status):

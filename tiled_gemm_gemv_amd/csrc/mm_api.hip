@@ -165,10 +165,14 @@ int64_t conv_out_dim(int64_t in, int64_t filter, int64_t stride, int64_t pad, in
     return (padded - span - 1) / stride + 1;
 }
 
-int run_conv(int cfg, int64_t N, int64_t C, int64_t H, int64_t W, int64_t K, int64_t R,
-             int64_t S, int64_t sh, int64_t sw, int64_t ph, int64_t pw, int64_t dh, int64_t dw,
-             const float *x, const float *w, float *y, void *stream)
+// Checks a convolution's arguments and fills `a`. Returns MM_OK, or the error; *work
+// is false when there is no output element (nothing to enqueue).
+int check_conv(int64_t N, int64_t C, int64_t H, int64_t W, int64_t K, int64_t R, int64_t S,
+               int64_t sh, int64_t sw, int64_t ph, int64_t pw, int64_t dh, int64_t dw,
+               const float *x, const float *w, const float *y, bool check_pointers,
+               mm::ConvArgs &a, bool &work)
 {
+    work = false;
     if (N < 0 || C < 0 || H < 0 || W < 0 || K < 0) return invalid("negative size");
     if (R < 1 || S < 1) return invalid("filter size below 1");
     if (sh < 1 || sw < 1) return invalid("stride below 1");
@@ -185,21 +189,23 @@ int run_conv(int cfg, int64_t N, int64_t C, int64_t H, int64_t W, int64_t K, int
     }
     if (K > kMaxDim || N > kMaxDim || C > kMaxDim) return invalid("size above 2^31 - 1");
     const int64_t HW = H * W, PQ = P * Q;  // each below 2^58
-    if (PQ > kMaxDim) return invalid("P * Q above 2^31 - 1");
-    if (C > 0 && HW > kMaxDim / C) return invalid("C * H * W above 2^31 - 1");
+    const int64_t kMaxImage = (int64_t(1) << 30) - 1;
+    if (C > 0 && HW > kMaxImage / C) return invalid("C * H * W above 2^30 - 1");
+    // P * Q <= (H + 2 ph)(W + 2 pw), so this also keeps P * Q below 2^30
+    if ((H + 2 * ph) * (W + 2 * pw) > kMaxImage) return invalid("padded plane above 2^30 - 1");
     if (C > 0 && R * S > kMaxDim / C) return invalid("C * R * S above 2^31 - 1");
     const int64_t limit = INT64_MAX / 4;
     const int64_t CHW = C * HW, CRS = C * R * S;
     if (N > 0 && CHW > limit / N) return invalid("x extent overflows");
     if (K > 0 && PQ > 0 && N > limit / K / PQ) return invalid("y extent overflows");
-    const bool has_x = N > 0 && CHW > 0, has_w = K > 0 && CRS > 0, has_y = N > 0 && K > 0;
-    if (has_x && !x) return invalid("x is NULL");
-    if (has_w && !w) return invalid("w is NULL");
-    if (has_y && !y) return invalid("y is NULL");
-    if ((uintptr_t)x % 4 || (uintptr_t)w % 4 || (uintptr_t)y % 4)
-        return invalid("pointer not aligned to its element size");
-    if (!has_y) return MM_OK;  // P, Q >= 1 here, so no output means N or K is 0
-    mm::ConvArgs a;
+    if (check_pointers) {
+        const bool has_x = N > 0 && CHW > 0, has_w = K > 0 && CRS > 0, has_y = N > 0 && K > 0;
+        if (has_x && !x) return invalid("x is NULL");
+        if (has_w && !w) return invalid("w is NULL");
+        if (has_y && !y) return invalid("y is NULL");
+        if ((uintptr_t)x % 4 || (uintptr_t)w % 4 || (uintptr_t)y % 4)
+            return invalid("pointer not aligned to its element size");
+    }
     a.N = N;
     a.C = C;
     a.H = H;
@@ -217,7 +223,19 @@ int run_conv(int cfg, int64_t N, int64_t C, int64_t H, int64_t W, int64_t K, int
     a.Q = Q;
     a.x = x;
     a.w = w;
-    a.y = y;
+    a.y = const_cast<float *>(y);
+    work = N > 0 && K > 0;  // P, Q >= 1 here
+    return MM_OK;
+}
+
+int run_conv(int cfg, int64_t N, int64_t C, int64_t H, int64_t W, int64_t K, int64_t R,
+             int64_t S, int64_t sh, int64_t sw, int64_t ph, int64_t pw, int64_t dh, int64_t dw,
+             const float *x, const float *w, float *y, void *stream)
+{
+    mm::ConvArgs a;
+    bool work;
+    const int st = check_conv(N, C, H, W, K, R, S, sh, sw, ph, pw, dh, dw, x, w, y, true, a, work);
+    if (st != MM_OK || !work) return st;
     return from_hip("conv2d launch", mm::conv_launch(cfg, a, static_cast<hipStream_t>(stream)));
 }
 
@@ -361,10 +379,16 @@ int mm_conv2d_f32_num_configs(void) { return mm::conv_num_configs(); }
 
 const char *mm_conv2d_f32_config_name(int cfg) { return mm::conv_config_name(cfg); }
 
-int mm_conv2d_f32_select(int64_t K, int64_t NPQ)
+int mm_conv2d_f32_select(int64_t N, int64_t C, int64_t H, int64_t W, int64_t K, int64_t R,
+                         int64_t S, int64_t sh, int64_t sw, int64_t ph, int64_t pw, int64_t dh,
+                         int64_t dw)
 {
-    if (K < 0 || NPQ < 0) return 0;
-    return mm::conv_select_config(K, NPQ);
+    mm::ConvArgs a;
+    bool work;
+    if (check_conv(N, C, H, W, K, R, S, sh, sw, ph, pw, dh, dw, nullptr, nullptr, nullptr, false, a,
+                   work) != MM_OK)
+        return -1;
+    return mm::conv_choose_config(a);
 }
 
 const char *mm_status_string(int status)

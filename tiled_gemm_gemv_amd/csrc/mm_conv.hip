@@ -30,76 +30,98 @@
 namespace mm {
 namespace {
 
-constexpr int kFar = -(1 << 30);  // added to a row or column index, puts it outside any image
+constexpr int kFar = -(1 << 30);  // an input row that is outside any image
 
 // B = the im2col matrix of a run of images of x (p.B points at the first), C = those
-// images of y. p.N = images * P * Q, p.K = C * R * S, p.ldc = P * Q. The host keeps
-// images * C * H * W below 2^31 and H + 2 ph, W + 2 pw, dh (R - 1), dw (S - 1) below
-// 2^29, so every offset below fits in int32 and kFar keeps an index negative.
+// images of y; p.N = images * P * Q, p.K = C * R * S, p.ldc = P * Q.
+//
+// Piece idx of a K-step is one column of the panel, col = idx % BN, at 16
+// consecutive k rows from k0 + 16 (idx / BN). BN is a multiple of 64, so the 64
+// lanes of a wave take 64 adjacent output positions at the same 16 rows: (c, r, s)
+// and everything derived from them are the same in every lane (scalar registers),
+// and at unit stride neighbouring lanes read neighbouring floats of x. Loads need no
+// branch: an element outside the image reads x[0] and is replaced by zero.
+//
+// The host keeps a run of images below 2^30 elements (byte offsets fit in 32 bits)
+// and the padded plane (H + 2 ph)(W + 2 pw) below 2^30, so every offset below fits
+// in int32.
 struct Im2colOperands {
     static constexpr bool kMatrixB = false;
     int H, W, R, S, sh, sw, ph, pw, dh, dw;
     int Q, PQ, HW, RS, CHW;
     int64_t KPQ;
 
-    // Per output column (n, p, q): the input row and column under the filter's first
-    // tap, and the offset of image n. Columns past the end get a row of kFar.
+    // Output column (n, p, q): input row h0 and column w0 under the filter's first
+    // tap, and base = offset of x[n][0][h0][w0] (negative when in the padding).
+    // Columns past the end get h0 = kFar.
     struct Cols {
-        int h0[4], w0[4], img[4];
+        int h0, w0, base;
     };
 
-    __device__ __forceinline__ Cols columns(const GemmArgs &p, int gn) const
+    template <class T>
+    __device__ __forceinline__ Cols columns(const GemmArgs &p, int n0, int idx) const
     {
+        static_assert(T::BN % 64 == 0 && T::BK % 16 == 0, "a wave's lanes must share their rows");
+        const int j = n0 + idx % T::BN;
         Cols c;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int j = gn + e;
-            if (j < p.N) {
-                const int n = (unsigned)j / (unsigned)PQ, pq = j - n * PQ;
-                const int op = (unsigned)pq / (unsigned)Q, oq = pq - op * Q;
-                c.h0[e] = op * sh - ph;
-                c.w0[e] = oq * sw - pw;
-                c.img[e] = n * CHW;
-            } else {
-                c.h0[e] = kFar;
-                c.w0[e] = 0;
-                c.img[e] = 0;
-            }
+        if (j < p.N) {
+            const int n = (unsigned)j / (unsigned)PQ, pq = j - n * PQ;
+            const int op = (unsigned)pq / (unsigned)Q, oq = pq - op * Q;
+            c.h0 = op * sh - ph;
+            c.w0 = oq * sw - pw;
+            c.base = n * CHW + c.h0 * W + c.w0;
+        } else {
+            c.h0 = kFar;
+            c.w0 = 0;
+            c.base = 0;
         }
         return c;
     }
 
-    // Rows gk .. gk + 3 of the im2col matrix at the thread's 4 columns. Row
-    // (c, r, s) is found once by division; the next rows step s, then r, then c.
-    template <bool VEC>
-    __device__ __forceinline__ void load_b(const GemmArgs &p, const Cols &cl, int gk, int, bool,
-                                           f32x4 (&b)[4]) const
+    template <class T, bool VEC>
+    __device__ __forceinline__ void load_b(const GemmArgs &p, const Cols &cl, int k0, int, int idx,
+                                           bool, f32x4 (&b)[4]) const
     {
-        unsigned c = (unsigned)gk / (unsigned)RS;
-        const unsigned rem = (unsigned)gk - c * (unsigned)RS;
-        unsigned r = rem / (unsigned)S;
-        unsigned s = rem - r * (unsigned)S;
+        // first row of the piece: (c, r, s) by division once, then stepped
+        const int gk0 = __builtin_amdgcn_readfirstlane(k0 + 16 * (idx / T::BN));
+        int c = gk0 / RS;
+        const int rem = gk0 - c * RS;
+        int r = rem / S;
+        int s = rem - r * S;
+        int dy = r * dh, dx = s * dw;
+        int rowoff = c * HW + dy * W + dx;  // offset of (c, dy, dx) from (0, h0, w0)
+        const char *x = reinterpret_cast<const char *>(p.B);
 #pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-            const int dy = (gk + rr < p.K) ? (int)r * dh : kFar;
-            const int dx = (int)s * dw;
-            const int chan = (int)c * HW;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int h = cl.h0[e] + dy, w = cl.w0[e] + dx;
-                float v = 0.f;
-                if ((unsigned)h < (unsigned)H && (unsigned)w < (unsigned)W)
-                    v = p.B[cl.img[e] + chan + h * W + w];
-                b[rr][e] = v;
-            }
-            if (++s == (unsigned)S) {
+        for (int i = 0; i < 16; ++i) {
+            const int h = cl.h0 + dy, w = cl.w0 + dx;
+            const bool ok = (gk0 + i < p.K) && (unsigned)h < (unsigned)H && (unsigned)w < (unsigned)W;
+            const unsigned off = ok ? (unsigned)(cl.base + rowoff) * 4u : 0u;
+            const float v = *reinterpret_cast<const float *>(x + off);
+            b[i >> 2][i & 3] = ok ? v : 0.f;
+            dx += dw;
+            rowoff += dw;
+            if (++s == S) {
                 s = 0;
-                if (++r == (unsigned)R) {
+                dx = 0;
+                dy += dh;
+                rowoff += dh * W - S * dw;
+                if (++r == R) {
                     r = 0;
+                    dy = 0;
+                    rowoff += HW - R * dh * W;
                     ++c;
                 }
             }
         }
+    }
+
+    // b[j] holds k rows 4j .. 4j + 3 of the piece: one 16-byte LDS write each
+    template <class T>
+    __device__ __forceinline__ void store_b(float *Bs, int idx, const f32x4 (&b)[4]) const
+    {
+        float *dst = Bs + (idx % T::BN) * T::PITCH + 16 * (idx / T::BN);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) *reinterpret_cast<f32x4 *>(dst + 4 * j) = b[j];
     }
 
     // Column (n, p, q) of the product is y[n][.][p][q]: image offset + p Q + q.
@@ -137,6 +159,7 @@ const ConvConfig kConvConfigs[] = {
 constexpr int kNumConvConfigs = sizeof(kConvConfigs) / sizeof(kConvConfigs[0]);
 constexpr int kCus = 256;
 constexpr int64_t kMaxI32 = 0x7fffffff;
+constexpr int64_t kMaxRun = (int64_t(1) << 30) - 1;  // elements of x per launch
 
 }  // namespace
 
@@ -147,25 +170,44 @@ const char *conv_config_name(int cfg)
     return (cfg >= 0 && cfg < kNumConvConfigs) ? kConvConfigs[cfg].name : nullptr;
 }
 
-// The product is M = K filters by N = images * P * Q columns. Filter counts are often
-// 64-256, so a tall tile can be mostly padding; the choice weighs each tile shape's
-// padded area, the rounds of tiles the 256 CUs need, and the tile's own rate:
+// The product is M = K filters by N columns (batch such products side by side).
+// Filter counts are often 64-256, so a tall tile can be mostly padding; the choice
+// weighs each tile shape's padded area, the rounds of tiles the 256 CUs need and the
+// tile's own rate, with as many workgroups per CU as there are tiles to share it:
+//   per CU = min(workgroups a CU holds, ceil(tiles / CUs)),
 //   time ~ ceil(tiles / (CUs * per CU)) * per CU * BM * BN / rate.
-int conv_select_config(int64_t M, int64_t N)
+int conv_select_config(int64_t M, int64_t N, int64_t batch)
 {
     int best = 0;
     double best_t = 0;
     for (int c = 0; c < kNumConvConfigs; ++c) {
         const ConvConfig &k = kConvConfigs[c];
-        const int64_t tiles = ((M + k.bm - 1) / k.bm) * ((N + k.bn - 1) / k.bn);
-        const int64_t slots = (int64_t)kCus * k.wg_per_cu;
-        const double t = (double)((tiles + slots - 1) / slots) * k.wg_per_cu * k.bm * k.bn / k.tflops;
+        const int64_t tiles = ((M + k.bm - 1) / k.bm) * ((N + k.bn - 1) / k.bn) * batch;
+        int64_t per_cu = (tiles + kCus - 1) / kCus;
+        if (per_cu > k.wg_per_cu) per_cu = k.wg_per_cu;
+        const int64_t slots = kCus * per_cu;
+        const double t = (double)((tiles + slots - 1) / slots) * per_cu * k.bm * k.bn / k.tflops;
         if (c == 0 || t < best_t) {
             best = c;
             best_t = t;
         }
     }
     return best;
+}
+
+// 1 x 1 filters, unit stride, no padding, feature maps large enough that per-image
+// products waste little of their last tile: y[n] (K x HW) = w (K x C) x[n] (C x HW),
+// the images as one strided batch of the plain GEMM.
+bool conv_is_batched_gemm(const ConvArgs &a)
+{
+    return a.R == 1 && a.S == 1 && a.sh == 1 && a.sw == 1 && a.ph == 0 && a.pw == 0 &&
+           a.H * a.W >= 1024;
+}
+
+int conv_choose_config(const ConvArgs &a)
+{
+    if (conv_is_batched_gemm(a)) return conv_select_config(a.K, a.H * a.W, a.N < 65535 ? a.N : 65535);
+    return conv_select_config(a.K, a.N * a.P * a.Q, 1);
 }
 
 // Shapes are validated by the caller: every size >= 1 (C may be 0: then y is zeroed),
@@ -175,12 +217,9 @@ hipError_t conv_launch(int cfg, const ConvArgs &a, hipStream_t stream)
     const int64_t PQ = a.P * a.Q, HW = a.H * a.W, CHW = a.C * HW, KPQ = a.K * PQ;
     if (a.C == 0) return zero_fill_launch(a.y, a.N * a.K, PQ, PQ, stream);
 
-    // Pointwise filter over feature maps large enough that per-image products waste
-    // little of their last tile: y[n] (K x HW) = w (K x C) x[n] (C x HW), the images
-    // as one strided batch.
-    if (a.R == 1 && a.S == 1 && a.sh == 1 && a.sw == 1 && a.ph == 0 && a.pw == 0 && HW >= 1024) {
-        const int gcfg = (cfg >= 0) ? kConvConfigs[cfg].gemm_cfg
-                                    : gemm_select_config(a.K, HW, a.C, a.N < 65535 ? a.N : 65535);
+    if (cfg < 0) cfg = conv_choose_config(a);
+    if (conv_is_batched_gemm(a)) {
+        const int gcfg = kConvConfigs[cfg].gemm_cfg;
         for (int64_t n0 = 0; n0 < a.N; n0 += 65535) {
             GemmArgs g;
             g.A = a.w;
@@ -202,7 +241,6 @@ hipError_t conv_launch(int cfg, const ConvArgs &a, hipStream_t stream)
         return hipSuccess;
     }
 
-    if (cfg < 0) cfg = conv_select_config(a.K, a.N * PQ);
     Im2colOperands o;
     o.H = (int)a.H;
     o.W = (int)a.W;
@@ -220,8 +258,8 @@ hipError_t conv_launch(int cfg, const ConvArgs &a, hipStream_t stream)
     o.RS = (int)(a.R * a.S);
     o.CHW = (int)CHW;
     o.KPQ = KPQ;
-    // images per launch: x offsets and product columns stay below 2^31
-    int64_t per = kMaxI32 / CHW;
+    // images per launch: x offsets below 2^30, product columns below 2^31
+    int64_t per = kMaxRun / CHW;
     if (kMaxI32 / PQ < per) per = kMaxI32 / PQ;
     for (int64_t n0 = 0; n0 < a.N; n0 += per) {
         const int64_t nb = (a.N - n0 < per) ? a.N - n0 : per;

@@ -36,7 +36,7 @@
 //
 // An operand policy Ops says where the B panel comes from and where C goes:
 // DenseOperands (below) reads B as a matrix; the convolution gathers B from the
-// input image on the fly.
+// input image on the fly (mm_conv.hip).
 #pragma once
 
 #include "mm_internal.h"
@@ -109,18 +109,30 @@ __device__ __forceinline__ f32x4 load4_masked(const float *p, int valid)
     return v;
 }
 
+// Operand policies. A policy says where the B panel comes from and where C goes:
+//   Cols columns<T>(p, n0, idx)       state of B piece idx's columns, fixed over K;
+//   load_b<T, VEC>(p, cols, k0, n0, idx, full, b)
+//                                     HBM -> registers: piece idx of the K-step at k0
+//                                     (16 elements, zeros outside the operand);
+//   store_b<T>(Bs, idx, b)            registers -> the LDS panel (BN rows of BK
+//                                     k-values, row pitch PITCH);
+//   int64_t c_column(p, gn)           offset of C's column gn (C[m][n] at
+//                                     C + c_column(n) + m * ldc).
+// Pieces idx cover the BK x BN panel exactly once between them.
+
 // The plain product: B is a K x N matrix with row stride ldb, and C element (m, n)
-// is at C + m * ldc + n.
+// is at C + m * ldc + n. Piece idx is the 4 x 4 block at k-group idx % KQ, column
+// group idx / KQ, so the lanes of a wave read 8 rows x 128 contiguous bytes each.
 struct DenseOperands {
     static constexpr bool kMatrixB = true;
     struct Cols {};
-    __device__ Cols columns(const GemmArgs &, int) const { return {}; }
-    // Rows gk .. gk + 3 of B, columns gn .. gn + 3, zeros outside the matrix.
-    // full: the whole piece is inside.
-    template <bool VEC>
-    __device__ __forceinline__ void load_b(const GemmArgs &p, const Cols &, int gk, int gn, bool full,
-                                           f32x4 (&b)[4]) const
+    template <class T>
+    __device__ Cols columns(const GemmArgs &, int, int) const { return {}; }
+    template <class T, bool VEC>
+    __device__ __forceinline__ void load_b(const GemmArgs &p, const Cols &, int k0, int n0, int idx,
+                                           bool full, f32x4 (&b)[4]) const
     {
+        const int gk = k0 + 4 * (idx % T::KQ), gn = n0 + 4 * (idx / T::KQ);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const float *src = p.B + (int64_t)(gk + r) * p.ldb + gn;
@@ -130,6 +142,17 @@ struct DenseOperands {
                 const int valid = (gk + r < p.K) ? p.N - gn : 0;
                 b[r] = load4_masked<VEC>(src, valid);
             }
+        }
+    }
+    // b[r] is k-row r of 4 columns: transposed on the way into LDS
+    template <class T>
+    __device__ __forceinline__ void store_b(float *Bs, int idx, const f32x4 (&b)[4]) const
+    {
+        const int kg = idx % T::KQ, ng = idx / T::KQ;
+#pragma unroll
+        for (int col = 0; col < 4; ++col) {
+            const f32x4 v = {b[0][col], b[1][col], b[2][col], b[3][col]};
+            *reinterpret_cast<f32x4 *>(Bs + (4 * ng + col) * T::PITCH + 4 * kg) = v;
         }
     }
     __device__ int64_t c_column(const GemmArgs &, int gn) const { return gn; }
@@ -191,17 +214,17 @@ __global__ __launch_bounds__(T::NT) void gemm_f32_kernel(GemmArgs p, Ops ops)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-    // What the B source needs to know about the columns this thread stages (the
-    // same columns in every K-step).
+    // What the B source needs to know about the columns of each B piece this thread
+    // stages (the same columns in every K-step).
     typename Ops::Cols cols[T::B_PER_T];
 #pragma unroll
-    for (int c = 0; c < T::B_PER_T; ++c) cols[c] = ops.columns(p, n0 + 4 * ((tid + c * T::NT) / T::KQ));
+    for (int c = 0; c < T::B_PER_T; ++c) cols[c] = ops.template columns<T>(p, n0, tid + c * T::NT);
 
     typename T::Staged r0, r1;
 
     // HBM -> registers for K-step kt. Piece c of thread tid is index tid + c * NT.
     // A piece: row idx / KQ, k-group idx % KQ (a row's pieces are adjacent lanes).
-    // B piece: k-group idx % KQ, column group idx / KQ.
+    // B piece: 16 elements of the BK x BN panel, placed by Ops.
     auto global_load = [&](int kt, typename T::Staged &st) {
         const int k0 = kt * T::BK;
         const bool full = inner_mn && (k0 + T::BK <= p.K);
@@ -222,14 +245,12 @@ __global__ __launch_bounds__(T::NT) void gemm_f32_kernel(GemmArgs p, Ops ops)
 #pragma unroll
         for (int c = 0; c < T::B_PER_T; ++c) {
             const int idx = tid + c * T::NT;
-            if (T::B_BLOCKS % T::NT == 0 || idx < T::B_BLOCKS) {
-                const int kg = idx % T::KQ, ng = idx / T::KQ;
-                ops.template load_b<VEC_B>(p, cols[c], k0 + 4 * kg, n0 + 4 * ng, full, st.b[c]);
-            }
+            if (T::B_BLOCKS % T::NT == 0 || idx < T::B_BLOCKS)
+                ops.template load_b<T, VEC_B>(p, cols[c], k0, n0, idx, full, st.b[c]);
         }
     };
 
-    // registers -> LDS stage `buf` (B transposed on the way in).
+    // registers -> LDS stage `buf` (B stored column by column, k contiguous).
     auto lds_store = [&](int buf, const typename T::Staged &st) {
         float *As = lds + buf * T::STAGE;
         float *Bs = As + T::A_TILE;
@@ -244,15 +265,7 @@ __global__ __launch_bounds__(T::NT) void gemm_f32_kernel(GemmArgs p, Ops ops)
 #pragma unroll
         for (int c = 0; c < T::B_PER_T; ++c) {
             const int idx = tid + c * T::NT;
-            if (T::B_BLOCKS % T::NT == 0 || idx < T::B_BLOCKS) {
-                const int kg = idx % T::KQ, ng = idx / T::KQ;
-#pragma unroll
-                for (int col = 0; col < 4; ++col) {
-                    const f32x4 v = {st.b[c][0][col], st.b[c][1][col], st.b[c][2][col],
-                                     st.b[c][3][col]};
-                    *reinterpret_cast<f32x4 *>(Bs + (4 * ng + col) * T::PITCH + 4 * kg) = v;
-                }
-            }
+            if (T::B_BLOCKS % T::NT == 0 || idx < T::B_BLOCKS) ops.template store_b<T>(Bs, idx, st.b[c]);
         }
     };
 

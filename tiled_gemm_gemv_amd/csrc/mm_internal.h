@@ -90,11 +90,14 @@ struct ConvArgs {
 // Convolution configurations: tile shapes of the GEMM (names as there).
 int conv_num_configs();
 const char *conv_config_name(int cfg);
-// Choice for a product of M filters by N = images * P * Q output positions.
-int conv_select_config(int64_t M, int64_t N);
+// Choice for `batch` products of M filters by N output positions each.
+int conv_select_config(int64_t M, int64_t N, int64_t batch);
+// The configuration conv_launch uses for a shape when none is given.
+int conv_choose_config(const ConvArgs &a);
 // Enqueue the convolution (cfg < 0: choose). The caller has checked the shape:
-// N, K, P, Q >= 1, C >= 0, one image of x below 2^31 elements, C R S and P Q below
-// 2^31, H + 2 ph, W + 2 pw, dh (R - 1), dw (S - 1) below 2^29.
+// N, K, P, Q >= 1, C >= 0, one image of x and the padded plane (H + 2 ph)(W + 2 pw)
+// below 2^30 elements, C R S and P Q below 2^31, H + 2 ph, W + 2 pw, dh (R - 1),
+// dw (S - 1) below 2^29.
 hipError_t conv_launch(int cfg, const ConvArgs &a, hipStream_t stream);
 
 // Enqueue the GEMV (M >= 1, N >= 1).

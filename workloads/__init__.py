@@ -108,6 +108,11 @@ class ConvWorkload:
         Q = (self.W + 2 * self.pad[1] - self.dilation[1] * (self.S - 1) - 1) // self.stride[1] + 1
         return P, Q
 
+    def geometry(self):
+        """(N, C, H, W, K, R, S, sh, sw, ph, pw, dh, dw), the order of the C entry points."""
+        return (self.N, self.C, self.H, self.W, self.K, self.R, self.S, *self.stride, *self.pad,
+                *self.dilation)
+
     def with_dist(self, dist: str) -> "ConvWorkload":
         return ConvWorkload(self.name + "_" + dist, self.N, self.C, self.H, self.W, self.K, self.R,
                             self.S, self.stride, self.pad, self.dilation, self.seed, dist, dist,
