@@ -84,7 +84,7 @@ struct Im2colOperands {
     {
         // first row of the piece: (c, r, s) by division once, then stepped
         const int gk0 = __builtin_amdgcn_readfirstlane(k0 + 16 * (idx / T::BN));
-        int c = gk0 / RS;
+        const int c = gk0 / RS;  // channel of the first row
         const int rem = gk0 - c * RS;
         int r = rem / S;
         int s = rem - r * S;
@@ -98,6 +98,8 @@ struct Im2colOperands {
             const unsigned off = ok ? (unsigned)(cl.base + rowoff) * 4u : 0u;
             const float v = *reinterpret_cast<const float *>(x + off);
             b[i >> 2][i & 3] = ok ? v : 0.f;
+            // next row: s + 1, carrying into r and then c (uniform branches, mostly
+            // not taken: cheaper here than selects evaluated on every row)
             dx += dw;
             rowoff += dw;
             if (++s == S) {
@@ -109,7 +111,6 @@ struct Im2colOperands {
                     r = 0;
                     dy = 0;
                     rowoff += HW - R * dh * W;
-                    ++c;
                 }
             }
         }
@@ -137,7 +138,8 @@ struct ConvConfig {
     hipError_t (*launch)(const GemmArgs &, const Im2colOperands &, hipStream_t);
     int gemm_cfg;       // the same tile shape as a GEMM config (used for 1 x 1 filters)
     int bm, bn;
-    int wg_per_cu;      // workgroups one CU holds (LDS-limited)
+    int waves;          // per workgroup
+    int wg_per_cu;      // workgroups one CU holds (registers and LDS)
     double tflops;      // rate of the tile on large dense shapes, for the choice below
 };
 
@@ -150,14 +152,13 @@ hipError_t launch_im2col(const GemmArgs &a, const Im2colOperands &o, hipStream_t
 // Tile shapes of the fp32 GEMM. The 256 x 256 tile is left out: with the gather's
 // per-column state it no longer fits its 256 registers per lane.
 const ConvConfig kConvConfigs[] = {
-    {"128x128x32 w64x64 pf2 ks1 (4 waves)", &launch_im2col<T128x128k32p2>, 1, 128, 128, 2, 122},
-    {"128x128x32 w64x64 pf1 ks2 (8 waves)", &launch_im2col<T128x128k32s2>, 2, 128, 128, 2, 122},
-    {"64x64x64 w32x32 pf2 ks1 (4 waves)", &launch_im2col<T64x64k64p2>, 3, 64, 64, 2, 113},
-    {"64x64x64 w32x32 pf2 ks2 (8 waves)", &launch_im2col<T64x64k64p2s2>, 4, 64, 64, 2, 94},
-    {"128x64x64 w64x32 pf1 ks2 (8 waves)", &launch_im2col<T128x64k64s2>, 5, 128, 64, 1, 111},
+    {"128x128x32 w64x64 pf2 ks1 (4 waves)", &launch_im2col<T128x128k32p2>, 1, 128, 128, 4, 2, 122},
+    {"128x128x32 w64x64 pf1 ks2 (8 waves)", &launch_im2col<T128x128k32s2>, 2, 128, 128, 8, 1, 122},
+    {"64x64x64 w32x32 pf2 ks1 (4 waves)", &launch_im2col<T64x64k64p2>, 3, 64, 64, 4, 2, 113},
+    {"64x64x64 w32x32 pf2 ks2 (8 waves)", &launch_im2col<T64x64k64p2s2>, 4, 64, 64, 8, 2, 94},
+    {"128x64x64 w64x32 pf1 ks2 (8 waves)", &launch_im2col<T128x64k64s2>, 5, 128, 64, 8, 1, 111},
 };
 constexpr int kNumConvConfigs = sizeof(kConvConfigs) / sizeof(kConvConfigs[0]);
-constexpr int kCus = 256;
 constexpr int64_t kMaxI32 = 0x7fffffff;
 constexpr int64_t kMaxRun = (int64_t(1) << 30) - 1;  // elements of x per launch
 
@@ -171,11 +172,9 @@ const char *conv_config_name(int cfg)
 }
 
 // The product is M = K filters by N columns (batch such products side by side).
-// Filter counts are often 64-256, so a tall tile can be mostly padding; the choice
-// weighs each tile shape's padded area, the rounds of tiles the 256 CUs need and the
-// tile's own rate, with as many workgroups per CU as there are tiles to share it:
-//   per CU = min(workgroups a CU holds, ceil(tiles / CUs)),
-//   time ~ ceil(tiles / (CUs * per CU)) * per CU * BM * BN / rate.
+// Filter counts are often 64-256, so a tall tile can be mostly padding; the choice is
+// the least modelled time (tile_time: padded tile area, rounds over the 256 CUs,
+// waves per CU, the tile's own rate).
 int conv_select_config(int64_t M, int64_t N, int64_t batch)
 {
     int best = 0;
@@ -183,10 +182,7 @@ int conv_select_config(int64_t M, int64_t N, int64_t batch)
     for (int c = 0; c < kNumConvConfigs; ++c) {
         const ConvConfig &k = kConvConfigs[c];
         const int64_t tiles = ((M + k.bm - 1) / k.bm) * ((N + k.bn - 1) / k.bn) * batch;
-        int64_t per_cu = (tiles + kCus - 1) / kCus;
-        if (per_cu > k.wg_per_cu) per_cu = k.wg_per_cu;
-        const int64_t slots = kCus * per_cu;
-        const double t = (double)((tiles + slots - 1) / slots) * per_cu * k.bm * k.bn / k.tflops;
+        const double t = tile_time(tiles, k.bm, k.bn, k.waves, k.wg_per_cu, k.tflops);
         if (c == 0 || t < best_t) {
             best = c;
             best_t = t;

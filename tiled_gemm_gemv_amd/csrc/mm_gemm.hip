@@ -16,19 +16,22 @@ struct ConfigEntry {
     const char *name;
     hipError_t (*launch)(const GemmArgs &, hipStream_t);
     int bm, bn;
+    int waves;       // per workgroup
+    int wg_per_cu;   // workgroups a CU holds (registers and LDS)
+    double tflops;   // measured on large shapes, for the choice below
 };
 
 // name: BMxBNxBK, wave tile, prefetch depth, waves per output block (K split).
 const ConfigEntry kConfigs[] = {
-    {"256x256x32 w128x64 pf1 ks1 (8 waves)", &launch_tile<T256x256k32>, 256, 256},
-    {"128x128x32 w64x64 pf2 ks1 (4 waves)", &launch_tile<T128x128k32p2>, 128, 128},
-    {"128x128x32 w64x64 pf1 ks2 (8 waves)", &launch_tile<T128x128k32s2>, 128, 128},
-    {"64x64x64 w32x32 pf2 ks1 (4 waves)", &launch_tile<T64x64k64p2>, 64, 64},
-    {"64x64x64 w32x32 pf2 ks2 (8 waves)", &launch_tile<T64x64k64p2s2>, 64, 64},
-    {"128x64x64 w64x32 pf1 ks2 (8 waves)", &launch_tile<T128x64k64s2>, 128, 64},
-    {"narrow 16x64 (16x16x4 MFMA), K over 8 waves, 16/NB chunks", &gemm_skinny_launch<8, 16>, 16, 64},
-    {"narrow 16x64 (16x16x4 MFMA), K over 4 waves, 16/NB chunks", &gemm_skinny_launch<4, 16>, 16, 64},
-    {"narrow 16x64 (16x16x4 MFMA), K over 16 waves, 4/NB chunks", &gemm_skinny_launch<16, 4>, 16, 64},
+    {"256x256x32 w128x64 pf1 ks1 (8 waves)", &launch_tile<T256x256k32>, 256, 256, 8, 1, 137},
+    {"128x128x32 w64x64 pf2 ks1 (4 waves)", &launch_tile<T128x128k32p2>, 128, 128, 4, 2, 122},
+    {"128x128x32 w64x64 pf1 ks2 (8 waves)", &launch_tile<T128x128k32s2>, 128, 128, 8, 1, 122},
+    {"64x64x64 w32x32 pf2 ks1 (4 waves)", &launch_tile<T64x64k64p2>, 64, 64, 4, 2, 113},
+    {"64x64x64 w32x32 pf2 ks2 (8 waves)", &launch_tile<T64x64k64p2s2>, 64, 64, 8, 1, 94},
+    {"128x64x64 w64x32 pf1 ks2 (8 waves)", &launch_tile<T128x64k64s2>, 128, 64, 8, 1, 111},
+    {"narrow 16x64 (16x16x4 MFMA), K over 8 waves, 16/NB chunks", &gemm_skinny_launch<8, 16>, 16, 64, 8, 1, 0},
+    {"narrow 16x64 (16x16x4 MFMA), K over 4 waves, 16/NB chunks", &gemm_skinny_launch<4, 16>, 16, 64, 4, 1, 0},
+    {"narrow 16x64 (16x16x4 MFMA), K over 16 waves, 4/NB chunks", &gemm_skinny_launch<16, 4>, 16, 64, 16, 1, 0},
 };
 constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
 
@@ -47,17 +50,26 @@ const char *gemm_config_name(int cfg)
     return (cfg >= 0 && cfg < kNumConfigs) ? kConfigs[cfg].name : nullptr;
 }
 
-// Largest tile that still gives most of the 256 CUs a tile: a big tile reuses
-// each staged element more often, a small one fills the chip on small shapes.
-// (Thresholds from a rocprofv3-timed sweep of every config over 128^3 .. 8192^2.)
+// A big tile reuses each staged element more often; a small one fills the chip on
+// small shapes and leaves a shorter last round. Among the macro-tile configs the
+// choice is the least modelled time (tile_time: padded tile area, rounds over the
+// 256 CUs, waves per CU; rates from a timed sweep of every config, 128^3 .. 8192^2).
 int gemm_select_config(int64_t M, int64_t N, int64_t K, int64_t batch)
 {
     (void)K;
     if (N <= 64) return 8;  // a few columns: stream A once (mm_gemm_skinny.hip)
-    if (batch * tiles_for(0, M, N) >= 200) return 0;
-    if (batch * tiles_for(1, M, N) >= 200) return 1;
-    if (batch * tiles_for(4, M, N) >= 128) return 4;
-    return 6;               // few 64 x 64 tiles: 16-row tiles fill more CUs
+    if (batch * tiles_for(4, M, N) < 128) return 6;  // few 64 x 64 tiles: 16-row tiles fill more CUs
+    int best = 0;
+    double best_t = 0;
+    for (int c = 0; c < 6; ++c) {
+        const ConfigEntry &e = kConfigs[c];
+        const double t = tile_time(batch * tiles_for(c, M, N), e.bm, e.bn, e.waves, e.wg_per_cu, e.tflops);
+        if (c == 0 || t < best_t) {
+            best = c;
+            best_t = t;
+        }
+    }
+    return best;
 }
 
 hipError_t gemm_launch(int cfg, const GemmArgs &a, hipStream_t stream)

@@ -54,10 +54,16 @@ constexpr int kXcds = 8;  // MI355X deals consecutive workgroups to 8 XCDs in tu
 // KS_: waves that share each WM x WN output block. Each takes 1/KS of every K-step's
 // k range; at the end the partial sums meet in LDS and are added in a fixed order.
 // It puts more waves on each SIMD when C has few tiles, with no memory beyond C.
-template <int BM_, int BN_, int BK_, int WM_, int WN_, int GROUP_M_, int PF_ = 1, int KS_ = 1>
+// MID_ (PF = 1): write the next K-step's staged data to LDS halfway through the
+// current step's MFMAs rather than after them, so the wait for those loads and the
+// LDS writes overlap matrix work. Off where the registers are already full (the
+// fragments of both halves and the staged data are then live together).
+template <int BM_, int BN_, int BK_, int WM_, int WN_, int GROUP_M_, int PF_ = 1, int KS_ = 1,
+          bool MID_ = true>
 struct Tile {
     static constexpr int BM = BM_, BN = BN_, BK = BK_, WM = WM_, WN = WN_;
     static constexpr int GROUP_M = GROUP_M_, PF = PF_, KS = KS_;
+    static constexpr bool MID = MID_;
     static constexpr int WAVES_M = BM / WM, WAVES_N = BN / WN;
     static constexpr int WAVES_MN = WAVES_M * WAVES_N;
     static constexpr int NT = WAVES_MN * KS * 64;
@@ -316,10 +322,16 @@ __global__ __launch_bounds__(T::NT) void gemm_f32_kernel(GemmArgs p, Ops ops)
         for (int kt = 0; kt < nk; ++kt) {
             const int cur = kt & 1;
             if (kt + 1 < nk) global_load(kt + 1, r0);
-            multiply(cur, nothing);
             // The other stage was last read in step kt - 1, which every wave
             // finished before the barrier that ended that step.
-            if (kt + 1 < nk) lds_store(cur ^ 1, r0);
+            if constexpr (T::MID) {
+                multiply(cur, [&] {
+                    if (kt + 1 < nk) lds_store(cur ^ 1, r0);
+                });
+            } else {
+                multiply(cur, nothing);
+                if (kt + 1 < nk) lds_store(cur ^ 1, r0);
+            }
             __syncthreads();
         }
     } else {
@@ -432,7 +444,7 @@ hipError_t launch_tile_ops(const GemmArgs &a, const Ops &ops, hipStream_t stream
 }
 
 // The tile shapes of the fp32 GEMM (public config indices 0-5).
-using T256x256k32 = Tile<256, 256, 32, 128, 64, 8>;
+using T256x256k32 = Tile<256, 256, 32, 128, 64, 8, 1, 1, false>;
 using T128x128k32p2 = Tile<128, 128, 32, 64, 64, 8, 2>;
 using T128x128k32s2 = Tile<128, 128, 32, 64, 64, 8, 1, 2>;
 using T64x64k64p2 = Tile<64, 64, 64, 32, 32, 8, 2>;

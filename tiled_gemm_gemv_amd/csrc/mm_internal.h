@@ -56,6 +56,22 @@ struct GemvArgs {
     int M, N;
 };
 
+// Time model for choosing a tile shape (arbitrary units): a workgroup of `waves` waves
+// computes a BM x BN tile at `tflops` when 8 or more waves share its CU, and
+// proportionally slower with fewer (latency is then exposed); a CU holds at most
+// wg_per_cu workgroups; tiles run in rounds over the 256 CUs.
+inline double tile_time(int64_t tiles, int bm, int bn, int waves, int wg_per_cu, double tflops)
+{
+    constexpr int64_t kCus = 256;
+    int64_t per_cu = (tiles + kCus - 1) / kCus;
+    if (per_cu > wg_per_cu) per_cu = wg_per_cu;
+    if (per_cu < 1) per_cu = 1;
+    const int64_t rounds = (tiles + kCus * per_cu - 1) / (kCus * per_cu);
+    double fill = (double)(per_cu * waves) / 8.0;
+    if (fill > 1.0) fill = 1.0;
+    return (double)rounds * per_cu * bm * bn / (tflops * fill);
+}
+
 // GEMM tile configurations, in the order of the public config index.
 int gemm_num_configs();
 const char *gemm_config_name(int cfg);
