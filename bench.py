@@ -455,7 +455,7 @@ def sweep(kind, torch, mm, dev):
         shapes += [(512, 512, 512, ""), (1536, 1536, 1536, ""), (2048, 2048, 2048, ""),
                    (3072, 3072, 3072, ""), (4096, 4096, 4096, ""), (1024, 4096, 4096, ""),
                    (8192, 1792, 4096, "projection, 1/8 of N")]
-        shapes += [(4096, n, 4096, f"FC layer 4096x4096, batch of {n}") for n in (8, 16, 32, 64)]
+        shapes += [(4096, n, 4096, f"FC layer 4096x4096, batch of {n}") for n in (1, 2, 4, 8, 16, 32, 64)]
         nc = mm.mm_gemm_f32_num_configs()
         print("# fp32 GEMM, TFLOP/s per tile configuration (back-to-back launches between two "
               "events, inputs N(0,1))")

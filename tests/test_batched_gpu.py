@@ -74,6 +74,19 @@ def test_narrow_batches(dev):
     check_batch(C.cpu().numpy(), A, B, True)
 
 
+@pytest.mark.parametrize("N", [1, 2, 3, 4])
+def test_few_column_batches(dev, N):
+    """N <= 4 takes the few-columns kernel; batch index on the third grid dimension,
+    odd K and M, and one A shared by every problem (batch stride 0)."""
+    batch, M, K = 4, 301, 1031
+    A = wl.random_matrix(120 + N, M, K, "int4")
+    B = np.stack([wl.random_matrix(130 + b, K, N, "int4") for b in range(batch)])
+    Ad = to_device(A, dev).unsqueeze(0).expand(batch, M, K)
+    C = mm.gemm_batched(Ad, to_device(B, dev))
+    torch.cuda.synchronize()
+    check_batch(C.cpu().numpy(), np.stack([A] * batch), B, True)
+
+
 def test_empty_and_k_zero(dev):
     C = torch.full((3, 4, 5), float("nan"), device=dev)
     mm.gemm_batched(torch.empty((3, 4, 0), device=dev), torch.empty((3, 0, 5), device=dev), out=C)

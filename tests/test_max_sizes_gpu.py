@@ -190,7 +190,7 @@ def test_gemm16_grid_beyond_2_32_work_items(dev, cfg):
     torch.cuda.empty_cache()
 
 
-@pytest.mark.parametrize("cfg", [None, 6, 7, 8])   # the narrow-C kernel: 16-row blocks
+@pytest.mark.parametrize("cfg", [None, 6, 7, 8, 9])   # narrow-C kernels: 16-row, 8-row blocks
 def test_narrow_gemm_grid_beyond_2_32_work_items(dev, cfg):
     K, N, blk = 2, 3, 1024
     M = 70_000_640                                 # 4,375,040 blocks of 16 rows

@@ -32,6 +32,7 @@ const ConfigEntry kConfigs[] = {
     {"narrow 16x64 (16x16x4 MFMA), K over 8 waves, 16/NB chunks", &gemm_skinny_launch<8, 16>, 16, 64, 8, 1, 0},
     {"narrow 16x64 (16x16x4 MFMA), K over 4 waves, 16/NB chunks", &gemm_skinny_launch<4, 16>, 16, 64, 4, 1, 0},
     {"narrow 16x64 (16x16x4 MFMA), K over 16 waves, 4/NB chunks", &gemm_skinny_launch<16, 4>, 16, 64, 16, 1, 0},
+    {"columns <= 4: one wave per row, B rounds in LDS (8 x 4 per workgroup)", &gemm_cols_launch, 8, 4, 4, 1, 0},
 };
 constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
 
@@ -57,6 +58,7 @@ const char *gemm_config_name(int cfg)
 int gemm_select_config(int64_t M, int64_t N, int64_t K, int64_t batch)
 {
     (void)K;
+    if (N <= 4) return 9;   // a GEMV with a few vectors (mm_gemm_cols.hip)
     if (N <= 64) return 8;  // a few columns: stream A once (mm_gemm_skinny.hip)
     if (batch * tiles_for(4, M, N) < 128) return 6;  // few 64 x 64 tiles: 16-row tiles fill more CUs
     int best = 0;

@@ -86,6 +86,10 @@ hipError_t gemm_launch(int cfg, const GemmArgs &a, hipStream_t stream);
 template <int W, int L>
 hipError_t gemm_skinny_launch(const GemmArgs &a, hipStream_t stream);
 
+// GEMM for C with few columns (mm_gemm_cols.hip): one wave per row, B staged in LDS;
+// correct for any shape, meant for N <= 4.
+hipError_t gemm_cols_launch(const GemmArgs &a, hipStream_t stream);
+
 // GEMM with 16-bit inputs (mm_gemm_h16.hip); A and B hold bf16 (bf16 = true) or
 // binary16 bit patterns, C is fp32. M, N, K >= 1.
 int gemm16_num_configs();
