@@ -88,6 +88,32 @@ def test_workloads(dev, fmt, cfg, name):
     assert r, str(r)
 
 
+# Shapes the direct HBM -> LDS pipeline takes (K % 32 == 0, N % 8 == 0, aligned): one,
+# two, three and many K-steps (its prologue fills up to three stages), M and N that
+# are not tile multiples (clamped loads, masked stores), a single row.
+DIRECT_SHAPES = [(1, 8, 32), (37, 8, 64), (300, 264, 96), (257, 520, 128), (129, 136, 4096),
+                 (1000, 1528, 800)]
+
+
+@pytest.mark.parametrize("fmt", list(FORMATS))
+@pytest.mark.parametrize("cfg", [5, 6, None])
+@pytest.mark.parametrize("shape", DIRECT_SHAPES)
+def test_direct_pipeline_shapes(dev, fmt, cfg, shape):
+    M, N, K = shape
+    A = wl.random_matrix(700 + M, M, K, "int4")
+    B = wl.random_matrix(800 + N, K, N, "int4")
+    C, Af, Bf = run(A, B, fmt, dev, cfg)
+    C64, _ = oracle.gemm(Af, Bf)
+    r = verify.exact(C, C64)
+    assert r, f"{shape}: {r}"
+    A = wl.random_matrix(900 + M, M, K, "normal")
+    B = wl.random_matrix(1000 + N, K, N, "normal")
+    C, Af, Bf = run(A, B, fmt, dev, cfg)
+    C64, S64 = oracle.gemm(Af, Bf)
+    r = verify.within_tol(C, C64, S64, REL_TOL)
+    assert r, f"{shape}: {r}"
+
+
 @pytest.mark.parametrize("fmt", list(FORMATS))
 @pytest.mark.parametrize("cfg", CONFIGS)
 def test_permutation_and_edges(dev, fmt, cfg):

@@ -344,6 +344,217 @@ hipError_t launch16(const Gemm16Args &a, hipStream_t stream)
     return hipLaunchKernel(fn, dim3(gx, gy), dim3(T::NT), args, 0, stream);
 }
 
+// ---------------------------------------------------------------------------
+// Direct HBM -> LDS pipeline (the fast path for aligned shapes).
+//
+// gfx950's global_load_lds_dwordx4 moves 16 bytes per lane from memory straight into
+// LDS (lane l's bytes land at M0 + 16 l), with no staging registers. That frees the
+// registers the loop above spends on staged data, so the pipeline can run NS = 4 LDS
+// stages deep: the loads for K-step kt + 3 are issued while step kt's MFMAs run, which
+// covers three K-steps of MFMA time instead of one. BK = 32 (64-byte A rows).
+//   * A panel (BM rows x 32 k): stored as loaded, 64 bytes per row; the four 16-byte
+//     chunks of row r sit in slots c ^ swz_a(r), so that the MFMA operand reads of 32
+//     rows at one k fall in distinct banks (no padding; the load pattern applies the
+//     permutation by choosing which chunk each lane fetches).
+//   * B panel (32 k rows x BN): stored row-major as loaded, chunks of row k in slots
+//     c ^ swz_b(k). The MFMA wants 8 consecutive k of one column per lane; gfx950's
+//     ds_read_b64_tr_b16 provides them: in each group of 16 lanes, result lane i,
+//     element c is element i % 4 of the 4 values lane 4 c + i / 4 addressed. Lane j of a
+//     group therefore addresses row k0 + j / 4, columns n + 4 (j % 4), and result lane i
+//     receives column n + i at rows k0 .. k0 + 3; two such reads give the 8 k.
+//   * One barrier per K-step, after an explicit wait for the step's loads (vmcnt
+//     counts the loads of the steps issued after it). The loads are issued from inline
+//     asm so that the compiler does not add a wait for all of them before every LDS read.
+//   * Requirements (checked on the host): K % 32 == 0, N % 8 == 0, lda and ldb
+//     multiples of 8 elements, A and B 16-byte aligned. Rows past M and column chunks
+//     past N are clamped to in-range ones; they only feed C elements that are not
+//     stored. K needs no mask (whole K-steps).
+template <int BM_, int BN_, int WM_, int WN_>
+struct Direct16 {
+    static constexpr int BM = BM_, BN = BN_, BK = 32, NS = 4, WM = WM_, WN = WN_;
+    static constexpr int WAVES = (BM / WM) * (BN / WN), NT = WAVES * 64;
+    static constexpr int FM = WM / 32, FN = WN / 32;
+    static constexpr int A_BYTES = BM * BK * 2, B_BYTES = BK * BN * 2;
+    static constexpr int STAGE = A_BYTES + B_BYTES;
+    static constexpr int B_ROW = BN * 2;                      // bytes per B row
+    static constexpr int A_LOADS = BM / 16 / WAVES;           // 1 KB loads per wave per step
+    static constexpr int B_LOADS = BN / 16 / WAVES;
+    static constexpr int B_ROWS_PER_LOAD = 1024 / B_ROW;
+    static_assert(BM % (16 * WAVES) == 0 && BN % (16 * WAVES) == 0, "whole 1 KB loads per wave");
+    static_assert(BN >= 64 && BN % 32 == 0 && WN % 32 == 0 && WM % 32 == 0, "tile shape");
+    static_assert(NS * STAGE <= 160 * 1024, "stages must fit the 160 KB LDS");
+};
+
+__device__ __forceinline__ int swz_a16(int row) { return ((row >> 1) ^ (row >> 3)) & 3; }
+
+template <class T>
+__device__ __forceinline__ int swz_b16(int krow)
+{
+    return (krow % (T::BN / 32)) * 4;  // spreads 4 consecutive rows over the banks
+}
+
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) char lds_char;
+
+// 16 bytes per lane from src into LDS at lds_addr + 16 * lane (lds_addr wave-uniform).
+__device__ __forceinline__ void load_to_lds(unsigned lds_addr, const unsigned short *src)
+{
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
+                 :: "s"(__builtin_amdgcn_readfirstlane(lds_addr)), "v"(src) : "memory");
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt()
+{
+    static_assert(N >= 0 && N <= 63, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
+}
+
+template <class T, bool BF16>
+__global__ __launch_bounds__(T::NT) void gemm_h16_direct_kernel(Gemm16Args p)
+{
+    __shared__ __attribute__((aligned(1024))) char lds[T::NS * T::STAGE];
+    const int tiles_m = (p.M + T::BM - 1) / T::BM;
+    const int tiles_n = (p.N + T::BN - 1) / T::BN;
+    const int64_t tiles = (int64_t)tiles_m * tiles_n;
+    const int64_t bid = linear_block();
+    if (bid >= tiles) return;  // padding of a 2-D grid (whole workgroup, before any barrier)
+    int tm, tn;
+    tile_of_block16((int)bid, (int)tiles, tiles_m, tiles_n, tm, tn);
+    const int m0 = tm * T::BM, n0 = tn * T::BN;
+
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int wm0 = (w / (T::BN / T::WN)) * T::WM, wn0 = (w % (T::BN / T::WN)) * T::WN;
+    const int nk = p.K / T::BK;
+
+    // this lane's sources for the wave's loads of every K-step (advanced by BK per step)
+    const unsigned short *asrc[T::A_LOADS];
+    const unsigned short *bsrc[T::B_LOADS];
+#pragma unroll
+    for (int i = 0; i < T::A_LOADS; ++i) {
+        const int row = 16 * (T::A_LOADS * w + i) + (lane >> 2);
+        const int chunk = (lane & 3) ^ swz_a16(row);
+        asrc[i] = p.A + (int64_t)min(m0 + row, p.M - 1) * p.lda + 8 * chunk;
+    }
+#pragma unroll
+    for (int i = 0; i < T::B_LOADS; ++i) {
+        constexpr int CPR = T::B_ROW / 16;  // 16-byte chunks per B row
+        const int krow = T::B_ROWS_PER_LOAD * (T::B_LOADS * w + i) + lane / CPR;
+        const int chunk = (lane % CPR) ^ swz_b16<T>(krow);
+        bsrc[i] = p.B + (int64_t)krow * p.ldb + min(n0 + 8 * chunk, p.N - 8);
+    }
+    const unsigned lds0 = (unsigned)(uintptr_t)(lds_char *)lds;  // LDS byte offset of the array
+    auto issue = [&](int kt) {
+        const unsigned st = lds0 + (kt % T::NS) * T::STAGE;
+#pragma unroll
+        for (int i = 0; i < T::A_LOADS; ++i)
+            load_to_lds(st + (T::A_LOADS * w + i) * 1024, asrc[i] + (int64_t)kt * T::BK);
+#pragma unroll
+        for (int i = 0; i < T::B_LOADS; ++i)
+            load_to_lds(st + T::A_BYTES + (T::B_LOADS * w + i) * 1024,
+                        bsrc[i] + (int64_t)kt * T::BK * p.ldb);
+    };
+
+    // operand addresses inside a stage (bytes), for the two 16-k halves of a K-step
+    int a_off[2][T::FM], b_off[2][2][T::FN];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+        for (int i = 0; i < T::FM; ++i) {
+            const int row = wm0 + 32 * i + (lane & 31);
+            a_off[ks][i] = row * 64 + 16 * ((2 * ks + (lane >> 5)) ^ swz_a16(row));
+        }
+        const int g = lane >> 4, j16 = lane & 15;
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int j = 0; j < T::FN; ++j) {
+                const int krow = 16 * ks + 8 * (g >> 1) + 4 * h + (j16 >> 2);
+                const int col = wn0 + 32 * j + 16 * (g & 1) + 4 * (j16 & 3);
+                b_off[ks][h][j] = T::A_BYTES + krow * T::B_ROW +
+                                  16 * ((col >> 3) ^ swz_b16<T>(krow)) + 8 * ((col >> 2) & 1);
+            }
+    }
+
+    f32x16 acc[T::FM][T::FN];
+#pragma unroll
+    for (int i = 0; i < T::FM; ++i)
+#pragma unroll
+        for (int j = 0; j < T::FN; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+    constexpr int LOADS = T::A_LOADS + T::B_LOADS;  // per wave per K-step
+    for (int s = 0; s < T::NS - 1 && s < nk; ++s) issue(s);
+    for (int kt = 0; kt < nk; ++kt) {
+        // step kt's loads are done when at most the later steps' loads are outstanding
+        const int later = nk - 1 - kt;
+        if (later >= 2) wait_vmcnt<2 * LOADS>();
+        else if (later == 1) wait_vmcnt<LOADS>();
+        else wait_vmcnt<0>();
+        // every wave's loads for stage kt are in LDS, and every wave is done with the
+        // stage the next issue overwrites (read in step kt - 1)
+        __syncthreads();
+        if (kt + T::NS - 1 < nk) issue(kt + T::NS - 1);
+        const lds_char *st = (const lds_char *)lds + (kt % T::NS) * T::STAGE;
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            u32x4 a[T::FM], b[T::FN];
+#pragma unroll
+            for (int i = 0; i < T::FM; ++i)
+                a[i] = *(const __attribute__((address_space(3))) u32x4 *)(st + a_off[ks][i]);
+#pragma unroll
+            for (int j = 0; j < T::FN; ++j) {
+                const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (__attribute__((address_space(3))) v4i16 *)(st + b_off[ks][0][j]));
+                const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (__attribute__((address_space(3))) v4i16 *)(st + b_off[ks][1][j]));
+                const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+                b[j] = u32x4{l2[0], l2[1], h2[0], h2[1]};
+            }
+#pragma unroll
+            for (int i = 0; i < T::FM; ++i)
+#pragma unroll
+                for (int j = 0; j < T::FN; ++j) acc[i][j] = mfma16<BF16>(a[i], b[j], acc[i][j]);
+        }
+    }
+
+    const int col_l = lane & 31, row_l = 4 * (lane >> 5);
+#pragma unroll
+    for (int i = 0; i < T::FM; ++i)
+#pragma unroll
+        for (int j = 0; j < T::FN; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int gm = m0 + wm0 + i * 32 + 8 * (r >> 2) + row_l + (r & 3);
+                const int gn = n0 + wn0 + j * 32 + col_l;
+                if (gm < p.M && gn < p.N) p.C[(int64_t)gm * p.ldc + gn] = acc[i][j][r];
+            }
+}
+
+// The direct pipeline's requirements (see above).
+bool direct_ok(const Gemm16Args &a)
+{
+    return a.K % 32 == 0 && a.N >= 8 && a.N % 8 == 0 && a.lda % 8 == 0 && a.ldb % 8 == 0 &&
+           (uintptr_t)a.A % 16 == 0 && (uintptr_t)a.B % 16 == 0;
+}
+
+template <class T, bool BF16>
+hipError_t launch16_direct(const Gemm16Args &a, hipStream_t stream)
+{
+    const int64_t tiles = (int64_t)((a.M + T::BM - 1) / T::BM) * ((a.N + T::BN - 1) / T::BN);
+    if (tiles > 0x7fffffff) return hipErrorInvalidConfiguration;
+    unsigned gx, gy;
+    if (!grid_for(tiles, gx, gy)) return hipErrorInvalidConfiguration;
+    Gemm16Args arg = a;
+    void *args[] = {&arg};
+    return hipLaunchKernel(reinterpret_cast<const void *>(&gemm_h16_direct_kernel<T, BF16>),
+                           dim3(gx, gy), dim3(T::NT), args, 0, stream);
+}
+
+using D16L = Direct16<256, 256, 128, 64>;
+using D16M = Direct16<128, 128, 64, 64>;
+
 using T16L = Tile16<256, 256, 128, 64>;
 using T16M = Tile16<128, 128, 64, 64>;
 using T16S = Tile16<64, 64, 32, 32>;
@@ -352,21 +563,25 @@ using T16Sp2 = Tile16<64, 64, 32, 32, 2>;
 
 }  // namespace
 
-int gemm16_num_configs() { return 5; }
+int gemm16_num_configs() { return 7; }
 
 const char *gemm16_config_name(int cfg)
 {
     static const char *names[] = {"256x256x64 w128x64 pf1 (8 waves)", "128x128x64 w64x64 pf1 (4 waves)",
                                   "64x64x64 w32x32 pf1 (4 waves)", "128x128x64 w64x64 pf2 (4 waves)",
-                                  "64x64x64 w32x32 pf2 (4 waves)"};
-    return (cfg >= 0 && cfg < 5) ? names[cfg] : nullptr;
+                                  "64x64x64 w32x32 pf2 (4 waves)",
+                                  "256x256x32 w128x64 direct-to-LDS 4 stages (8 waves)",
+                                  "128x128x32 w64x64 direct-to-LDS 4 stages (4 waves)"};
+    return (cfg >= 0 && cfg < 7) ? names[cfg] : nullptr;
 }
 
 int gemm16_select_config(int64_t M, int64_t N, int64_t K)
 {
     (void)K;
-    if (((M + 255) / 256) * ((N + 255) / 256) >= 200) return 0;
-    if (((M + 127) / 128) * ((N + 127) / 128) >= 200) return 3;
+    // 5 and 6 are the direct pipelines; on shapes they cannot take they run the 256 x 256
+    // and 128 x 128 register-staged kernels (configs 0 and 3)
+    if (((M + 255) / 256) * ((N + 255) / 256) >= 200) return 5;
+    if (((M + 127) / 128) * ((N + 127) / 128) >= 200) return 6;
     return 4;
 }
 
@@ -388,7 +603,15 @@ hipError_t gemm16_launch(int cfg, bool bf16, const void *A, int64_t lda, const v
     case 1: return bf16 ? launch16<T16M, true>(a, stream) : launch16<T16M, false>(a, stream);
     case 2: return bf16 ? launch16<T16S, true>(a, stream) : launch16<T16S, false>(a, stream);
     case 3: return bf16 ? launch16<T16Mp2, true>(a, stream) : launch16<T16Mp2, false>(a, stream);
-    default: return bf16 ? launch16<T16Sp2, true>(a, stream) : launch16<T16Sp2, false>(a, stream);
+    case 4: return bf16 ? launch16<T16Sp2, true>(a, stream) : launch16<T16Sp2, false>(a, stream);
+    // the direct pipelines; shapes they do not take run the same tile size staged
+    // through registers
+    case 5:
+        if (!direct_ok(a)) return gemm16_launch(0, bf16, A, lda, B, ldb, C, ldc, M, N, K, stream);
+        return bf16 ? launch16_direct<D16L, true>(a, stream) : launch16_direct<D16L, false>(a, stream);
+    default:
+        if (!direct_ok(a)) return gemm16_launch(3, bf16, A, lda, B, ldb, C, ldc, M, N, K, stream);
+        return bf16 ? launch16_direct<D16M, true>(a, stream) : launch16_direct<D16M, false>(a, stream);
     }
 }
 
