@@ -74,6 +74,22 @@ def test_narrow_batches(dev):
     check_batch(C.cpu().numpy(), A, B, True)
 
 
+def test_large_batches_sampled_rows(dev):
+    """16 problems of 1024^3: enough tiles for the 256 x 256 direct-to-LDS tile (batch on
+    the third grid dimension); 8 sampled rows of every problem checked exactly."""
+    batch, M, N, K = 16, 1024, 1024, 1024
+    A = np.stack([wl.random_matrix(140 + b, M, K, "int4") for b in range(batch)])
+    B = np.stack([wl.random_matrix(160 + b, K, N, "int4") for b in range(batch)])
+    C = mm.gemm_batched(to_device(A, dev), to_device(B, dev))
+    torch.cuda.synchronize()
+    got = C.cpu().numpy()
+    rows = np.array([0, 1, 255, 256, 511, 700, 1022, 1023])
+    for b in range(batch):
+        C64, _ = oracle.gemm(A[b], B[b], rows=rows)
+        r = verify.exact(got[b][rows], C64)
+        assert r, f"problem {b}: {r}"
+
+
 @pytest.mark.parametrize("N", [1, 2, 3, 4])
 def test_few_column_batches(dev, N):
     """N <= 4 takes the few-columns kernel; batch index on the third grid dimension,

@@ -113,6 +113,25 @@ def edge_shapes(seed, count):
     return shapes
 
 
+# Shapes the direct-to-LDS pipelines take (K % 16 == 0, N % 4 == 0, aligned): one, two,
+# three, four and many K-steps (the prologue fills up to three stages), M and N that are
+# not tile multiples (clamped loads, masked stores).
+DIRECT_SHAPES = [(1, 4, 16), (37, 8, 32), (300, 264, 48), (257, 520, 64), (129, 136, 4096),
+                 (1000, 1532, 800)]
+
+
+@pytest.mark.parametrize("cfg", [10, 11, None])
+@pytest.mark.parametrize("shape", DIRECT_SHAPES)
+def test_direct_pipeline_shapes(dev, cfg, shape):
+    M, N, K = shape
+    A = wl.random_matrix(1100 + M, M, K, "int4")
+    B = wl.random_matrix(1200 + N, K, N, "int4")
+    assert_exact(gpu_gemm(A, B, dev, cfg), A, B)
+    A = wl.random_matrix(1300 + M, M, K, "normal")
+    B = wl.random_matrix(1400 + N, K, N, "normal")
+    assert_tol(gpu_gemm(A, B, dev, cfg), A, B)
+
+
 @pytest.mark.parametrize("cfg", CONFIGS)
 def test_edge_shape_sweep(dev, cfg):
     """Shapes around tile multiples in every dimension; integer inputs, exact."""

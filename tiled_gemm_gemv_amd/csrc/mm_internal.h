@@ -86,6 +86,12 @@ hipError_t gemm_launch(int cfg, const GemmArgs &a, hipStream_t stream);
 template <int W, int L>
 hipError_t gemm_skinny_launch(const GemmArgs &a, hipStream_t stream);
 
+// fp32 GEMM with panels loaded straight into LDS (mm_gemm_direct.hip), 256 x 256 and
+// 128 x 128 tiles; only for shapes direct_f32_ok accepts.
+bool direct_f32_ok(const GemmArgs &a);
+hipError_t gemm_direct_launch_256(const GemmArgs &a, hipStream_t stream);
+hipError_t gemm_direct_launch_128(const GemmArgs &a, hipStream_t stream);
+
 // GEMM for C with few columns (mm_gemm_cols.hip): one wave per row, B staged in LDS;
 // correct for any shape, meant for N <= 4.
 hipError_t gemm_cols_launch(const GemmArgs &a, hipStream_t stream);
