@@ -90,8 +90,9 @@ __device__ __forceinline__ void gemv_round(const f32x4 *ar, const f32x4 *x4, int
 // all of them (x would otherwise be read from L2 by every wave: as many bytes as A).
 // The two LDS buffers alternate between rounds: buffer r & 1 is written in round r
 // only after the barrier of round r - 1, by which time every wave has finished
-// reading it in round r - 2.
-__global__ __launch_bounds__(kRows * 64) void gemv_f32_vec_kernel(GemvArgs p)
+// reading it in round r - 2. TAIL: the last round of a row is partial.
+template <bool TAIL>
+__device__ __forceinline__ void gemv_vec_rows(const GemvArgs &p)
 {
     __shared__ f32x4 xs[2][kRound];
     const int64_t groups = ((int64_t)p.M + kRows - 1) / kRows;
@@ -108,9 +109,25 @@ __global__ __launch_bounds__(kRows * 64) void gemv_f32_vec_kernel(GemvArgs p)
     float acc = 0.f;
     int r = 0;
     for (; r < full; ++r) gemv_round<true>(ar, x4, n4, r * kRound, rot, xs[r & 1], acc);
-    if (r * kRound < n4) gemv_round<false>(ar, x4, n4, r * kRound, rot, xs[r & 1], acc);
+    if (TAIL) gemv_round<false>(ar, x4, n4, r * kRound, rot, xs[r & 1], acc);
     acc = wave_sum(acc);
     if (row_ok && lane == 0) p.y[row] = acc;
+}
+
+// N a multiple of 4096 (every round full). At most 128 VGPRs, so that a SIMD holds 4
+// of these waves and a CU 4 workgroups: the 1024 workgroups of a 4096 x 4096 A then
+// all start at once. With the partial-round code in the same kernel it took 130 VGPRs
+// (3 workgroups per CU: a quarter of them waited for a second pass, 3% slower).
+__global__ __launch_bounds__(kRows * 64) __attribute__((amdgpu_waves_per_eu(4)))
+void gemv_f32_vec_kernel(GemvArgs p)
+{
+    gemv_vec_rows<false>(p);
+}
+
+// Other N (N % 4 == 0): the last round of each row is partial.
+__global__ __launch_bounds__(kRows * 64) void gemv_f32_vec_tail_kernel(GemvArgs p)
+{
+    gemv_vec_rows<true>(p);
 }
 
 // Any alignment: one wave (workgroup) per row, 4-byte pieces, x from L1/L2.
@@ -159,8 +176,9 @@ hipError_t gemv_launch(const GemvArgs &a, hipStream_t stream)
     unsigned gx, gy;
     if (vec) {
         if (!grid_for(((int64_t)a.M + kRows - 1) / kRows, gx, gy)) return hipErrorInvalidConfiguration;
-        return hipLaunchKernel(reinterpret_cast<const void *>(&gemv_f32_vec_kernel), dim3(gx, gy),
-                               dim3(kRows * 64), args, 0, stream);
+        const void *fn = (a.N % (4 * kRound) == 0) ? reinterpret_cast<const void *>(&gemv_f32_vec_kernel)
+                                                    : reinterpret_cast<const void *>(&gemv_f32_vec_tail_kernel);
+        return hipLaunchKernel(fn, dim3(gx, gy), dim3(kRows * 64), args, 0, stream);
     }
     if (!grid_for(a.M, gx, gy)) return hipErrorInvalidConfiguration;
     return hipLaunchKernel(reinterpret_cast<const void *>(&gemv_f32_kernel), dim3(gx, gy), dim3(64),
