@@ -120,7 +120,7 @@ DIRECT_SHAPES = [(1, 4, 16), (37, 8, 32), (300, 264, 48), (257, 520, 64), (129, 
                  (1000, 1532, 800)]
 
 
-@pytest.mark.parametrize("cfg", [10, 11, None])
+@pytest.mark.parametrize("cfg", [10, 11, 12, 13, None])
 @pytest.mark.parametrize("shape", DIRECT_SHAPES)
 def test_direct_pipeline_shapes(dev, cfg, shape):
     M, N, K = shape
@@ -129,6 +129,25 @@ def test_direct_pipeline_shapes(dev, cfg, shape):
     assert_exact(gpu_gemm(A, B, dev, cfg), A, B)
     A = wl.random_matrix(1300 + M, M, K, "normal")
     B = wl.random_matrix(1400 + N, K, N, "normal")
+    assert_tol(gpu_gemm(A, B, dev, cfg), A, B)
+
+
+# Shapes that only the 4-byte DMA lanes take (K % 16 != 0, odd leading dimensions, N < 4):
+# a partial K-step alone (K < 16), after one or many full steps, with a pipeline deeper
+# than the K loop, and the ragged shape of the benchmark set (lda 777, ldb 1531).
+DIRECT_RAGGED = [(1, 1, 1), (5, 3, 7), (64, 64, 15), (130, 70, 33), (257, 2, 1), (65, 129, 113),
+                 (1000, 1531, 777), (129, 67, 4099)]
+
+
+@pytest.mark.parametrize("cfg", [11, 12, 13])
+@pytest.mark.parametrize("shape", DIRECT_RAGGED)
+def test_direct_pipeline_ragged(dev, cfg, shape):
+    M, N, K = shape
+    A = wl.random_matrix(1500 + M, M, K, "int4")
+    B = wl.random_matrix(1600 + N, K, N, "int4")
+    assert_exact(gpu_gemm(A, B, dev, cfg), A, B)
+    A = wl.random_matrix(1700 + M, M, K, "normal")
+    B = wl.random_matrix(1800 + N, K, N, "normal")
     assert_tol(gpu_gemm(A, B, dev, cfg), A, B)
 
 

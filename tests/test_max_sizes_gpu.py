@@ -156,7 +156,7 @@ def _equal_to_repeated(out: torch.Tensor, want: np.ndarray, dim: int) -> bool:
     return torch.equal(out, w.repeat(*rep))
 
 
-@pytest.mark.parametrize("cfg", [3, 4, 5])   # the tiles 64 columns wide
+@pytest.mark.parametrize("cfg", [3, 4, 5, 12, 13])   # the tiles 64 columns wide
 def test_gemm_grid_beyond_2_32_work_items(dev, cfg):
     M, K, blk = 3, 2, 1024
     N = 293 << 20                              # 307,232,768 columns

@@ -12,16 +12,18 @@ hipError_t launch_tile(const GemmArgs &a, hipStream_t stream)
     return launch_tile_ops<T>(a, DenseOperands{}, stream);
 }
 
-// The direct-to-LDS pipelines on the shapes they take; the register-staged kernel of
-// the same tile size on the rest.
+// The direct-to-LDS pipelines (mm_gemm_direct.hip). The 256 x 256 one needs 16-byte DMA
+// lanes; on other shapes the register-staged kernel of that tile size runs instead.
 hipError_t direct_or_staged_256(const GemmArgs &a, hipStream_t stream)
 {
-    return direct_f32_ok(a) ? gemm_direct_launch_256(a, stream) : launch_tile<T256x256k32>(a, stream);
+    return direct_f32_wide_ok(a) ? gemm_direct_launch(DirectTile::T256, a, stream)
+                                 : launch_tile<T256x256k32>(a, stream);
 }
 
-hipError_t direct_or_staged_128(const GemmArgs &a, hipStream_t stream)
+template <DirectTile T>
+hipError_t direct(const GemmArgs &a, hipStream_t stream)
 {
-    return direct_f32_ok(a) ? gemm_direct_launch_128(a, stream) : launch_tile<T128x128k32p2>(a, stream);
+    return gemm_direct_launch(T, a, stream);
 }
 
 struct ConfigEntry {
@@ -46,7 +48,9 @@ const ConfigEntry kConfigs[] = {
     {"narrow 16x64 (16x16x4 MFMA), K over 16 waves, 4/NB chunks", &gemm_skinny_launch<16, 4>, 16, 64, 16, 1, 0},
     {"columns <= 4: one wave per row, B rounds in LDS (8 x 4 per workgroup)", &gemm_cols_launch, 8, 4, 4, 1, 0},
     {"256x256x16 w128x64 direct-to-LDS 4 stages (8 waves)", &direct_or_staged_256, 256, 256, 8, 1, 142},
-    {"128x128x16 w64x64 direct-to-LDS 4 stages (4 waves)", &direct_or_staged_128, 128, 128, 4, 2, 135},
+    {"128x128x16 w64x64 direct-to-LDS 4 stages (4 waves)", &direct<DirectTile::T128>, 128, 128, 4, 2, 135},
+    {"64x64x16 w32x32 direct-to-LDS 8 stages (4 waves)", &direct<DirectTile::T64S8>, 64, 64, 4, 2, 114},
+    {"64x64x16 w32x32 direct-to-LDS 4 stages (4 waves)", &direct<DirectTile::T64S4>, 64, 64, 4, 5, 114},
 };
 constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
 
@@ -74,16 +78,16 @@ int gemm_select_config(int64_t M, int64_t N, int64_t K, int64_t batch)
     if (N <= 4) return 9;   // a GEMV with a few vectors (mm_gemm_cols.hip)
     if (N <= 64) return 8;  // a few columns: stream A once (mm_gemm_skinny.hip)
     if (batch * tiles_for(4, M, N) < 128) return 6;  // few 64 x 64 tiles: 16-row tiles fill more CUs
-    // the macro-tile configs; 10 and 11 run 0's and 1's kernels on shapes the direct
-    // pipeline does not take (alignment is not known here)
-    // The direct pipelines fill 3 stages before a tile's first MFMA; below K = 2048 that
-    // costs more than the deeper pipeline saves (measured: K = 512 and 1024 slower by 10%
-    // and 3%, K = 4096 faster by 5%).
-    static const int kTileConfigs[] = {0, 1, 2, 3, 4, 5, 10, 11};
+    // the macro-tile configs (10 runs 0's kernel on shapes its 16-byte DMA does not take;
+    // alignment is not known here). The 256 and 128 direct tiles fill 3 stages of a big
+    // tile before their first MFMA; below K = 2048 that costs more than the deeper
+    // pipeline saves (measured: K = 512 and 1024 slower by 10% and 3%, K = 4096 faster
+    // by 5%).
+    static const int kTileConfigs[] = {0, 1, 2, 3, 4, 5, 10, 11, 12, 13};
     int best = 0;
     double best_t = 0;
     for (int c : kTileConfigs) {
-        if (c >= 10 && K < 2048) continue;
+        if ((c == 10 || c == 11) && K < 2048) continue;
         const ConfigEntry &e = kConfigs[c];
         const double t = tile_time(batch * tiles_for(c, M, N), e.bm, e.bn, e.waves, e.wg_per_cu, e.tflops);
         if (c == 0 || t < best_t) {

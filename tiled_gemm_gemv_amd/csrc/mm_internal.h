@@ -86,11 +86,13 @@ hipError_t gemm_launch(int cfg, const GemmArgs &a, hipStream_t stream);
 template <int W, int L>
 hipError_t gemm_skinny_launch(const GemmArgs &a, hipStream_t stream);
 
-// fp32 GEMM with panels loaded straight into LDS (mm_gemm_direct.hip), 256 x 256 and
-// 128 x 128 tiles; only for shapes direct_f32_ok accepts.
-bool direct_f32_ok(const GemmArgs &a);
-hipError_t gemm_direct_launch_256(const GemmArgs &a, hipStream_t stream);
-hipError_t gemm_direct_launch_128(const GemmArgs &a, hipStream_t stream);
+// fp32 GEMM with panels loaded straight into LDS (mm_gemm_direct.hip): 16-byte DMA
+// lanes for shapes direct_f32_wide_ok accepts, 4-byte lanes (any shape) otherwise.
+// T256 takes only the former (hipErrorInvalidValue otherwise). T64S8 / T64S4: 64 x 64
+// tiles with 8 / 4 LDS stages.
+enum class DirectTile { T256, T128, T64S8, T64S4 };
+bool direct_f32_wide_ok(const GemmArgs &a);
+hipError_t gemm_direct_launch(DirectTile t, const GemmArgs &a, hipStream_t stream);
 
 // GEMM for C with few columns (mm_gemm_cols.hip): one wave per row, B staged in LDS;
 // correct for any shape, meant for N <= 4.
