@@ -453,7 +453,8 @@ def sweep(kind, torch, mm, dev):
         sweep_conv(torch, mm, dev)
     elif kind == "gemm":
         shapes = [(w.M, w.N, w.K, w.name) for w in wl.WORKLOADS.values() if w.op == "gemm"]
-        shapes += [(512, 512, 512, ""), (1536, 1536, 1536, ""), (2048, 2048, 2048, ""),
+        shapes += [(1000, 1532, 784, "ragged M, aligned rows (N, K multiples of 4 and 16)"),
+                   (512, 512, 512, ""), (1536, 1536, 1536, ""), (2048, 2048, 2048, ""),
                    (3072, 3072, 3072, ""), (4096, 4096, 4096, ""), (1024, 4096, 4096, ""),
                    (8192, 1792, 4096, "projection, 1/8 of N")]
         shapes += [(4096, n, 4096, f"FC layer 4096x4096, batch of {n}") for n in (1, 2, 4, 8, 16, 32, 64)]

@@ -49,8 +49,8 @@ const ConfigEntry kConfigs[] = {
     {"columns <= 4: one wave per row, B rounds in LDS (8 x 4 per workgroup)", &gemm_cols_launch, 8, 4, 4, 1, 0},
     {"256x256x16 w128x64 direct-to-LDS 4 stages (8 waves)", &direct_or_staged_256, 256, 256, 8, 1, 142},
     {"128x128x16 w64x64 direct-to-LDS 4 stages (4 waves)", &direct<DirectTile::T128>, 128, 128, 4, 2, 135},
-    {"64x64x16 w32x32 direct-to-LDS 8 stages (4 waves)", &direct<DirectTile::T64S8>, 64, 64, 4, 2, 114},
-    {"64x64x16 w32x32 direct-to-LDS 4 stages (4 waves)", &direct<DirectTile::T64S4>, 64, 64, 4, 5, 114},
+    {"64x64x16 w32x32 direct-to-LDS 8 stages (4 waves)", &direct<DirectTile::T64S8>, 64, 64, 4, 2, 108},
+    {"64x64x16 w32x32 direct-to-LDS 4 stages (4 waves)", &direct<DirectTile::T64S4>, 64, 64, 4, 5, 116},
 };
 constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
 

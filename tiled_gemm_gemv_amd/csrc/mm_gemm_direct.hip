@@ -3,11 +3,11 @@
 // ML-inference tutorial, "Tiled Implementation with Shared Memory"; "CUDA Programming
 // (6)", sections 3.2-3.3) with the staging step done by gfx950's LDS DMA.
 //
-// global_load_lds_dword{,x4} writes each lane's 4 or 16 bytes to LDS at M0 + VEC * lane
-// without passing through registers. The waves then never write LDS themselves (except
-// to clear a partial last K-step), so the end of a K-step is only a wait and a barrier,
-// and no registers hold staged data: the ring runs NS = 4 or 8 stages deep, step
-// kt + NS - 1 loading while step kt is multiplied.
+// global_load_lds_dword{,x4} writes each lane's 4 or 16 bytes to LDS at M0 + 4 * lane or
+// M0 + 16 * lane without passing through registers. The waves then never write LDS
+// themselves (except to clear a partial last K-step), so the end of a K-step is only a
+// wait and a barrier, and no registers hold staged data: the ring runs NS = 4 or 8
+// stages deep, step kt + NS - 1 loading while step kt is multiplied.
 //   * BK = 16. A panel: BM rows of 64 bytes. The 16-byte chunk c of row r sits in slot
 //     c ^ swz_a(r), so that a wave's reads of 32 rows at one k hit distinct banks. Each
 //     lane reads 4 consecutive k of its row with one 16-byte read.
@@ -15,23 +15,25 @@
 //     per lane per step, so a lane reads its column's value of the step's k row with a
 //     4-byte read; rows r and r + 8 (read by the two wave halves at once) are put on
 //     opposite halves of the banks by swz_b.
-//   * The LDS image is the same whatever the DMA width: a lane's bytes land at a fixed
-//     place, so each lane fetches the element the permutations put there. 16-byte lanes
-//     need K % 16 == 0, N % 4 == 0, lda and ldb multiples of 4 and 16-byte aligned A and
-//     B (direct_f32_wide_ok); 4-byte lanes take any shape and alignment (four times the
-//     load instructions).
+//   * Load width. A lane's bytes land at a fixed place, so each lane fetches the
+//     element(s) the permutations put there, and 4- and 16-byte lanes build the same
+//     LDS image. Full K-steps load A with 16-byte lanes whatever its alignment (gfx950
+//     serves 16-byte loads from any 4-byte-aligned address, also into LDS; a full step's
+//     chunks never cross a row end). B takes 16-byte lanes too, except in the last tile
+//     column when N % 4 != 0, whose chunks would cross the row end: 4-byte lanes there.
+//   * Edges: rows past M and columns past N are clamped to in-range data that only feeds
+//     C elements that are not stored. A partial last K-step (K % 16 != 0) loads both
+//     panels with 4-byte lanes at k clamped to K - 1, then the workgroup writes zeros
+//     over the k >= K entries of both panels between two barriers.
 //   * k order: as in the register-staged kernel, lanes 0-31 take k = 4 q + j and lanes
 //     32-63 k = 8 + 4 q + j at step j of group q, so each k of the K-step is added once,
 //     in the same order, and both kernels give the same bits.
 //   * One barrier per K-step, after an explicit s_waitcnt vmcnt that counts the loads of
-//     the steps issued after it. The loads are issued from inline asm (M0 set there): the
-//     compiler cannot tell the stages apart and would otherwise wait for every load in
-//     flight before each LDS read, which removes the pipeline. No other code in these
-//     kernels uses M0.
-//   * Edges: rows past M and columns past N are clamped to in-range data that only feeds
-//     C elements that are not stored. A partial last K-step (K % 16 != 0, 4-byte lanes
-//     only) loads clamped k, then the workgroup writes zeros over the k >= K entries of
-//     both panels between two barriers.
+//     the steps issued after it (a partial last step issues more loads than a full one,
+//     which only makes that count conservative). The loads are issued from inline asm
+//     (M0 set there): the compiler cannot tell the stages apart and would otherwise wait
+//     for every load in flight before each LDS read, which removes the pipeline. No
+//     other code in these kernels uses M0.
 #include "mm_gemm_tile.h"
 
 namespace mm {
@@ -40,24 +42,25 @@ namespace {
 typedef __attribute__((address_space(3))) char lds_char;
 typedef __attribute__((address_space(3))) float lds_float;
 
-template <int BM_, int BN_, int WM_, int WN_, int NS_, int VEC_>
+// GEN: every shape (4-byte lanes where needed); otherwise K % 16 == 0 and N % 4 == 0 only
+// (direct_f32_wide_ok), which keeps the narrow-lane code out of the kernel.
+template <int BM_, int BN_, int WM_, int WN_, int NS_, bool GEN_>
 struct DirectF32 {
-    static constexpr int BM = BM_, BN = BN_, BK = 16, NS = NS_, WM = WM_, WN = WN_, VEC = VEC_;
+    static constexpr int BM = BM_, BN = BN_, BK = 16, NS = NS_, WM = WM_, WN = WN_;
+    static constexpr bool GEN = GEN_;
     static constexpr int WAVES = (BM / WM) * (BN / WN), NT = WAVES * 64;
     static constexpr int FM = WM / 32, FN = WN / 32;
     static constexpr int A_BYTES = BM * BK * 4, B_BYTES = BK * BN * 4;
     static constexpr int STAGE = A_BYTES + B_BYTES;
-    static constexpr int B_ROW = BN * 4;                          // bytes per B row
-    static constexpr int LOAD_BYTES = 64 * VEC;                   // one wave instruction
-    static constexpr int A_LOADS = A_BYTES / LOAD_BYTES / WAVES;  // per wave per K-step
-    static constexpr int B_LOADS = B_BYTES / LOAD_BYTES / WAVES;
-    static constexpr int LOADS = A_LOADS + B_LOADS;
-    static_assert(VEC == 4 || VEC == 16, "4- or 16-byte lanes");
-    static_assert(A_BYTES % (LOAD_BYTES * WAVES) == 0 && B_BYTES % (LOAD_BYTES * WAVES) == 0,
-                  "whole loads");
+    static constexpr int B_ROW = BN * 4;  // bytes per B row
+    // loads per wave per K-step with 16-byte (1 KB per wave) and 4-byte lanes (256 B)
+    static constexpr int A16 = A_BYTES / 1024 / WAVES, B16 = B_BYTES / 1024 / WAVES;
+    static constexpr int A4 = A_BYTES / 256 / WAVES, B4 = B_BYTES / 256 / WAVES;
+    static constexpr int LOADS_WIDE = A16 + B16, LOADS_NARROW_B = A16 + B4;
+    static_assert(A_BYTES % (1024 * WAVES) == 0 && B_BYTES % (1024 * WAVES) == 0, "whole loads");
     static_assert(B_ROW >= 256 && B_ROW <= 1024, "B rows of 64 to 256 floats");
     static_assert(NS * STAGE <= 160 * 1024, "stages must fit the 160 KB LDS");
-    static_assert((NS - 2) * LOADS <= 63, "vmcnt range");
+    static_assert((NS - 2) * LOADS_NARROW_B <= 63, "vmcnt range");
 };
 
 __device__ __forceinline__ int swz_a(int row) { return ((row >> 1) ^ (row >> 3)) & 3; }
@@ -117,51 +120,41 @@ __global__ __launch_bounds__(T::NT) void gemm_f32_direct_kernel(GemmArgs p)
     const int wm0 = (w / (T::BN / T::WN)) * T::WM, wn0 = (w % (T::BN / T::WN)) * T::WN;
     const int nk = (p.K + T::BK - 1) / T::BK;
 
-    // Each load's lane lands at a fixed panel byte; the element stored there is this
-    // lane's source. asrc/bsrc address it at k0 = 0; ak/bk are its k within a K-step.
-    const float *asrc[T::A_LOADS];
-    const float *bsrc[T::B_LOADS];
-    int ak[T::A_LOADS], bk[T::B_LOADS];
+    // Each load's lane lands at a fixed panel byte; the element(s) stored there are this
+    // lane's source. 16-byte lanes of full K-steps: asrc/bsrc address them at k0 = 0.
+    const float *asrc[T::A16];
+    const float *bsrc[T::B16];
 #pragma unroll
-    for (int i = 0; i < T::A_LOADS; ++i) {
-        const int o = (T::A_LOADS * w + i) * T::LOAD_BYTES + T::VEC * lane;  // panel byte
-        const int row = o / 64, slot = (o % 64) / 4;                         // 4-byte slot
-        ak[i] = 4 * ((slot >> 2) ^ swz_a(row)) + (slot & 3);
-        asrc[i] = p.A + (int64_t)min(m0 + row, p.M - 1) * p.lda + ak[i];
+    for (int i = 0; i < T::A16; ++i) {
+        const int o = (T::A16 * w + i) * 1024 + 16 * lane;  // panel byte
+        const int row = o / 64, chunk = (o % 64) / 16;
+        asrc[i] = p.A + (int64_t)min(m0 + row, p.M - 1) * p.lda + 4 * (chunk ^ swz_a(row));
     }
+    // B chunks stay inside their row when N % 4 == 0 (clamped to the last chunk) or when
+    // the whole tile lies left of the last partial chunk
+    const bool wide_b = !T::GEN || (p.N % 4 == 0) || (n0 + T::BN <= p.N - p.N % 4);
 #pragma unroll
-    for (int i = 0; i < T::B_LOADS; ++i) {
-        const int o = (T::B_LOADS * w + i) * T::LOAD_BYTES + T::VEC * lane;
+    for (int i = 0; i < T::B16; ++i) {
+        const int o = (T::B16 * w + i) * 1024 + 16 * lane;
+        const int krow = o / T::B_ROW, chunk = (o % T::B_ROW) / 16;
+        const int col = n0 + 4 * (chunk ^ swz_b(krow));
+        bsrc[i] = p.B + (int64_t)krow * p.ldb + max(min(col, p.N - 4), 0);
+    }
+    // 4-byte lanes: source of load i at K-step k0, k clamped to K - 1 (partial step)
+    auto a4_src = [&](int i, int k0) {
+        const int o = (T::A4 * w + i) * 256 + 4 * lane;
+        const int row = o / 64, slot = (o % 64) / 4;
+        const int k = min(k0 + 4 * ((slot >> 2) ^ swz_a(row)) + (slot & 3), p.K - 1);
+        return p.A + (int64_t)min(m0 + row, p.M - 1) * p.lda + k;
+    };
+    auto b4_src = [&](int i, int k0) {
+        const int o = (T::B4 * w + i) * 256 + 4 * lane;
         const int krow = o / T::B_ROW, slot = (o % T::B_ROW) / 4;
         const int col = n0 + 4 * ((slot >> 2) ^ swz_b(krow)) + (slot & 3);
-        bk[i] = krow;
-        bsrc[i] = p.B + (int64_t)krow * p.ldb + min(col, T::VEC == 16 ? p.N - 4 : p.N - 1);
-    }
-    const unsigned lds0 = (unsigned)(uintptr_t)(lds_char *)lds;  // LDS byte offset of the array
-    auto issue = [&](int kt) {
-        const unsigned st = lds0 + (kt % T::NS) * T::STAGE;
-        const int k0 = kt * T::BK;
-        // 16-byte lanes come with K % 16 == 0: no partial step
-        if (T::VEC == 16 || k0 + T::BK <= p.K) {
-#pragma unroll
-            for (int i = 0; i < T::A_LOADS; ++i)
-                load_to_lds<T::VEC>(st + (T::A_LOADS * w + i) * T::LOAD_BYTES, asrc[i] + k0);
-#pragma unroll
-            for (int i = 0; i < T::B_LOADS; ++i)
-                load_to_lds<T::VEC>(st + T::A_BYTES + (T::B_LOADS * w + i) * T::LOAD_BYTES,
-                                    bsrc[i] + (int64_t)k0 * p.ldb);
-        } else if constexpr (T::VEC == 4) {
-            // partial last step: k clamped to K - 1 (cleared after it lands)
-#pragma unroll
-            for (int i = 0; i < T::A_LOADS; ++i)
-                load_to_lds<T::VEC>(st + (T::A_LOADS * w + i) * T::LOAD_BYTES,
-                                    asrc[i] + (min(k0 + ak[i], p.K - 1) - ak[i]));
-#pragma unroll
-            for (int i = 0; i < T::B_LOADS; ++i)
-                load_to_lds<T::VEC>(st + T::A_BYTES + (T::B_LOADS * w + i) * T::LOAD_BYTES,
-                                    bsrc[i] + (int64_t)(min(k0 + bk[i], p.K - 1) - bk[i]) * p.ldb);
-        }
+        return p.B + (int64_t)min(k0 + krow, p.K - 1) * p.ldb + min(col, p.N - 1);
     };
+    const unsigned lds0 = (unsigned)(uintptr_t)(lds_char *)lds;  // LDS byte offset of the array
+    const int nk_full = p.K / T::BK;  // full K-steps; a partial one follows if K % 16 != 0
 
     // operand addresses inside a stage (bytes): A per group q and block i; B per group q,
     // step j and block jj (k = 8 (lane / 32) + 4 q + j, column wn0 + 32 jj + lane % 32)
@@ -192,27 +185,8 @@ __global__ __launch_bounds__(T::NT) void gemm_f32_direct_kernel(GemmArgs p)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][jj][r] = 0.f;
 
-    for (int s = 0; s < T::NS - 1 && s < nk; ++s) issue(s);
-    for (int kt = 0; kt < nk; ++kt) {
-        // step kt's loads are done when at most the later steps' loads are outstanding
-        wait_steps<T::LOADS, T::NS - 2>(nk - 1 - kt);
-        // every wave's loads for stage kt are in LDS, and every wave is done with the
-        // stage the next issue overwrites (read in step kt - 1)
-        __syncthreads();
-        if (kt + T::NS - 1 < nk) issue(kt + T::NS - 1);
-        lds_char *st = (lds_char *)lds + (kt % T::NS) * T::STAGE;
-        if (T::VEC == 4 && kt * T::BK + T::BK > p.K) {
-            // partial last step: zeros over k >= K in both panels (no load is in flight
-            // into this stage and no wave reads it before the barrier below)
-            const int kr = p.K - kt * T::BK, nz = T::BK - kr;
-            for (int e = threadIdx.x; e < T::BM * nz; e += T::NT) {
-                const int r = e / nz, k = kr + e % nz;
-                *(lds_float *)(st + r * 64 + 16 * ((k >> 2) ^ swz_a(r)) + 4 * (k & 3)) = 0.f;
-            }
-            for (int e = threadIdx.x; e < nz * T::BN; e += T::NT)
-                *(lds_float *)(st + T::A_BYTES + (kr + e / T::BN) * T::B_ROW + 4 * (e % T::BN)) = 0.f;
-            __syncthreads();
-        }
+    auto multiply = [&](int kt) {
+        const lds_char *st = (const lds_char *)lds + (kt % T::NS) * T::STAGE;
 #pragma unroll
         for (int q = 0; q < 2; ++q) {
             f32x4 a[T::FM];
@@ -233,7 +207,76 @@ __global__ __launch_bounds__(T::NT) void gemm_f32_direct_kernel(GemmArgs p)
                         acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[i][j], b[j][jj], acc[i][jj],
                                                                          0, 0, 0);
         }
-    }
+    };
+
+    // The K loop, compiled once per kind of tile (16- or 4-byte B lanes), so that a K-step
+    // tests nothing but whether it has a step to issue.
+    auto k_loop = [&](auto wide_tag) {
+        constexpr bool WIDE = decltype(wide_tag)::value;
+        constexpr int L = WIDE ? T::LOADS_WIDE : T::LOADS_NARROW_B;
+        auto issue_full = [&](int kt) {
+            const unsigned st = lds0 + (kt % T::NS) * T::STAGE;
+            const int k0 = kt * T::BK;
+#pragma unroll
+            for (int i = 0; i < T::A16; ++i) load_to_lds<16>(st + (T::A16 * w + i) * 1024, asrc[i] + k0);
+            if constexpr (WIDE) {
+#pragma unroll
+                for (int i = 0; i < T::B16; ++i)
+                    load_to_lds<16>(st + T::A_BYTES + (T::B16 * w + i) * 1024, bsrc[i] + (int64_t)k0 * p.ldb);
+            } else {
+#pragma unroll
+                for (int i = 0; i < T::B4; ++i)
+                    load_to_lds<4>(st + T::A_BYTES + (T::B4 * w + i) * 256, b4_src(i, k0));
+            }
+        };
+        // the partial last step: 4-byte lanes, k clamped (cleared after it lands)
+        auto issue_partial = [&](int kt) {
+            if constexpr (T::GEN) {
+                const unsigned st = lds0 + (kt % T::NS) * T::STAGE;
+                const int k0 = kt * T::BK;
+#pragma unroll
+                for (int i = 0; i < T::A4; ++i) load_to_lds<4>(st + (T::A4 * w + i) * 256, a4_src(i, k0));
+#pragma unroll
+                for (int i = 0; i < T::B4; ++i)
+                    load_to_lds<4>(st + T::A_BYTES + (T::B4 * w + i) * 256, b4_src(i, k0));
+            }
+        };
+        auto issue = [&](int kt) {
+            if (kt < nk_full) issue_full(kt);
+            else if (T::GEN && kt < nk) issue_partial(kt);
+        };
+        for (int s = 0; s < T::NS - 1; ++s) issue(s);
+        for (int kt = 0; kt < nk_full; ++kt) {
+            // step kt's loads are done when at most the later steps' loads are outstanding
+            // (a partial step among them issues more than L: the count is then conservative)
+            wait_steps<L, T::NS - 2>(nk - 1 - kt);
+            // every wave's loads for stage kt are in LDS, and every wave is done with the
+            // stage the next issue overwrites (read in step kt - 1)
+            __syncthreads();
+            const int next = kt + T::NS - 1;
+            if (next < nk_full) issue_full(next);
+            else if (T::GEN && next < nk) issue_partial(next);
+            multiply(kt);
+        }
+        if (T::GEN && nk_full < nk) {
+            wait_vmcnt<0>();
+            __syncthreads();
+            // zeros over k >= K in both panels (no load is in flight into this stage and
+            // no wave reads it before the barrier below)
+            lds_char *st = (lds_char *)lds + (nk_full % T::NS) * T::STAGE;
+            const int kr = p.K - nk_full * T::BK, nz = T::BK - kr;
+            for (int e = threadIdx.x; e < T::BM * nz; e += T::NT) {
+                const int r = e / nz, k = kr + e % nz;
+                *(lds_float *)(st + r * 64 + 16 * ((k >> 2) ^ swz_a(r)) + 4 * (k & 3)) = 0.f;
+            }
+            for (int e = threadIdx.x; e < nz * T::BN; e += T::NT)
+                *(lds_float *)(st + T::A_BYTES + (kr + e / T::BN) * T::B_ROW + 4 * (e % T::BN)) = 0.f;
+            __syncthreads();
+            multiply(nk_full);
+        }
+    };
+    if (!T::GEN || wide_b) k_loop(std::true_type{});
+    else k_loop(std::false_type{});
 
     // accumulator layout of v_mfma_f32_32x32x2_f32: lane l, register r holds row
     // 8 (r / 4) + 4 (l / 32) + r % 4, column l % 32 of the 32 x 32 block
@@ -263,34 +306,39 @@ hipError_t launch_direct(const GemmArgs &a, hipStream_t stream)
                            dim3(gx, gy, (unsigned)a.batch), dim3(T::NT), args, 0, stream);
 }
 
-template <int BM, int BN, int WM, int WN, int NS>
-hipError_t launch_either(const GemmArgs &a, hipStream_t stream)
-{
-    return direct_f32_wide_ok(a) ? launch_direct<DirectF32<BM, BN, WM, WN, NS, 16>>(a, stream)
-                                 : launch_direct<DirectF32<BM, BN, WM, WN, NS, 4>>(a, stream);
-}
-
 }  // namespace
 
 bool direct_f32_wide_ok(const GemmArgs &a)
 {
-    const bool aligned = (uintptr_t)a.A % 16 == 0 && (uintptr_t)a.B % 16 == 0 &&
-                         (a.batch == 1 || (a.sa % 4 == 0 && a.sb % 4 == 0));
-    return a.K % 16 == 0 && a.N >= 4 && a.N % 4 == 0 && a.lda % 4 == 0 && a.ldb % 4 == 0 && aligned;
+    return a.K % 16 == 0 && a.N >= 4 && a.N % 4 == 0;
 }
+
+namespace {
+
+// The kernel without the partial-step and narrow-lane code where the shape allows it: its
+// K loop is leaner (measured up to 20% faster on the 64 x 64 tile, whose waves issue only
+// 8 MFMAs per K-step).
+template <int BM, int BN, int WM, int WN, int NS>
+hipError_t launch_lean_or_general(const GemmArgs &a, hipStream_t stream)
+{
+    return direct_f32_wide_ok(a) ? launch_direct<DirectF32<BM, BN, WM, WN, NS, false>>(a, stream)
+                                 : launch_direct<DirectF32<BM, BN, WM, WN, NS, true>>(a, stream);
+}
+
+}  // namespace
 
 hipError_t gemm_direct_launch(DirectTile t, const GemmArgs &a, hipStream_t stream)
 {
     switch (t) {
-    case DirectTile::T256:  // 16-byte lanes only
+    case DirectTile::T256:
         if (!direct_f32_wide_ok(a)) return hipErrorInvalidValue;
-        return launch_direct<DirectF32<256, 256, 128, 64, 4, 16>>(a, stream);
+        return launch_direct<DirectF32<256, 256, 128, 64, 4, false>>(a, stream);
     case DirectTile::T128:
-        return launch_either<128, 128, 64, 64, 4>(a, stream);
+        return launch_lean_or_general<128, 128, 64, 64, 4>(a, stream);
     case DirectTile::T64S8:
-        return launch_either<64, 64, 32, 32, 8>(a, stream);
+        return launch_lean_or_general<64, 64, 32, 32, 8>(a, stream);
     case DirectTile::T64S4:
-        return launch_either<64, 64, 32, 32, 4>(a, stream);
+        return launch_lean_or_general<64, 64, 32, 32, 4>(a, stream);
     }
     return hipErrorInvalidValue;
 }

@@ -86,10 +86,9 @@ hipError_t gemm_launch(int cfg, const GemmArgs &a, hipStream_t stream);
 template <int W, int L>
 hipError_t gemm_skinny_launch(const GemmArgs &a, hipStream_t stream);
 
-// fp32 GEMM with panels loaded straight into LDS (mm_gemm_direct.hip): 16-byte DMA
-// lanes for shapes direct_f32_wide_ok accepts, 4-byte lanes (any shape) otherwise.
-// T256 takes only the former (hipErrorInvalidValue otherwise). T64S8 / T64S4: 64 x 64
-// tiles with 8 / 4 LDS stages.
+// fp32 GEMM with panels loaded straight into LDS (mm_gemm_direct.hip); any shape and
+// alignment, except T256, which takes only shapes direct_f32_wide_ok accepts
+// (hipErrorInvalidValue otherwise). T64S8 / T64S4: 64 x 64 tiles with 8 / 4 LDS stages.
 enum class DirectTile { T256, T128, T64S8, T64S4 };
 bool direct_f32_wide_ok(const GemmArgs &a);
 hipError_t gemm_direct_launch(DirectTile t, const GemmArgs &a, hipStream_t stream);
