@@ -25,12 +25,16 @@
 // A 1 x 1 filter with unit stride and no padding needs no gather: each image of x is
 // then a C x HW matrix and the convolution is the strided batched GEMM of the same
 // kernel with a plain B.
-#include "mm_gemm_tile.h"
+#include "mm_direct.h"
 
 namespace mm {
 namespace {
 
 constexpr int kFar = -(1 << 30);  // an input row that is outside any image
+
+// Read by the LDS DMA for every element of the product that is zero: a tap in the
+// padding, a row past K (partial K-step) or a column past N.
+__device__ float kZeros[64];
 
 // B = the im2col matrix of a run of images of x (p.B points at the first), C = those
 // images of y; p.N = images * P * Q, p.K = C * R * S, p.ldc = P * Q.
@@ -49,6 +53,7 @@ struct Im2colOperands {
     static constexpr bool kMatrixB = false;
     int H, W, R, S, sh, sw, ph, pw, dh, dw;
     int Q, PQ, HW, RS, CHW;
+    int s16, r16, c16;  // 16 rows of the im2col matrix: s += s16, r += r16, c += c16 (with carries)
     int64_t KPQ;
 
     // Output column (n, p, q): input row h0 and column w0 under the filter's first
@@ -62,7 +67,12 @@ struct Im2colOperands {
     __device__ __forceinline__ Cols columns(const GemmArgs &p, int n0, int idx) const
     {
         static_assert(T::BN % 64 == 0 && T::BK % 16 == 0, "a wave's lanes must share their rows");
-        const int j = n0 + idx % T::BN;
+        return columns_of(p, n0 + idx % T::BN);
+    }
+
+    // The state of output column j (any j; h0 = kFar past the end).
+    __device__ __forceinline__ Cols columns_of(const GemmArgs &p, int j) const
+    {
         Cols c;
         if (j < p.N) {
             const int n = (unsigned)j / (unsigned)PQ, pq = j - n * PQ;
@@ -133,6 +143,156 @@ struct Im2colOperands {
     }
 };
 
+// The implicit GEMM on the direct-to-LDS tiles of mm_direct.h: filters (A) by 16-byte DMA
+// lanes, the im2col matrix (B) gathered by 4-byte DMA lanes straight into the B panel.
+// A lane of a B load lands at a fixed column of one k row of the panel, so it keeps that
+// column's state (h0, w0, image offset) for the whole K loop; the row's (c, r, s) and
+// offset are the same in every lane (scalar registers), found by one division per
+// K-step and stepped across the wave's 4 consecutive rows. An element that is zero
+// (padding, k >= K, column >= N) is read from kZeros, so a partial last K-step needs
+// no clearing. A's partial step takes 4-byte lanes with the same rule.
+template <class T>
+__global__ __launch_bounds__(T::NT) void conv_direct_kernel(GemmArgs p, Im2colOperands o)
+{
+    static_assert(T::B_ROW <= 1024 && (T::B4 * 256) % T::B_ROW == 0, "a wave's B loads cover whole rows");
+    constexpr int ROWS = T::B4 * 256 / T::B_ROW;      // k rows of a K-step one wave loads
+    constexpr int PER_ROW = T::B_ROW / 256;           // loads per row
+    static_assert(ROWS * T::WAVES == T::BK, "the waves split the k rows");
+    __shared__ __attribute__((aligned(1024))) char lds[T::NS * T::STAGE];
+    const int tiles_m = (p.M + T::BM - 1) / T::BM;
+    const int tiles_n = (p.N + T::BN - 1) / T::BN;
+    const int64_t tiles = (int64_t)tiles_m * tiles_n;
+    const int64_t bid = linear_block();
+    if (bid >= tiles) return;  // padding of a 2-D grid (whole workgroup, before any barrier)
+    int tm, tn;
+    tile_of_block((int)bid, (int)tiles, tiles_m, tiles_n, 8, tm, tn);
+    const int m0 = tm * T::BM, n0 = tn * T::BN;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int wm0 = (w / (T::BN / T::WN)) * T::WM, wn0 = (w % (T::BN / T::WN)) * T::WN;
+    const int nk = (p.K + T::BK - 1) / T::BK;
+    const float *zeros = kZeros + lane;
+    const char *x = reinterpret_cast<const char *>(p.B);
+
+    // A: 16-byte lanes on full K-steps (sources at k0 = 0)
+    const float *asrc[T::A16];
+#pragma unroll
+    for (int i = 0; i < T::A16; ++i) {
+        const int ob = (T::A16 * w + i) * 1024 + 16 * lane;
+        const int row = ob / 64, chunk = (ob % 64) / 16;
+        asrc[i] = p.A + (int64_t)min(m0 + row, p.M - 1) * p.lda + 4 * (chunk ^ swz_a(row));
+    }
+    // B: the wave loads rows ROWS * w .. ROWS * w + ROWS - 1 of each K-step, PER_ROW loads
+    // per row; this lane's column in load h of a row, and that column's state
+    const int krow0 = ROWS * w;
+    Im2colOperands::Cols cols[PER_ROW];
+#pragma unroll
+    for (int h = 0; h < PER_ROW; ++h) {
+        const int slot = 64 * h + lane;  // 4-byte slot in the row
+        const int col = n0 + 4 * ((slot >> 2) ^ swz_b(krow0)) + (slot & 3);
+        cols[h] = o.columns_of(p, col);
+    }
+    static_assert(8 % ROWS == 0, "a wave's rows lie in one 8-row half: they share swz_b");
+
+    const unsigned lds0 = (unsigned)(uintptr_t)(lds_char *)lds;
+    // (c, r, s) of row krow0 of the next K-step to issue (one division, here)
+    int fc = krow0 / o.RS, fr = (krow0 - fc * o.RS) / o.S;
+    int fs = krow0 - fc * o.RS - fr * o.S;
+    auto issue = [&](int kt) {
+        const unsigned st = lds0 + (kt % T::NS) * T::STAGE;
+        const int k0 = kt * T::BK;
+        if (k0 + T::BK <= p.K) {
+#pragma unroll
+            for (int i = 0; i < T::A16; ++i) load_to_lds<16>(st + (T::A16 * w + i) * 1024, asrc[i] + k0);
+        } else {
+#pragma unroll
+            for (int i = 0; i < T::A4; ++i) {
+                const int ob = (T::A4 * w + i) * 256 + 4 * lane;
+                const int row = ob / 64, slot = (ob % 64) / 4;
+                const int k = k0 + 4 * ((slot >> 2) ^ swz_a(row)) + (slot & 3);
+                const float *src = k < p.K ? p.A + (int64_t)min(m0 + row, p.M - 1) * p.lda + k : zeros;
+                load_to_lds<4>(st + (T::A4 * w + i) * 256, src);
+            }
+        }
+        // (c, r, s) of the wave's first row: carried over from the previous issue (the
+        // steps are issued in order), then stepped across the wave's rows
+        int k = k0 + krow0;
+        int r = fr, s = fs;
+        int dy = r * o.dh, dx = s * o.dw;
+        int rowoff = fc * o.HW + dy * o.W + dx;
+        // advance the first row by one K-step (16 rows) for the next issue
+        fs += o.s16;
+        const int cs = fs >= o.S;
+        fs -= cs ? o.S : 0;
+        fr += o.r16 + cs;
+        const int cr = fr >= o.R;
+        fr -= cr ? o.R : 0;
+        fc += o.c16 + cr;
+#pragma unroll
+        for (int rr = 0; rr < ROWS; ++rr) {
+#pragma unroll
+            for (int h = 0; h < PER_ROW; ++h) {
+                const int hh = cols[h].h0 + dy, ww = cols[h].w0 + dx;
+                const bool ok = k < p.K && (unsigned)hh < (unsigned)o.H && (unsigned)ww < (unsigned)o.W;
+                const float *src = ok ? reinterpret_cast<const float *>(x + (unsigned)(cols[h].base + rowoff) * 4u)
+                                      : zeros;
+                load_to_lds<4>(st + T::A_BYTES + (krow0 + rr) * T::B_ROW + 256 * h, src);
+            }
+            ++k;
+            dx += o.dw;
+            rowoff += o.dw;
+            if (++s == o.S) {
+                s = 0;
+                dx = 0;
+                dy += o.dh;
+                rowoff += o.dh * o.W - o.S * o.dw;
+                if (++r == o.R) {
+                    r = 0;
+                    dy = 0;
+                    rowoff += o.HW - o.R * o.dh * o.W;
+                }
+            }
+        }
+    };
+
+    int a_off[2][T::FM], b_off[2][4][T::FN];
+    direct_operand_offsets<T>(lane, wm0, wn0, a_off, b_off);
+    f32x16 acc[T::FM][T::FN];
+#pragma unroll
+    for (int i = 0; i < T::FM; ++i)
+#pragma unroll
+        for (int jj = 0; jj < T::FN; ++jj)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][jj][r] = 0.f;
+
+    // loads per wave per K-step (a partial step issues more: the count is then conservative)
+    constexpr int L = T::A16 + T::B4;
+    static_assert((T::NS - 2) * L <= 63, "vmcnt range");
+    for (int st = 0; st < T::NS - 1 && st < nk; ++st) issue(st);
+    for (int kt = 0; kt < nk; ++kt) {
+        wait_steps<L, T::NS - 2>(nk - 1 - kt);
+        __syncthreads();
+        // the MFMAs first: the gather's address work for the step NS - 1 ahead then runs
+        // while they execute
+        direct_multiply<T>((const lds_char *)lds + (kt % T::NS) * T::STAGE, a_off, b_off, acc);
+        if (kt + T::NS - 1 < nk) issue(kt + T::NS - 1);
+    }
+    direct_store<T>(p, m0, n0, wm0, wn0, lane, acc, [&](int gn) { return o.c_column(p, gn); });
+}
+
+template <class T>
+hipError_t launch_conv_direct(const GemmArgs &a, const Im2colOperands &o, hipStream_t stream)
+{
+    const int64_t tiles = (int64_t)((a.M + T::BM - 1) / T::BM) * ((a.N + T::BN - 1) / T::BN);
+    if (tiles > 0x7fffffff) return hipErrorInvalidConfiguration;
+    unsigned gx, gy;
+    if (!grid_for(tiles, gx, gy)) return hipErrorInvalidConfiguration;
+    GemmArgs ga = a;
+    Im2colOperands oa = o;
+    void *args[] = {&ga, &oa};
+    return hipLaunchKernel(reinterpret_cast<const void *>(&conv_direct_kernel<T>), dim3(gx, gy), dim3(T::NT),
+                           args, 0, stream);
+}
+
 struct ConvConfig {
     const char *name;
     hipError_t (*launch)(const GemmArgs &, const Im2colOperands &, hipStream_t);
@@ -140,7 +300,8 @@ struct ConvConfig {
     int bm, bn;
     int waves;          // per workgroup
     int wg_per_cu;      // workgroups one CU holds (registers and LDS)
-    double tflops;      // rate of the tile on large dense shapes, for the choice below
+    double tflops;      // rate of the tile on the gather, for the choice below
+    int bk;             // K-step depth
 };
 
 template <class T>
@@ -150,13 +311,19 @@ hipError_t launch_im2col(const GemmArgs &a, const Im2colOperands &o, hipStream_t
 }
 
 // Tile shapes of the fp32 GEMM. The 256 x 256 tile is left out: with the gather's
-// per-column state it no longer fits its 256 registers per lane.
+// per-column state it no longer fits its 256 registers per lane. Rates: fitted to a timed
+// sweep of image-network layers (3 x 3 at strides 1 and 2, dilated 3 x 3, 7 x 7 input
+// layer), gather included.
 const ConvConfig kConvConfigs[] = {
-    {"128x128x32 w64x64 pf2 ks1 (4 waves)", &launch_im2col<T128x128k32p2>, 1, 128, 128, 4, 2, 122},
-    {"128x128x32 w64x64 pf1 ks2 (8 waves)", &launch_im2col<T128x128k32s2>, 2, 128, 128, 8, 1, 122},
-    {"64x64x64 w32x32 pf2 ks1 (4 waves)", &launch_im2col<T64x64k64p2>, 3, 64, 64, 4, 2, 113},
-    {"64x64x64 w32x32 pf2 ks2 (8 waves)", &launch_im2col<T64x64k64p2s2>, 4, 64, 64, 8, 2, 94},
-    {"128x64x64 w64x32 pf1 ks2 (8 waves)", &launch_im2col<T128x64k64s2>, 5, 128, 64, 8, 1, 111},
+    {"128x128x32 w64x64 pf2 ks1 (4 waves)", &launch_im2col<T128x128k32p2>, 1, 128, 128, 4, 2, 100, 32},
+    {"128x128x32 w64x64 pf1 ks2 (8 waves)", &launch_im2col<T128x128k32s2>, 2, 128, 128, 8, 1, 100, 32},
+    {"64x64x64 w32x32 pf2 ks1 (4 waves)", &launch_im2col<T64x64k64p2>, 3, 64, 64, 4, 2, 90, 64},
+    {"64x64x64 w32x32 pf2 ks2 (8 waves)", &launch_im2col<T64x64k64p2s2>, 4, 64, 64, 8, 2, 86, 64},
+    {"128x64x64 w64x32 pf1 ks2 (8 waves)", &launch_im2col<T128x64k64s2>, 5, 128, 64, 8, 1, 80, 64},
+    {"64x64x16 w32x32 direct-to-LDS gather 4 stages (4 waves)", &launch_conv_direct<DirectF32<64, 64, 32, 32, 4, false>>,
+     13, 64, 64, 4, 5, 85, 16},
+    {"128x128x16 w64x64 direct-to-LDS gather 4 stages (4 waves)",
+     &launch_conv_direct<DirectF32<128, 128, 64, 64, 4, false>>, 11, 128, 128, 4, 2, 115, 16},
 };
 constexpr int kNumConvConfigs = sizeof(kConvConfigs) / sizeof(kConvConfigs[0]);
 constexpr int64_t kMaxI32 = 0x7fffffff;
@@ -171,18 +338,34 @@ const char *conv_config_name(int cfg)
     return (cfg >= 0 && cfg < kNumConvConfigs) ? kConvConfigs[cfg].name : nullptr;
 }
 
-// The product is M = K filters by N columns (batch such products side by side).
-// Filter counts are often 64-256, so a tall tile can be mostly padding; the choice is
-// the least modelled time (tile_time: padded tile area, rounds over the 256 CUs,
-// waves per CU, the tile's own rate).
-int conv_select_config(int64_t M, int64_t N, int64_t batch)
+// The product is M = K filters by N columns by CRS. Filter counts are often 64-256, so a
+// tall tile can be mostly padding, and CRS is often small, so a deep K-step can be mostly
+// padding too; the choice is the least modelled time (tile_time: padded tile area, the
+// busiest CU's tiles and its occupancy, the tile's rate on the gather; k_steps_factor).
+int conv_select_config(int64_t M, int64_t N, int64_t K)
 {
     int best = 0;
     double best_t = 0;
     for (int c = 0; c < kNumConvConfigs; ++c) {
         const ConvConfig &k = kConvConfigs[c];
-        const int64_t tiles = ((M + k.bm - 1) / k.bm) * ((N + k.bn - 1) / k.bn) * batch;
-        const double t = tile_time(tiles, k.bm, k.bn, k.waves, k.wg_per_cu, k.tflops);
+        const int64_t tiles = ((M + k.bm - 1) / k.bm) * ((N + k.bn - 1) / k.bn);
+        const double t = tile_time(tiles, k.bm, k.bn, k.waves, k.wg_per_cu, k.tflops) * k_steps_factor(K, k.bk);
+        if (c == 0 || t < best_t) {
+            best = c;
+            best_t = t;
+        }
+    }
+    return best;
+}
+
+// 1 x 1 layers on large maps run the batched GEMM: the config whose GEMM tile the GEMM's
+// own model times fastest.
+int conv_select_batched_gemm(int64_t M, int64_t N, int64_t K, int64_t batch)
+{
+    int best = 0;
+    double best_t = 0;
+    for (int c = 0; c < kNumConvConfigs; ++c) {
+        const double t = gemm_config_time(kConvConfigs[c].gemm_cfg, M, N, K, batch);
         if (c == 0 || t < best_t) {
             best = c;
             best_t = t;
@@ -202,8 +385,8 @@ bool conv_is_batched_gemm(const ConvArgs &a)
 
 int conv_choose_config(const ConvArgs &a)
 {
-    if (conv_is_batched_gemm(a)) return conv_select_config(a.K, a.H * a.W, a.N < 65535 ? a.N : 65535);
-    return conv_select_config(a.K, a.N * a.P * a.Q, 1);
+    if (conv_is_batched_gemm(a)) return conv_select_batched_gemm(a.K, a.H * a.W, a.C, a.N < 65535 ? a.N : 65535);
+    return conv_select_config(a.K, a.N * a.P * a.Q, a.C * a.R * a.S);
 }
 
 // Shapes are validated by the caller: every size >= 1 (C may be 0: then y is zeroed),
@@ -253,6 +436,9 @@ hipError_t conv_launch(int cfg, const ConvArgs &a, hipStream_t stream)
     o.HW = (int)HW;
     o.RS = (int)(a.R * a.S);
     o.CHW = (int)CHW;
+    o.s16 = (int)(16 % a.S);
+    o.r16 = (int)((16 / a.S) % a.R);
+    o.c16 = (int)(16 / (a.R * a.S));
     o.KPQ = KPQ;
     // images per launch: x offsets below 2^30, product columns below 2^31
     int64_t per = kMaxRun / CHW;

@@ -1,0 +1,155 @@
+// mm_direct.h -- building blocks of the fp32 tiles whose panels the LDS DMA moves from
+// HBM straight into LDS (the GEMM of mm_gemm_direct.hip and the convolution of
+// mm_conv_direct.hip): tile parameters, the LDS layout's permutations, the DMA and wait
+// primitives, and the MFMA step on one stage.
+//
+// LDS layout of a stage (BK = 16):
+//   * A panel: BM rows of 64 bytes. The 16-byte chunk c of row r sits in slot
+//     c ^ swz_a(r), so that a wave's reads of 32 rows at one k hit distinct banks; each
+//     lane reads 4 consecutive k of its row with one 16-byte read.
+//   * B panel: 16 rows of BN floats, row-major. v_mfma_f32_32x32x2_f32 takes one B value
+//     per lane per step, so a lane reads its column's value of the step's k row with a
+//     4-byte read; rows r and r + 8 (read by the two wave halves at once) are put on
+//     opposite halves of the banks by swz_b (chunk index ^ 8).
+//   * k order: lanes 0-31 take k = 4 q + j and lanes 32-63 k = 8 + 4 q + j at step j of
+//     group q, so each k of the K-step is added once, in the register-staged kernel's
+//     order (the same bits).
+#pragma once
+#include "mm_gemm_tile.h"
+
+namespace mm {
+namespace {
+
+typedef __attribute__((address_space(3))) char lds_char;
+typedef __attribute__((address_space(3))) float lds_float;
+
+// GEN: every shape (4-byte lanes where needed); otherwise K % 16 == 0 and N % 4 == 0 only
+// (direct_f32_wide_ok), which keeps the narrow-lane code out of the kernel.
+template <int BM_, int BN_, int WM_, int WN_, int NS_, bool GEN_>
+struct DirectF32 {
+    static constexpr int BM = BM_, BN = BN_, BK = 16, NS = NS_, WM = WM_, WN = WN_;
+    static constexpr bool GEN = GEN_;
+    static constexpr int WAVES = (BM / WM) * (BN / WN), NT = WAVES * 64;
+    static constexpr int FM = WM / 32, FN = WN / 32;
+    static constexpr int A_BYTES = BM * BK * 4, B_BYTES = BK * BN * 4;
+    static constexpr int STAGE = A_BYTES + B_BYTES;
+    static constexpr int B_ROW = BN * 4;  // bytes per B row
+    // loads per wave per K-step with 16-byte (1 KB per wave) and 4-byte lanes (256 B)
+    static constexpr int A16 = A_BYTES / 1024 / WAVES, B16 = B_BYTES / 1024 / WAVES;
+    static constexpr int A4 = A_BYTES / 256 / WAVES, B4 = B_BYTES / 256 / WAVES;
+    static constexpr int LOADS_WIDE = A16 + B16, LOADS_NARROW_B = A16 + B4;
+    static_assert(A_BYTES % (1024 * WAVES) == 0 && B_BYTES % (1024 * WAVES) == 0, "whole loads");
+    static_assert(B_ROW >= 256 && B_ROW <= 1024, "B rows of 64 to 256 floats");
+    static_assert(NS * STAGE <= 160 * 1024, "stages must fit the 160 KB LDS");
+    static_assert((NS - 2) * LOADS_NARROW_B <= 63, "vmcnt range");
+};
+
+__device__ __forceinline__ int swz_a(int row) { return ((row >> 1) ^ (row >> 3)) & 3; }
+__device__ __forceinline__ int swz_b(int krow) { return ((krow >> 3) & 1) * 8; }
+
+// VEC bytes per lane from src into LDS at lds_addr + VEC * lane (lds_addr wave-uniform).
+template <int VEC>
+__device__ __forceinline__ void load_to_lds(unsigned lds_addr, const float *src)
+{
+    if constexpr (VEC == 16)
+        asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
+                     :: "s"(__builtin_amdgcn_readfirstlane(lds_addr)), "v"(src) : "memory");
+    else
+        asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off"
+                     :: "s"(__builtin_amdgcn_readfirstlane(lds_addr)), "v"(src) : "memory");
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt()
+{
+    asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
+}
+
+// Wait until at most min(steps, S) K-steps of L loads each are outstanding.
+template <int L, int S>
+__device__ __forceinline__ void wait_steps(int steps)
+{
+    if constexpr (S > 0) {
+        if (steps >= S) {
+            wait_vmcnt<S * L>();
+            return;
+        }
+        wait_steps<L, S - 1>(steps);
+    } else {
+        wait_vmcnt<0>();
+    }
+}
+
+// This lane's operand addresses inside a stage (bytes): A per group q and block i; B per
+// group q, step j and block jj (k = 8 (lane / 32) + 4 q + j, column wn0 + 32 jj + lane % 32).
+template <class T>
+__device__ __forceinline__ void direct_operand_offsets(int lane, int wm0, int wn0, int (&a_off)[2][T::FM],
+                                                       int (&b_off)[2][4][T::FN])
+{
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+#pragma unroll
+        for (int i = 0; i < T::FM; ++i) {
+            const int row = wm0 + 32 * i + (lane & 31);
+            a_off[q][i] = row * 64 + 16 * ((q + 2 * (lane >> 5)) ^ swz_a(row));
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int jj = 0; jj < T::FN; ++jj) {
+                const int krow = 8 * (lane >> 5) + 4 * q + j;
+                const int col = wn0 + 32 * jj + (lane & 31);
+                b_off[q][j][jj] = T::A_BYTES + krow * T::B_ROW + 16 * ((col >> 2) ^ swz_b(krow)) +
+                                  4 * (col & 3);
+            }
+    }
+}
+
+// The MFMAs of one K-step on stage st: two groups of 4 k per lane half.
+template <class T>
+__device__ __forceinline__ void direct_multiply(const lds_char *st, const int (&a_off)[2][T::FM],
+                                                const int (&b_off)[2][4][T::FN], f32x16 (&acc)[T::FM][T::FN])
+{
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        f32x4 a[T::FM];
+        float b[4][T::FN];
+#pragma unroll
+        for (int i = 0; i < T::FM; ++i)
+            a[i] = *(const __attribute__((address_space(3))) f32x4 *)(st + a_off[q][i]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int jj = 0; jj < T::FN; ++jj) b[j][jj] = *(const lds_float *)(st + b_off[q][j][jj]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int i = 0; i < T::FM; ++i)
+#pragma unroll
+                for (int jj = 0; jj < T::FN; ++jj)
+                    acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[i][j], b[j][jj], acc[i][jj], 0, 0, 0);
+    }
+}
+
+// Accumulator layout of v_mfma_f32_32x32x2_f32: lane l, register r holds row
+// 8 (r / 4) + 4 (l / 32) + r % 4, column l % 32 of the 32 x 32 block. Element (gm, gn)
+// of the product goes to C + gm * ldc + col_off(gn), for gm < M and gn < N.
+template <class T, class ColOff>
+__device__ __forceinline__ void direct_store(const GemmArgs &p, int m0, int n0, int wm0, int wn0, int lane,
+                                             const f32x16 (&acc)[T::FM][T::FN], ColOff col_off)
+{
+    const int col_l = lane & 31, row_l = 4 * (lane >> 5);
+#pragma unroll
+    for (int i = 0; i < T::FM; ++i)
+#pragma unroll
+        for (int jj = 0; jj < T::FN; ++jj)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int gm = m0 + wm0 + i * 32 + 8 * (r >> 2) + row_l + (r & 3);
+                const int gn = n0 + wn0 + jj * 32 + col_l;
+                if (gm < p.M && gn < p.N) p.C[(int64_t)gm * p.ldc + col_off(gn)] = acc[i][jj][r];
+            }
+}
+
+}  // namespace
+}  // namespace mm

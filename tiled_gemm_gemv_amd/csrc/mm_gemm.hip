@@ -33,24 +33,25 @@ struct ConfigEntry {
     int waves;       // per workgroup
     int wg_per_cu;   // workgroups a CU holds (registers and LDS)
     double tflops;   // measured on large shapes, for the choice below
+    int bk;          // K-step depth
 };
 
 // name: BMxBNxBK, wave tile, prefetch depth, waves per output block (K split).
 const ConfigEntry kConfigs[] = {
-    {"256x256x32 w128x64 pf1 ks1 (8 waves)", &launch_tile<T256x256k32>, 256, 256, 8, 1, 137},
-    {"128x128x32 w64x64 pf2 ks1 (4 waves)", &launch_tile<T128x128k32p2>, 128, 128, 4, 2, 122},
-    {"128x128x32 w64x64 pf1 ks2 (8 waves)", &launch_tile<T128x128k32s2>, 128, 128, 8, 1, 122},
-    {"64x64x64 w32x32 pf2 ks1 (4 waves)", &launch_tile<T64x64k64p2>, 64, 64, 4, 2, 113},
-    {"64x64x64 w32x32 pf2 ks2 (8 waves)", &launch_tile<T64x64k64p2s2>, 64, 64, 8, 1, 94},
-    {"128x64x64 w64x32 pf1 ks2 (8 waves)", &launch_tile<T128x64k64s2>, 128, 64, 8, 1, 111},
-    {"narrow 16x64 (16x16x4 MFMA), K over 8 waves, 16/NB chunks", &gemm_skinny_launch<8, 16>, 16, 64, 8, 1, 0},
-    {"narrow 16x64 (16x16x4 MFMA), K over 4 waves, 16/NB chunks", &gemm_skinny_launch<4, 16>, 16, 64, 4, 1, 0},
-    {"narrow 16x64 (16x16x4 MFMA), K over 16 waves, 4/NB chunks", &gemm_skinny_launch<16, 4>, 16, 64, 16, 1, 0},
-    {"columns <= 4: one wave per row, B rounds in LDS (8 x 4 per workgroup)", &gemm_cols_launch, 8, 4, 4, 1, 0},
-    {"256x256x16 w128x64 direct-to-LDS 4 stages (8 waves)", &direct_or_staged_256, 256, 256, 8, 1, 142},
-    {"128x128x16 w64x64 direct-to-LDS 4 stages (4 waves)", &direct<DirectTile::T128>, 128, 128, 4, 2, 135},
-    {"64x64x16 w32x32 direct-to-LDS 8 stages (4 waves)", &direct<DirectTile::T64S8>, 64, 64, 4, 2, 108},
-    {"64x64x16 w32x32 direct-to-LDS 4 stages (4 waves)", &direct<DirectTile::T64S4>, 64, 64, 4, 5, 116},
+    {"256x256x32 w128x64 pf1 ks1 (8 waves)", &launch_tile<T256x256k32>, 256, 256, 8, 1, 137, 32},
+    {"128x128x32 w64x64 pf2 ks1 (4 waves)", &launch_tile<T128x128k32p2>, 128, 128, 4, 2, 122, 32},
+    {"128x128x32 w64x64 pf1 ks2 (8 waves)", &launch_tile<T128x128k32s2>, 128, 128, 8, 1, 122, 32},
+    {"64x64x64 w32x32 pf2 ks1 (4 waves)", &launch_tile<T64x64k64p2>, 64, 64, 4, 2, 113, 64},
+    {"64x64x64 w32x32 pf2 ks2 (8 waves)", &launch_tile<T64x64k64p2s2>, 64, 64, 8, 1, 94, 64},
+    {"128x64x64 w64x32 pf1 ks2 (8 waves)", &launch_tile<T128x64k64s2>, 128, 64, 8, 1, 111, 64},
+    {"narrow 16x64 (16x16x4 MFMA), K over 8 waves, 16/NB chunks", &gemm_skinny_launch<8, 16>, 16, 64, 8, 1, 0, 16},
+    {"narrow 16x64 (16x16x4 MFMA), K over 4 waves, 16/NB chunks", &gemm_skinny_launch<4, 16>, 16, 64, 4, 1, 0, 16},
+    {"narrow 16x64 (16x16x4 MFMA), K over 16 waves, 4/NB chunks", &gemm_skinny_launch<16, 4>, 16, 64, 16, 1, 0, 16},
+    {"columns <= 4: one wave per row, B rounds in LDS (8 x 4 per workgroup)", &gemm_cols_launch, 8, 4, 4, 1, 0, 16},
+    {"256x256x16 w128x64 direct-to-LDS 4 stages (8 waves)", &direct_or_staged_256, 256, 256, 8, 1, 142, 16},
+    {"128x128x16 w64x64 direct-to-LDS 4 stages (4 waves)", &direct<DirectTile::T128>, 128, 128, 4, 2, 135, 16},
+    {"64x64x16 w32x32 direct-to-LDS 8 stages (4 waves)", &direct<DirectTile::T64S8>, 64, 64, 4, 2, 108, 16},
+    {"64x64x16 w32x32 direct-to-LDS 4 stages (4 waves)", &direct<DirectTile::T64S4>, 64, 64, 4, 5, 116, 16},
 };
 constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
 
@@ -88,14 +89,21 @@ int gemm_select_config(int64_t M, int64_t N, int64_t K, int64_t batch)
     double best_t = 0;
     for (int c : kTileConfigs) {
         if ((c == 10 || c == 11) && K < 2048) continue;
-        const ConfigEntry &e = kConfigs[c];
-        const double t = tile_time(batch * tiles_for(c, M, N), e.bm, e.bn, e.waves, e.wg_per_cu, e.tflops);
+        const double t = gemm_config_time(c, M, N, K, batch);
         if (c == 0 || t < best_t) {
             best = c;
             best_t = t;
         }
     }
     return best;
+}
+
+double gemm_config_time(int cfg, int64_t M, int64_t N, int64_t K, int64_t batch)
+{
+    if (cfg < 0 || cfg >= kNumConfigs || kConfigs[cfg].tflops <= 0) return 1e300;
+    const ConfigEntry &e = kConfigs[cfg];
+    return tile_time(batch * tiles_for(cfg, M, N), e.bm, e.bn, e.waves, e.wg_per_cu, e.tflops) *
+           k_steps_factor(K, e.bk);
 }
 
 hipError_t gemm_launch(int cfg, const GemmArgs &a, hipStream_t stream)

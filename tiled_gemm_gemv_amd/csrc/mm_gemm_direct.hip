@@ -34,70 +34,10 @@
 //     (M0 set there): the compiler cannot tell the stages apart and would otherwise wait
 //     for every load in flight before each LDS read, which removes the pipeline. No
 //     other code in these kernels uses M0.
-#include "mm_gemm_tile.h"
+#include "mm_direct.h"
 
 namespace mm {
 namespace {
-
-typedef __attribute__((address_space(3))) char lds_char;
-typedef __attribute__((address_space(3))) float lds_float;
-
-// GEN: every shape (4-byte lanes where needed); otherwise K % 16 == 0 and N % 4 == 0 only
-// (direct_f32_wide_ok), which keeps the narrow-lane code out of the kernel.
-template <int BM_, int BN_, int WM_, int WN_, int NS_, bool GEN_>
-struct DirectF32 {
-    static constexpr int BM = BM_, BN = BN_, BK = 16, NS = NS_, WM = WM_, WN = WN_;
-    static constexpr bool GEN = GEN_;
-    static constexpr int WAVES = (BM / WM) * (BN / WN), NT = WAVES * 64;
-    static constexpr int FM = WM / 32, FN = WN / 32;
-    static constexpr int A_BYTES = BM * BK * 4, B_BYTES = BK * BN * 4;
-    static constexpr int STAGE = A_BYTES + B_BYTES;
-    static constexpr int B_ROW = BN * 4;  // bytes per B row
-    // loads per wave per K-step with 16-byte (1 KB per wave) and 4-byte lanes (256 B)
-    static constexpr int A16 = A_BYTES / 1024 / WAVES, B16 = B_BYTES / 1024 / WAVES;
-    static constexpr int A4 = A_BYTES / 256 / WAVES, B4 = B_BYTES / 256 / WAVES;
-    static constexpr int LOADS_WIDE = A16 + B16, LOADS_NARROW_B = A16 + B4;
-    static_assert(A_BYTES % (1024 * WAVES) == 0 && B_BYTES % (1024 * WAVES) == 0, "whole loads");
-    static_assert(B_ROW >= 256 && B_ROW <= 1024, "B rows of 64 to 256 floats");
-    static_assert(NS * STAGE <= 160 * 1024, "stages must fit the 160 KB LDS");
-    static_assert((NS - 2) * LOADS_NARROW_B <= 63, "vmcnt range");
-};
-
-__device__ __forceinline__ int swz_a(int row) { return ((row >> 1) ^ (row >> 3)) & 3; }
-__device__ __forceinline__ int swz_b(int krow) { return ((krow >> 3) & 1) * 8; }
-
-// VEC bytes per lane from src into LDS at lds_addr + VEC * lane (lds_addr wave-uniform).
-template <int VEC>
-__device__ __forceinline__ void load_to_lds(unsigned lds_addr, const float *src)
-{
-    if constexpr (VEC == 16)
-        asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
-                     :: "s"(__builtin_amdgcn_readfirstlane(lds_addr)), "v"(src) : "memory");
-    else
-        asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off"
-                     :: "s"(__builtin_amdgcn_readfirstlane(lds_addr)), "v"(src) : "memory");
-}
-
-template <int N>
-__device__ __forceinline__ void wait_vmcnt()
-{
-    asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
-}
-
-// Wait until at most min(steps, S) K-steps of L loads each are outstanding.
-template <int L, int S>
-__device__ __forceinline__ void wait_steps(int steps)
-{
-    if constexpr (S > 0) {
-        if (steps >= S) {
-            wait_vmcnt<S * L>();
-            return;
-        }
-        wait_steps<L, S - 1>(steps);
-    } else {
-        wait_vmcnt<0>();
-    }
-}
 
 template <class T>
 __global__ __launch_bounds__(T::NT) void gemm_f32_direct_kernel(GemmArgs p)
@@ -156,26 +96,8 @@ __global__ __launch_bounds__(T::NT) void gemm_f32_direct_kernel(GemmArgs p)
     const unsigned lds0 = (unsigned)(uintptr_t)(lds_char *)lds;  // LDS byte offset of the array
     const int nk_full = p.K / T::BK;  // full K-steps; a partial one follows if K % 16 != 0
 
-    // operand addresses inside a stage (bytes): A per group q and block i; B per group q,
-    // step j and block jj (k = 8 (lane / 32) + 4 q + j, column wn0 + 32 jj + lane % 32)
     int a_off[2][T::FM], b_off[2][4][T::FN];
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-#pragma unroll
-        for (int i = 0; i < T::FM; ++i) {
-            const int row = wm0 + 32 * i + (lane & 31);
-            a_off[q][i] = row * 64 + 16 * ((q + 2 * (lane >> 5)) ^ swz_a(row));
-        }
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-            for (int jj = 0; jj < T::FN; ++jj) {
-                const int krow = 8 * (lane >> 5) + 4 * q + j;
-                const int col = wn0 + 32 * jj + (lane & 31);
-                b_off[q][j][jj] = T::A_BYTES + krow * T::B_ROW + 16 * ((col >> 2) ^ swz_b(krow)) +
-                                  4 * (col & 3);
-            }
-    }
+    direct_operand_offsets<T>(lane, wm0, wn0, a_off, b_off);
 
     f32x16 acc[T::FM][T::FN];
 #pragma unroll
@@ -186,27 +108,7 @@ __global__ __launch_bounds__(T::NT) void gemm_f32_direct_kernel(GemmArgs p)
             for (int r = 0; r < 16; ++r) acc[i][jj][r] = 0.f;
 
     auto multiply = [&](int kt) {
-        const lds_char *st = (const lds_char *)lds + (kt % T::NS) * T::STAGE;
-#pragma unroll
-        for (int q = 0; q < 2; ++q) {
-            f32x4 a[T::FM];
-            float b[4][T::FN];
-#pragma unroll
-            for (int i = 0; i < T::FM; ++i)
-                a[i] = *(const __attribute__((address_space(3))) f32x4 *)(st + a_off[q][i]);
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-#pragma unroll
-                for (int jj = 0; jj < T::FN; ++jj) b[j][jj] = *(const lds_float *)(st + b_off[q][j][jj]);
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-#pragma unroll
-                for (int i = 0; i < T::FM; ++i)
-#pragma unroll
-                    for (int jj = 0; jj < T::FN; ++jj)
-                        acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[i][j], b[j][jj], acc[i][jj],
-                                                                         0, 0, 0);
-        }
+        direct_multiply<T>((const lds_char *)lds + (kt % T::NS) * T::STAGE, a_off, b_off, acc);
     };
 
     // The K loop, compiled once per kind of tile (16- or 4-byte B lanes), so that a K-step
@@ -278,19 +180,7 @@ __global__ __launch_bounds__(T::NT) void gemm_f32_direct_kernel(GemmArgs p)
     if (!T::GEN || wide_b) k_loop(std::true_type{});
     else k_loop(std::false_type{});
 
-    // accumulator layout of v_mfma_f32_32x32x2_f32: lane l, register r holds row
-    // 8 (r / 4) + 4 (l / 32) + r % 4, column l % 32 of the 32 x 32 block
-    const int col_l = lane & 31, row_l = 4 * (lane >> 5);
-#pragma unroll
-    for (int i = 0; i < T::FM; ++i)
-#pragma unroll
-        for (int jj = 0; jj < T::FN; ++jj)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int gm = m0 + wm0 + i * 32 + 8 * (r >> 2) + row_l + (r & 3);
-                const int gn = n0 + wn0 + jj * 32 + col_l;
-                if (gm < p.M && gn < p.N) p.C[(int64_t)gm * p.ldc + gn] = acc[i][jj][r];
-            }
+    direct_store<T>(p, m0, n0, wm0, wn0, lane, acc, [](int gn) { return gn; });
 }
 
 template <class T>

@@ -56,20 +56,28 @@ struct GemvArgs {
     int M, N;
 };
 
-// Time model for choosing a tile shape (arbitrary units): a workgroup of `waves` waves
-// computes a BM x BN tile at `tflops` when 8 or more waves share its CU, and
-// proportionally slower with fewer (latency is then exposed); a CU holds at most
-// wg_per_cu workgroups; tiles run in rounds over the 256 CUs.
+// Time model for choosing a tile shape (arbitrary units): a CU computes a BM x BN tile
+// at `tflops` when 8 or more waves share it, and proportionally slower with fewer
+// (latency is then exposed). The busiest CU gets ceil(tiles / 256) tiles; it runs them in
+// sets of at most wg_per_cu concurrent workgroups, and a last, smaller set runs at its
+// own occupancy.
 inline double tile_time(int64_t tiles, int bm, int bn, int waves, int wg_per_cu, double tflops)
 {
     constexpr int64_t kCus = 256;
-    int64_t per_cu = (tiles + kCus - 1) / kCus;
-    if (per_cu > wg_per_cu) per_cu = wg_per_cu;
-    if (per_cu < 1) per_cu = 1;
-    const int64_t rounds = (tiles + kCus * per_cu - 1) / (kCus * per_cu);
-    double fill = (double)(per_cu * waves) / 8.0;
-    if (fill > 1.0) fill = 1.0;
-    return (double)rounds * per_cu * bm * bn / (tflops * fill);
+    const int64_t t = (tiles + kCus - 1) / kCus;
+    auto set_time = [&](int64_t wgs) {
+        double fill = (double)(wgs * waves) / 8.0;
+        if (fill > 1.0) fill = 1.0;
+        return (double)wgs * bm * bn / (tflops * fill);
+    };
+    const int64_t full = t / wg_per_cu, rem = t % wg_per_cu;
+    return (double)full * set_time(wg_per_cu) + (rem ? set_time(rem) : 0.0);
+}
+
+// K-steps of depth bk cover ceil(K / bk) bk rows: a partial last step costs a full one.
+inline double k_steps_factor(int64_t K, int bk)
+{
+    return K > 0 ? (double)((K + bk - 1) / bk * bk) / (double)K : 1.0;
 }
 
 // GEMM tile configurations, in the order of the public config index.
@@ -77,6 +85,8 @@ int gemm_num_configs();
 const char *gemm_config_name(int cfg);
 // batch: number of independent problems launched together (tiles are counted over all).
 int gemm_select_config(int64_t M, int64_t N, int64_t K, int64_t batch = 1);
+// The modelled time of tile config `cfg` (a macro-tile config; others: a large value).
+double gemm_config_time(int cfg, int64_t M, int64_t N, int64_t K, int64_t batch);
 // Enqueue config `cfg` of the GEMM (K >= 1, M >= 1, N >= 1).
 hipError_t gemm_launch(int cfg, const GemmArgs &a, hipStream_t stream);
 
@@ -114,11 +124,11 @@ struct ConvArgs {
     float *y;
 };
 
-// Convolution configurations: tile shapes of the GEMM (names as there).
+// Convolution configurations: tile shapes of the GEMM (BMxBNxBK and wave tile as there).
 int conv_num_configs();
 const char *conv_config_name(int cfg);
-// Choice for `batch` products of M filters by N output positions each.
-int conv_select_config(int64_t M, int64_t N, int64_t batch);
+// Choice for the implicit GEMM of M filters by N output positions by K = C R S.
+int conv_select_config(int64_t M, int64_t N, int64_t K);
 // The configuration conv_launch uses for a shape when none is given.
 int conv_choose_config(const ConvArgs &a);
 // Enqueue the convolution (cfg < 0: choose). The caller has checked the shape:
