@@ -54,7 +54,7 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
 CSRC = os.path.join(ROOT, "tiled_gemm_gemv_amd", "csrc")
 # the sources of each kernel whose HBM traffic profiles/hbm_traffic.txt records
 GEMM_SRC = [os.path.join(CSRC, "mm_gemm.hip"), os.path.join(CSRC, "mm_gemm_tile.h"),
-            os.path.join(CSRC, "mm_gemm_direct.hip")]
+            os.path.join(CSRC, "mm_gemm_direct.hip"), os.path.join(CSRC, "mm_direct.h")]
 GEMV_SRC = [os.path.join(CSRC, "mm_gemv.hip")]
 
 
