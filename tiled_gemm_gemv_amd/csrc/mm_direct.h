@@ -48,6 +48,9 @@ __device__ __forceinline__ int swz_a(int row) { return ((row >> 1) ^ (row >> 3))
 __device__ __forceinline__ int swz_b(int krow) { return ((krow >> 3) & 1) * 8; }
 
 // VEC bytes per lane from src into LDS at lds_addr + VEC * lane (lds_addr wave-uniform).
+// M0 is set and used inside one asm statement and not declared clobbered: the kernels
+// built on this header use M0 nowhere else (every M0 reference in their code is this
+// s_mov_b32 followed by its load), which their ISA was checked for.
 template <int VEC>
 __device__ __forceinline__ void load_to_lds(unsigned lds_addr, const float *src)
 {

@@ -7,14 +7,8 @@
 // M0 + 16 * lane without passing through registers. The waves then never write LDS
 // themselves (except to clear a partial last K-step), so the end of a K-step is only a
 // wait and a barrier, and no registers hold staged data: the ring runs NS = 4 or 8
-// stages deep, step kt + NS - 1 loading while step kt is multiplied.
-//   * BK = 16. A panel: BM rows of 64 bytes. The 16-byte chunk c of row r sits in slot
-//     c ^ swz_a(r), so that a wave's reads of 32 rows at one k hit distinct banks. Each
-//     lane reads 4 consecutive k of its row with one 16-byte read.
-//   * B panel: 16 rows of BN floats, row-major. v_mfma_f32_32x32x2_f32 takes one B value
-//     per lane per step, so a lane reads its column's value of the step's k row with a
-//     4-byte read; rows r and r + 8 (read by the two wave halves at once) are put on
-//     opposite halves of the banks by swz_b.
+// stages deep, step kt + NS - 1 loading while step kt is multiplied. The stage layout,
+// the k order and the MFMA step are in mm_direct.h.
 //   * Load width. A lane's bytes land at a fixed place, so each lane fetches the
 //     element(s) the permutations put there, and 4- and 16-byte lanes build the same
 //     LDS image. Full K-steps load A with 16-byte lanes whatever its alignment (gfx950
@@ -25,9 +19,6 @@
 //     C elements that are not stored. A partial last K-step (K % 16 != 0) loads both
 //     panels with 4-byte lanes at k clamped to K - 1, then the workgroup writes zeros
 //     over the k >= K entries of both panels between two barriers.
-//   * k order: as in the register-staged kernel, lanes 0-31 take k = 4 q + j and lanes
-//     32-63 k = 8 + 4 q + j at step j of group q, so each k of the K-step is added once,
-//     in the same order, and both kernels give the same bits.
 //   * One barrier per K-step, after an explicit s_waitcnt vmcnt that counts the loads of
 //     the steps issued after it (a partial last step issues more loads than a full one,
 //     which only makes that count conservative). The loads are issued from inline asm
