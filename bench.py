@@ -573,21 +573,31 @@ def sweep(kind, torch, mm, dev):
         rate = 1e3 / slope                      # bytes per second
         print(f"# cold fit over M >= 2048: fixed {t0 * 1e3:.2f} us per launch + streaming at "
               f"{rate / 1e9:.0f} GB/s ({100 * rate / rl.MI355X_HBM_PEAK:.1f}% of 8 TB/s)")
-        print("# transposed GEMV y = A^T x (mm_gemv_t_f32), same timing, cold")
+        print("# transposed GEMV y = A^T x, same timing, cold: mm_gemv_t_f32 (16-column strips) and "
+              "mm_gemv_t_f32_ws (row blocks, partial sums in a workspace, two launches)")
         for TM, TN in ((4096, 4096), (8192, 8192), (16384, 4096), (4096, 16384)):
             sets = max(2, min(16, (512 << 20) // (TM * TN * 4)))
             As = [torch.rand(TM, TN, device=dev) for _ in range(sets)]
             xs = [torch.rand(TM, device=dev) for _ in range(sets)]
             ys = [torch.empty(TN, device=dev) for _ in range(sets)]
+            ws = mm.gemv_t_workspace(TM, TN, dev)
+            wsb = 0 if ws is None else ws.numel()
 
             def cold_t(i, st):
                 k = i % sets
                 mm.mm_gemv_t_f32(TM, TN, As[k], xs[k], ys[k], st)
+
+            def cold_ws(i, st):
+                k = i % sets
+                mm.mm_gemv_t_f32_ws(TM, TN, As[k], xs[k], ys[k], ws, wsb, st)
             by = rl.FP32 * (TM * TN + TM + TN)
-            tc = burst_time_ms(torch, cold_t, 8 * sets)
-            print(f"#   M={TM:6d} N={TN:6d}: {tc * 1e3:8.2f} us {by / tc / 1e6:6.0f} GB/s "
-                  f"({100 * by * 1e3 / tc / rl.MI355X_HBM_PEAK:.1f}% of 8 TB/s)", flush=True)
-            del As, xs, ys
+            cells = []
+            for fn in (cold_t, cold_ws):
+                tc = burst_time_ms(torch, fn, 8 * sets)
+                cells.append(f"{tc * 1e3:8.2f} us {by / tc / 1e6:6.0f} GB/s "
+                             f"({100 * by * 1e3 / tc / rl.MI355X_HBM_PEAK:.1f}%)")
+            print(f"#   M={TM:6d} N={TN:6d}: strips {cells[0]}   workspace {cells[1]}", flush=True)
+            del As, xs, ys, ws
 
 
 if __name__ == "__main__":

@@ -105,6 +105,30 @@ int mm_gemv_t_f32(int64_t M, int64_t N, const float *A, const float *x, float *y
                   void *stream);
 
 /*
+ * mm_gemv_t_f32_ws: y = A^T x as mm_gemv_t_f32, with a caller-owned device workspace
+ * that lets it read A along whole rows (1 KB of a row per wave instruction, as the
+ * GEMV does): each workgroup sums a 256-column strip over a block of rows into the
+ * workspace, and a second launch on the same stream adds the row blocks' partial sums
+ * per column in row-block order, so results are deterministic (they may differ from
+ * mm_gemv_t_f32's in the last bits: the summation order differs).
+ *   workspace        device memory of at least mm_gemv_t_f32_workspace_bytes(M, N)
+ *                    bytes, 16-byte aligned; its contents on entry do not matter and
+ *                    are overwritten. May be NULL when that size is 0.
+ *   workspace_bytes  its size in bytes.
+ * Calls that share a workspace must not run at the same time (e.g. keep them on one
+ * stream). Shapes for which the row blocks gain nothing (fewer than 512 rows, rows not
+ * 16-byte aligned) run the kernel of mm_gemv_t_f32 and leave the workspace untouched.
+ * Other arguments and errors: as for mm_gemv_t_f32; MM_ERR_INVALID_ARG also for a
+ * workspace that is missing, too small or misaligned.
+ *
+ * mm_gemv_t_f32_workspace_bytes: bytes of workspace mm_gemv_t_f32_ws needs for (M, N)
+ * (0 when it needs none), or -1 for a negative or too large size.
+ */
+int64_t mm_gemv_t_f32_workspace_bytes(int64_t M, int64_t N);
+int mm_gemv_t_f32_ws(int64_t M, int64_t N, const float *A, const float *x, float *y,
+                     void *workspace, int64_t workspace_bytes, void *stream);
+
+/*
  * Tile configurations of the GEMM. mm_gemm_f32 picks one per shape; the calls
  * below expose the choice and let a caller (tests, tuning) run a given one.
  *   mm_gemm_f32_num_configs: number of configurations, >= 1.

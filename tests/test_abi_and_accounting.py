@@ -114,6 +114,29 @@ def test_gemv_rejects_invalid_arguments(lib, args, why):
     assert why in mm.mm_last_error()
 
 
+def test_gemv_t_workspace_sizes_and_checks(lib):
+    ws = mm.mm_gemv_t_f32_workspace_bytes
+    assert ws(4096, 4096) == 16 * 4096 * 4     # 16 strips of 256 columns, 16 row blocks
+    assert ws(4096, 16384) == 4 * 16384 * 4    # 64 strips: 4 row blocks make ~256 workgroups
+    assert ws(1000, 4096) == 3 * 4096 * 4      # at least 256 rows per block
+    for M, N in [(511, 4096), (4096, 1001), (300, 8), (0, 5), (5, 0)]:
+        assert ws(M, N) == 0, (M, N)           # served by the strips kernel
+    assert ws(-1, 3) == -1 and ws(3, 1 << 31) == -1
+    need = ws(4096, 4096)
+    f = lib.mm_gemv_t_f32_ws
+    for args, why in [((None, need), "workspace is NULL"), ((FAKE + 4, need), "16-byte"),
+                      ((FAKE, need - 4), "smaller")]:
+        assert f(4096, 4096, FAKE, FAKE, FAKE, *args, None) == mm.MM_ERR_INVALID_ARG
+        assert why in mm.mm_last_error()
+    for a, x, y, why in [(None, FAKE, FAKE, "A is NULL"), (FAKE, None, FAKE, "x is NULL"),
+                         (FAKE, FAKE, None, "y is NULL"), (FAKE + 2, FAKE, FAKE, "aligned")]:
+        assert f(4096, 4096, a, x, y, FAKE, need, None) == mm.MM_ERR_INVALID_ARG
+        assert why in mm.mm_last_error()
+    # no workspace needed: the checks of mm_gemv_t_f32, and nothing enqueued for N == 0
+    assert f(300, 8, None, FAKE, FAKE, None, 0, None) == mm.MM_ERR_INVALID_ARG
+    assert f(7, 0, None, FAKE, None, None, 0, None) == mm.MM_OK
+
+
 def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     import importlib
     monkeypatch.setattr(mm, "_lib", None)

@@ -74,3 +74,60 @@ def test_deterministic_and_m_zero(dev):
     mm.gemv_t(torch.empty((0, 8), device=dev), torch.empty(0, device=dev), out=y[:8])
     torch.cuda.synchronize()
     assert (y[:8] == 0).all().item() and torch.isnan(y[8]).item()
+
+
+def run_ws(A, x, dev, a_offset=0, ws=None):
+    """mm_gemv_t_f32_ws through the binding, with a NaN-filled workspace (its contents on
+    entry must not matter) and a canary after y."""
+    M, N = A.shape
+    abuf = to_device(np.concatenate([np.full(a_offset, np.nan, np.float32), A.ravel()]), dev)
+    Ad = abuf[a_offset:].view(M, N)
+    if ws is None:
+        ws = mm.gemv_t_workspace(M, N, dev)
+        if ws is not None:
+            ws.view(torch.float32).fill_(float("nan"))
+    y = torch.full((N + 1,), float("nan"), device=dev)
+    mm.gemv_t(Ad, to_device(x, dev), out=y[:N], workspace=ws)
+    torch.cuda.synchronize()
+    h = y.cpu().numpy()
+    assert np.isnan(h[N]), "wrote past the end of y"
+    return h[:N]
+
+
+# row blocks (several sizes of block and strip, a ragged last strip and block) and shapes
+# that fall back to the strips kernel (too few rows, N % 4 != 0, tiny)
+WS_SHAPES = [(4096, 4096), (512, 4096), (1000, 4096), (4096, 16384), (5000, 1000), (1300, 260),
+             (2600, 8), (511, 4096), (4096, 1001), (300, 8)]
+
+
+@pytest.mark.parametrize("M,N", WS_SHAPES)
+@pytest.mark.parametrize("a_offset", [0, 1])   # 1: rows not 16-byte aligned (strips kernel)
+def test_workspace_variant(dev, M, N, a_offset):
+    A = wl.random_matrix(520 + M, M, N, "int4")
+    x = wl.random_matrix(620 + N, 1, M, "int4")[0]
+    y64, _ = reference(A, x)
+    r = verify.exact(run_ws(A, x, dev, a_offset), y64)
+    assert r, f"{(M, N)}: {r}"
+    A = wl.random_matrix(720 + M, M, N, "u11")
+    x = wl.random_matrix(820 + N, 1, M, "u11")[0]
+    y64, s64 = reference(A, x)
+    r = verify.within_tol(run_ws(A, x, dev, a_offset), y64, s64, 1e-5)
+    assert r, f"{(M, N)}: {r}"
+
+
+def test_workspace_reuse_and_determinism(dev):
+    """One workspace for calls in a row (the second smaller): each overwrites what it
+    needs; repeated calls give the same bits."""
+    ws = mm.gemv_t_workspace(4096, 4096, dev)
+    for M, N in [(4096, 4096), (1000, 4096), (4096, 4096)]:
+        A = wl.random_matrix(930 + M, M, N, "int4")
+        x = wl.random_matrix(940 + N, 1, M, "int4")[0]
+        y64, _ = reference(A, x)
+        r = verify.exact(run_ws(A, x, dev, ws=ws), y64)
+        assert r, f"{(M, N)}: {r}"
+    A = to_device(wl.random_matrix(95, 4096, 4096, "u11"), dev)
+    x = to_device(wl.random_matrix(96, 1, 4096, "u11")[0], dev)
+    y1 = mm.gemv_t(A, x, workspace=ws)
+    y2 = mm.gemv_t(A, x, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(y1.view(torch.int32), y2.view(torch.int32))

@@ -85,6 +85,10 @@ def load():
     lib.mm_gemv_f32.argtypes = [i64, i64, vp, vp, vp, vp]
     lib.mm_gemv_t_f32.argtypes = [i64, i64, vp, vp, vp, vp]
     lib.mm_gemv_t_f32.restype = ci
+    lib.mm_gemv_t_f32_workspace_bytes.argtypes = [i64, i64]
+    lib.mm_gemv_t_f32_workspace_bytes.restype = i64
+    lib.mm_gemv_t_f32_ws.argtypes = [i64, i64, vp, vp, vp, vp, i64, vp]
+    lib.mm_gemv_t_f32_ws.restype = ci
     lib.mm_gemv_f32.restype = ci
     conv_args = [i64] * 13 + [vp, vp, vp, vp]
     lib.mm_conv2d_f32.argtypes = conv_args
@@ -211,6 +215,18 @@ def mm_gemv_t_f32(M, N, A, x, y, stream=None):
     lib = load()
     _check(lib.mm_gemv_t_f32(M, N, _addr(A), _addr(x), _addr(y), _stream(stream)),
            "mm_gemv_t_f32")
+
+
+def mm_gemv_t_f32_workspace_bytes(M, N):
+    """Bytes of workspace mm_gemv_t_f32_ws needs for (M, N); -1 for invalid sizes."""
+    return load().mm_gemv_t_f32_workspace_bytes(M, N)
+
+
+def mm_gemv_t_f32_ws(M, N, A, x, y, workspace, workspace_bytes, stream=None):
+    """y = A^T x reading A along whole rows, partial sums in `workspace`. Raises MMError."""
+    lib = load()
+    _check(lib.mm_gemv_t_f32_ws(M, N, _addr(A), _addr(x), _addr(y), _addr(workspace), workspace_bytes,
+                                _stream(stream)), "mm_gemv_t_f32_ws")
 
 
 def mm_gemm_f32_num_configs():
@@ -381,8 +397,19 @@ def gemv(A, x, out=None, stream=None):
     return out
 
 
-def gemv_t(A, x, out=None, stream=None):
-    """out = A.T @ x for an fp32 GPU matrix with packed rows and a contiguous vector."""
+def gemv_t_workspace(M, N, device):
+    """A device buffer of the size mm_gemv_t_f32_ws needs for (M, N) (None if none)."""
+    import torch
+    n = mm_gemv_t_f32_workspace_bytes(M, N)
+    if n < 0:
+        raise ValueError(f"invalid sizes {M} x {N}")
+    return torch.empty(n, dtype=torch.uint8, device=device) if n > 0 else None
+
+
+def gemv_t(A, x, out=None, workspace=None, stream=None):
+    """out = A.T @ x for an fp32 GPU matrix with packed rows and a contiguous vector.
+    With `workspace` (a device tensor of at least mm_gemv_t_f32_workspace_bytes bytes,
+    e.g. from gemv_t_workspace) it runs mm_gemv_t_f32_ws."""
     import torch
     _matrix(A, "A")
     M, N = A.shape
@@ -395,7 +422,12 @@ def gemv_t(A, x, out=None, stream=None):
     if out.dtype != torch.float32 or tuple(out.shape) != (N,) or not out.is_contiguous():
         raise ValueError(f"out must be a contiguous float32 vector of {N} entries")
     with torch.cuda.device(A.device):
-        mm_gemv_t_f32(M, N, A, x, out, stream)
+        if workspace is None:
+            mm_gemv_t_f32(M, N, A, x, out, stream)
+        else:
+            if workspace.device != A.device:
+                raise ValueError("workspace is on another device")
+            mm_gemv_t_f32_ws(M, N, A, x, out, workspace, workspace.numel() * workspace.element_size(), stream)
     return out
 
 

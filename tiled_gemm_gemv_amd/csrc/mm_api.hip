@@ -354,6 +354,40 @@ int mm_gemv_t_f32(int64_t M, int64_t N, const float *A, const float *x, float *y
     return from_hip("gemv_t launch", mm::gemv_t_launch(a, s));
 }
 
+int64_t mm_gemv_t_f32_workspace_bytes(int64_t M, int64_t N)
+{
+    if (M < 0 || N < 0 || M > kMaxDim || N > kMaxDim) return -1;
+    if (M == 0 || N == 0) return 0;
+    return 4 * mm::gemv_t_ws_floats(M, N);
+}
+
+int mm_gemv_t_f32_ws(int64_t M, int64_t N, const float *A, const float *x, float *y, void *workspace,
+                     int64_t workspace_bytes, void *stream)
+{
+    const int64_t need = mm_gemv_t_f32_workspace_bytes(M, N);
+    if (need > 0) {
+        if (!workspace) return invalid("workspace is NULL");
+        if ((uintptr_t)workspace % 16) return invalid("workspace not 16-byte aligned");
+        if (workspace_bytes < need) return invalid("workspace smaller than mm_gemv_t_f32_workspace_bytes");
+    }
+    if (need <= 0) return mm_gemv_t_f32(M, N, A, x, y, stream);  // the checks and the strips kernel
+    // same checks as mm_gemv_t_f32 (M, N >= 1 here)
+    if (!A) return invalid("A is NULL");
+    if (!x) return invalid("x is NULL");
+    if (!y) return invalid("y is NULL");
+    if ((uintptr_t)A % 4 || (uintptr_t)x % 4 || (uintptr_t)y % 4)
+        return invalid("pointer not aligned to its element size");
+    if (!extent_fits(M, N, N)) return invalid("A extent overflows");
+    mm::GemvArgs a;
+    a.A = A;
+    a.x = x;
+    a.y = y;
+    a.M = (int)M;
+    a.N = (int)N;
+    return from_hip("gemv_t launch", mm::gemv_t_ws_launch(a, static_cast<float *>(workspace),
+                                                            static_cast<hipStream_t>(stream)));
+}
+
 int mm_conv2d_f32(int64_t N, int64_t C, int64_t H, int64_t W, int64_t K, int64_t R, int64_t S,
                   int64_t sh, int64_t sw, int64_t ph, int64_t pw, int64_t dh, int64_t dw,
                   const float *x, const float *w, float *y, void *stream)

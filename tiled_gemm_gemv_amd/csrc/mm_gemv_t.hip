@@ -16,6 +16,16 @@
 //     to the same XCD (the launch order is renumbered as in the GEMM), so the two
 //     halves of a 128-byte line are read through one L2.
 // Rows that are not 16-byte aligned (N % 4 != 0 or an unaligned A) use 4-byte loads.
+//
+// With a workspace (gemv_t_ws_launch) the rows are read as the GEMV reads them: a
+// workgroup takes a 256-column strip of a block of rows, so a wave instruction reads
+// 1 KB of one row; the 16 waves of the workgroup take interleaved rows, 16 in flight
+// each, and their sums meet in LDS in wave order. Each workgroup writes its strip of
+// the row block's partial y to the workspace, and a second launch adds the row blocks'
+// partials per column in row-block order (deterministic). A single launch that let the
+// last workgroup of a strip add the partials needs device-scope release/acquire fences,
+// which on this GPU write back and invalidate a whole XCD's L2 per workgroup: measured
+// far slower than the second launch.
 #include "mm_internal.h"
 
 namespace mm {
@@ -97,7 +107,120 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_t_kernel(GemvArgs p)
         if (c < ncols) p.y[j0 + c] = acc[c];
 }
 
+constexpr int kWide = 256;     // columns per row-block workgroup (1 KB of a row per wave)
+constexpr int kRbWaves = 16;   // waves per row-block workgroup
+constexpr int kRbDepth = 16;   // rows in flight per wave
+constexpr int kMinBlockRows = kRbWaves * kRbDepth;
+
+// Pass 1: partial y of row block rb over columns [256 cs, 256 cs + 256) into
+// part[rb * N + j]. N % 4 == 0, A 16-byte aligned.
+__global__ __launch_bounds__(kRbWaves * 64) void gemv_t_rows_kernel(GemvArgs p, float *part, int blocks,
+                                                                     int block_rows)
+{
+    __shared__ f32x4 red[kRbWaves][64];
+    const int64_t strips = ((int64_t)p.N + kWide - 1) / kWide;
+    const int64_t bid = linear_block();
+    if (bid >= strips * blocks) return;  // padding of a 2-D grid (whole workgroup, before any barrier)
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int rb = (int)(bid / strips), cs = (int)(bid % strips);
+    const int j = cs * kWide + 4 * lane;
+    const bool col_ok = j < p.N;  // then j + 3 < N too (N % 4 == 0)
+    const int r0 = rb * block_rows;
+    const int r1 = min(p.M, r0 + block_rows);
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int t0 = r0 + w; t0 < r1; t0 += kRbWaves * kRbDepth) {
+        f32x4 va[kRbDepth];
+        float vx[kRbDepth];
+#pragma unroll
+        for (int d = 0; d < kRbDepth; ++d) {
+            const int i = t0 + d * kRbWaves;
+            const bool ok = i < r1;
+            va[d] = (ok && col_ok) ? __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(p.A + (int64_t)i * p.N + j))
+                                   : f32x4{0.f, 0.f, 0.f, 0.f};
+            vx[d] = ok ? p.x[i] : 0.f;
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int d = 0; d < kRbDepth; ++d) {
+            acc[0] += va[d][0] * vx[d];
+            acc[1] += va[d][1] * vx[d];
+            acc[2] += va[d][2] * vx[d];
+            acc[3] += va[d][3] * vx[d];
+        }
+    }
+    red[w][lane] = acc;
+    __syncthreads();
+    if (w != 0 || !col_ok) return;  // no barrier follows
+    f32x4 s = red[0][lane];
+#pragma unroll
+    for (int v = 1; v < kRbWaves; ++v) s += red[v][lane];
+    *reinterpret_cast<f32x4 *>(part + (int64_t)rb * p.N + j) = s;
+}
+
+// Pass 2: y[j .. j + 3] = sum over row blocks, in order, of the partials (one lane per 4
+// columns). The loads go out 8 at a time (a loop of dependent load-add steps would pay
+// one memory round trip per row block); past the last block they read as zeros, which
+// leave the sum as it is.
+__global__ __launch_bounds__(256) void gemv_t_sum_kernel(const float *part, float *y, int N, int blocks)
+{
+    const int64_t j = 4 * (linear_block() * 256 + threadIdx.x);
+    if (j >= N) return;
+    f32x4 t = {0.f, 0.f, 0.f, 0.f};
+    for (int r0 = 0; r0 < blocks; r0 += 8) {
+        f32x4 v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+            v[u] = (r0 + u < blocks) ? *reinterpret_cast<const f32x4 *>(part + (int64_t)(r0 + u) * N + j)
+                                     : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int u = 0; u < 8; ++u) t += v[u];
+    }
+#pragma unroll
+    for (int c = 0; c < 4; ++c) y[j + c] = t[c];
+}
+
+// Row blocks for (M, N): about 256 workgroups in all, at least kMinBlockRows rows each
+// (0: the strips kernel serves the shape better, or its rows are not 16-byte aligned).
+int row_blocks(int64_t M, int64_t N)
+{
+    if (N % 4 != 0) return 0;
+    const int64_t strips = (N + kWide - 1) / kWide;
+    int64_t blocks = (256 + strips - 1) / strips;
+    const int64_t most = M / kMinBlockRows;
+    if (blocks > most) blocks = most;
+    return blocks >= 2 ? (int)blocks : 0;
+}
+
 }  // namespace
+
+int64_t gemv_t_ws_floats(int64_t M, int64_t N)
+{
+    return (int64_t)row_blocks(M, N) * N;
+}
+
+hipError_t gemv_t_ws_launch(const GemvArgs &a, float *ws, hipStream_t stream)
+{
+    const int blocks = row_blocks(a.M, a.N);
+    if (blocks == 0 || (uintptr_t)a.A % 16 != 0) return gemv_t_launch(a, stream);
+    const int block_rows = (int)(((int64_t)a.M + blocks - 1) / blocks);
+    const int64_t strips = ((int64_t)a.N + kWide - 1) / kWide;
+    unsigned gx, gy;
+    if (!grid_for(strips * blocks, gx, gy)) return hipErrorInvalidConfiguration;
+    GemvArgs arg = a;
+    int nb = blocks, br = block_rows;
+    void *args1[] = {&arg, &ws, &nb, &br};
+    hipError_t e = hipLaunchKernel(reinterpret_cast<const void *>(&gemv_t_rows_kernel), dim3(gx, gy),
+                                   dim3(kRbWaves * 64), args1, 0, stream);
+    if (e != hipSuccess) return e;
+    const int64_t lanes = ((int64_t)a.N + 3) / 4;
+    if (!grid_for((lanes + 255) / 256, gx, gy)) return hipErrorInvalidConfiguration;
+    const float *part = ws;
+    float *y = a.y;
+    int n = a.N;
+    void *args2[] = {&part, &y, &n, &nb};
+    return hipLaunchKernel(reinterpret_cast<const void *>(&gemv_t_sum_kernel), dim3(gx, gy), dim3(256), args2, 0,
+                           stream);
+}
 
 hipError_t gemv_t_launch(const GemvArgs &a, hipStream_t stream)
 {

@@ -143,6 +143,12 @@ hipError_t gemv_launch(const GemvArgs &a, hipStream_t stream);
 // Enqueue the transposed GEMV y = A^T x (mm_gemv_t.hip); x has M entries, y has N.
 // M >= 1, N >= 1.
 hipError_t gemv_t_launch(const GemvArgs &a, hipStream_t stream);
+// y = A^T x in row blocks with partial sums in a workspace of gemv_t_ws_floats(M, N)
+// floats (16-byte aligned), then a second launch that adds them; shapes that gain
+// nothing from it (or whose rows are not 16-byte aligned) run gemv_t_launch and leave
+// the workspace alone. M, N >= 1.
+int64_t gemv_t_ws_floats(int64_t M, int64_t N);
+hipError_t gemv_t_ws_launch(const GemvArgs &a, float *ws, hipStream_t stream);
 
 // Enqueue a fill of the rows x cols matrix at p (row stride ld) with zeros.
 hipError_t zero_fill_launch(float *p, int64_t rows, int64_t cols, int64_t ld, hipStream_t stream);
