@@ -554,6 +554,7 @@ hipError_t launch16_direct(const Gemm16Args &a, hipStream_t stream)
 
 using D16L = Direct16<256, 256, 128, 64>;
 using D16M = Direct16<128, 128, 64, 64>;
+using D16S = Direct16<64, 64, 32, 32>;
 
 using T16L = Tile16<256, 256, 128, 64>;
 using T16M = Tile16<128, 128, 64, 64>;
@@ -563,7 +564,7 @@ using T16Sp2 = Tile16<64, 64, 32, 32, 2>;
 
 }  // namespace
 
-int gemm16_num_configs() { return 7; }
+int gemm16_num_configs() { return 8; }
 
 const char *gemm16_config_name(int cfg)
 {
@@ -571,18 +572,21 @@ const char *gemm16_config_name(int cfg)
                                   "64x64x64 w32x32 pf1 (4 waves)", "128x128x64 w64x64 pf2 (4 waves)",
                                   "64x64x64 w32x32 pf2 (4 waves)",
                                   "256x256x32 w128x64 direct-to-LDS 4 stages (8 waves)",
-                                  "128x128x32 w64x64 direct-to-LDS 4 stages (4 waves)"};
-    return (cfg >= 0 && cfg < 7) ? names[cfg] : nullptr;
+                                  "128x128x32 w64x64 direct-to-LDS 4 stages (4 waves)",
+                                  "64x64x32 w32x32 direct-to-LDS 4 stages (4 waves)"};
+    return (cfg >= 0 && cfg < 8) ? names[cfg] : nullptr;
 }
 
 int gemm16_select_config(int64_t M, int64_t N, int64_t K)
 {
     (void)K;
-    // 5 and 6 are the direct pipelines; on shapes they cannot take they run the 256 x 256
-    // and 128 x 128 register-staged kernels (configs 0 and 3)
+    // 5, 6 and 7 are the direct pipelines; on shapes they cannot take they run the
+    // register-staged kernels of their size (configs 0, 3 and 4). Smaller tiles where the
+    // big ones would leave CUs idle (1024^3 bf16: 243 TFLOP/s on the 64 x 64 direct tile
+    // against 144 staged).
     if (((M + 255) / 256) * ((N + 255) / 256) >= 200) return 5;
     if (((M + 127) / 128) * ((N + 127) / 128) >= 200) return 6;
-    return 4;
+    return 7;
 }
 
 hipError_t gemm16_launch(int cfg, bool bf16, const void *A, int64_t lda, const void *B, int64_t ldb,
@@ -609,9 +613,12 @@ hipError_t gemm16_launch(int cfg, bool bf16, const void *A, int64_t lda, const v
     case 5:
         if (!direct_ok(a)) return gemm16_launch(0, bf16, A, lda, B, ldb, C, ldc, M, N, K, stream);
         return bf16 ? launch16_direct<D16L, true>(a, stream) : launch16_direct<D16L, false>(a, stream);
-    default:
+    case 6:
         if (!direct_ok(a)) return gemm16_launch(3, bf16, A, lda, B, ldb, C, ldc, M, N, K, stream);
         return bf16 ? launch16_direct<D16M, true>(a, stream) : launch16_direct<D16M, false>(a, stream);
+    default:
+        if (!direct_ok(a)) return gemm16_launch(4, bf16, A, lda, B, ldb, C, ldc, M, N, K, stream);
+        return bf16 ? launch16_direct<D16S, true>(a, stream) : launch16_direct<D16S, false>(a, stream);
     }
 }
 
