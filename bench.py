@@ -13,7 +13,9 @@ line's `value` is the step's FLOP rate (the GEMM is more than 99.9% of it); the
 `gemm` and `gemv` objects give each kernel's own rate from HIP events recorded on
 the launch stream around every launch in the timed region. After the timed steps
 a burst of GEMV launches over 8 rotating 64 MiB matrices (more than the 256 MB
-Infinity Cache) gives the GEMV's HBM rate. Results are then verified against the
+Infinity Cache) gives the GEMV's HBM rate. A clock phase follows (--clock-seconds,
+default 2.5 s: the GEMM again, untimed, while amdsmi reports the graphics clock),
+for the fp32 peak at the clock the kernel ran at. Results are then verified against the
 CPU oracle (64+ sampled GEMM rows in full, every GEMV output) and the oracle's
 own time on a bounded sample of the same work is reported as `cpu_baseline`.
 
@@ -111,6 +113,94 @@ def host_threads():
     return max(1, min(n, 16))
 
 
+class ClockProbe:
+    """Graphics clock of the benchmark GPU as its power-management firmware reports
+    it (amdsmi GPU metrics: the current clock of each XCD, averaged over the XCDs).
+    The matrix peaks (157.3 TFLOP/s fp32, 2.5 PFLOP/s 16-bit) are quoted at 2.4 GHz and
+    scale with the clock, so the clock seen while a kernel runs gives the peak at that
+    clock. Reading it is optional: without the amdsmi module or a matching device the
+    probe reports why."""
+
+    def __init__(self, torch, dev):
+        self.handle, self.why, self.samples, self.inited = None, None, [], False
+        try:
+            import amdsmi
+        except ImportError as e:
+            self.why = f"amdsmi not importable ({e})"
+            return
+        self.amdsmi = amdsmi
+        try:
+            amdsmi.amdsmi_init()
+            self.inited = True
+            p = torch.cuda.get_device_properties(dev)
+            want = f"{p.pci_domain_id:04x}:{p.pci_bus_id:02x}:{p.pci_device_id:02x}."
+            for h in amdsmi.amdsmi_get_processor_handles():
+                if amdsmi.amdsmi_get_gpu_device_bdf(h).lower().startswith(want):
+                    self.handle = h
+            if self.handle is None:
+                self.why = f"no amdsmi device at PCI {want}"
+            elif self.read() is None:
+                self.handle, self.why = None, "GPU metrics carry no graphics clock"
+        except Exception as e:  # noqa: BLE001 - any amdsmi failure only drops the clock
+            self.handle, self.why = None, "amdsmi: " + " ".join(str(e).split())
+
+    def read(self):
+        """Current graphics clock in MHz (mean over the XCDs that report one), or None."""
+        m = self.amdsmi.amdsmi_get_gpu_metrics_info(self.handle)
+        per_xcd = m.get("current_gfxclks")
+        if isinstance(per_xcd, list):
+            vals = [v for v in per_xcd if isinstance(v, (int, float)) and v > 0]
+            if vals:
+                return float(np.mean(vals))
+        v = m.get("current_gfxclk")
+        return float(v) if isinstance(v, (int, float)) and v > 0 else None
+
+    def measure(self, torch, stream, launch, seconds, launch_s):
+        """Run `launch` back to back for about `seconds` and sample the clock every
+        20 ms meanwhile. The firmware's metrics are cached by the driver for a few
+        hundred milliseconds (an idle reading was still returned 0.3 s into a
+        sustained load), so only samples from the second half of the run are kept:
+        by then every reading was taken while the kernel was running."""
+        if self.handle is None or seconds <= 0:
+            return
+        n = max(1, min(2000, int(np.ceil(seconds / max(launch_s, 1e-6)))))
+        done = torch.cuda.Event()
+        t0 = time.perf_counter()
+        for _ in range(n):
+            launch()
+        done.record(stream)
+        timed = []
+        while not done.query():
+            v = self.read()
+            if v is not None:
+                timed.append((time.perf_counter() - t0, v))
+            time.sleep(0.02)
+        total = time.perf_counter() - t0
+        self.seconds = total
+        self.samples = [v for t, v in timed if t >= total / 2]
+
+    def summary(self, tflops, peak_tflops_at_max):
+        if not self.samples:
+            return {"gfxclk_mhz": None, "why": self.why or "no sample taken"}
+        f = float(np.median(self.samples))
+        peak = peak_tflops_at_max * (f * 1e6 / rl.MI355X_PEAK_SCLK_HZ)
+        return {"gfxclk_mhz": round(f, 1), "gfxclk_mhz_min": round(min(self.samples), 1),
+                "gfxclk_mhz_max": round(max(self.samples), 1), "samples": len(self.samples),
+                "source": f"amdsmi GPU metrics (current clock of each XCD, averaged), sampled "
+                          f"in the second half of {self.seconds:.1f} s of the same kernel run "
+                          f"back to back after the timed steps",
+                "peak_at_clock": round(peak, 2),
+                "frac_at_clock": round(tflops / peak, 4)}
+
+    def close(self):
+        if self.inited:
+            self.inited = False
+            try:
+                self.amdsmi.amdsmi_shut_down()
+            except Exception:  # noqa: BLE001
+                pass
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -121,6 +211,9 @@ def main():
                     help="target length of the oracle's timed sample")
     ap.add_argument("--only", choices=["gemm", "gemv", "copy", "h16", "conv"], default=None,
                     help="profiling helper: launch only this kernel --steps times")
+    ap.add_argument("--clock-seconds", type=float, default=None,
+                    help="length of the clock phase (default 2.5 s after the timed steps; "
+                         "with --only h16 none unless given; 0: no clock reading)")
     ap.add_argument("--sweep", choices=["gemm", "gemv", "h16", "conv"], default=None,
                     help="print a timing table instead of the benchmark line")
     args = ap.parse_args()
@@ -168,6 +261,14 @@ def main():
             mm.mm_gemm_bf16(M, N, K, A16, K, B16, N, C, N, stream)
         torch.cuda.synchronize()
         log(f"h16: {args.steps} bf16 launches")
+        if args.clock_seconds:
+            clock = ClockProbe(torch, dev)
+            clock.measure(torch, stream, lambda: mm.mm_gemm_bf16(M, N, K, A16, K, B16, N, C, N, stream),
+                          args.clock_seconds, 1e-3)
+            torch.cuda.synchronize()
+            c = clock.summary(0.0, rl.MI355X_16BIT_MFMA_PEAK / 1e12)
+            clock.close()
+            log(f"h16 clock: {json.dumps(c)}")
         return
 
     if args.only == "conv":
@@ -211,6 +312,8 @@ def main():
         torch.cuda.synchronize()
         log(f"gemv: {args.steps} launches")
         return
+
+    clock = ClockProbe(torch, dev)
 
     # ---------------------------------------------------------------- warm-up
     log(f"warm-up: {args.warmup} steps")
@@ -262,6 +365,11 @@ def main():
     gemv_gbs = gemv_bytes / (burst_ms / 1e3) / 1e9
     step_tflops = steps * (gemm_flop + gemv_flop) / elapsed / 1e12
     traffic = read_traffic()
+
+    # ------------------- clock phase: the same GEMM again, untimed, clock sampled
+    clock.measure(torch, stream, gemm, 2.5 if args.clock_seconds is None else args.clock_seconds,
+                  gemm_avg_s)
+    torch.cuda.synchronize()
 
     # ------------------------------------------- verification + CPU baseline leg
     import oracle
@@ -329,6 +437,7 @@ def main():
             "algorithmic_bytes": rl.gemm_algorithmic_bytes(M, N, K),
             "verified_rows": int(len(rows)),
             "verify": str(gemm_check),
+            "clock": clock.summary(gemm_tflops, rl.MI355X_FP32_MFMA_PEAK / 1e12),
         },
         "gemv": {
             "value": round(gemv_gbs, 1),
@@ -359,6 +468,7 @@ def main():
         },
         "verified": bool(gemm_check) and gemv_ok,
     }
+    clock.close()
     print(json.dumps(result), flush=True)
     if not result["verified"]:
         log(f"VERIFICATION FAILED: gemm {gemm_check}; gemv ok={gemv_ok}")
