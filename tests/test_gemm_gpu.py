@@ -116,8 +116,10 @@ def edge_shapes(seed, count):
 # Shapes the direct-to-LDS pipelines take (K % 16 == 0, N % 4 == 0, aligned): one, two,
 # three, four and many K-steps (the prologue fills up to three stages), M and N that are
 # not tile multiples (clamped loads, masked stores).
-DIRECT_SHAPES = [(1, 4, 16), (37, 8, 32), (300, 264, 48), (257, 520, 64), (129, 136, 4096),
-                 (1000, 1532, 800)]
+# K % 32 == 0 takes the 256 x 256 tile's K-steps of 32 (two stages; one, two, three and
+# many steps), other K its K-steps of 16.
+DIRECT_SHAPES = [(1, 4, 16), (37, 8, 32), (300, 264, 48), (257, 520, 64), (300, 264, 96),
+                 (513, 260, 160), (129, 136, 4096), (1000, 1532, 800)]
 
 
 @pytest.mark.parametrize("cfg", [10, 11, 12, 13, None])
@@ -130,6 +132,19 @@ def test_direct_pipeline_shapes(dev, cfg, shape):
     A = wl.random_matrix(1300 + M, M, K, "normal")
     B = wl.random_matrix(1400 + N, K, N, "normal")
     assert_tol(gpu_gemm(A, B, dev, cfg), A, B)
+
+
+@pytest.mark.parametrize("shape", [(300, 264, 96), (513, 260, 4096)])
+def test_direct_256_same_bits_as_staged_256(dev, shape):
+    """With K-steps of 32 the 256 x 256 direct tile adds each output's k terms in the
+    order of the register-staged 256 x 256 x 32 tile (configuration 0), so the two give
+    the same bits on random inputs."""
+    M, N, K = shape
+    A = wl.random_matrix(1900 + M, M, K, "normal")
+    B = wl.random_matrix(1950 + N, K, N, "normal")
+    C10 = gpu_gemm(A, B, dev, 10)
+    C0 = gpu_gemm(A, B, dev, 0)
+    assert np.array_equal(C10.view(np.int32), C0.view(np.int32))
 
 
 # Shapes that only the 4-byte DMA lanes take (K % 16 != 0, odd leading dimensions, N < 4):

@@ -179,7 +179,7 @@ __global__ __launch_bounds__(T::NT) void conv_direct_kernel(GemmArgs p, Im2colOp
     for (int i = 0; i < T::A16; ++i) {
         const int ob = (T::A16 * w + i) * 1024 + 16 * lane;
         const int row = ob / 64, chunk = (ob % 64) / 16;
-        asrc[i] = p.A + (int64_t)min(m0 + row, p.M - 1) * p.lda + 4 * (chunk ^ swz_a(row));
+        asrc[i] = p.A + (int64_t)min(m0 + row, p.M - 1) * p.lda + 4 * (chunk ^ swz_a<T>(row));
     }
     // B: the wave loads rows ROWS * w .. ROWS * w + ROWS - 1 of each K-step, PER_ROW loads
     // per row; this lane's column in load h of a row, and that column's state
@@ -188,7 +188,7 @@ __global__ __launch_bounds__(T::NT) void conv_direct_kernel(GemmArgs p, Im2colOp
 #pragma unroll
     for (int h = 0; h < PER_ROW; ++h) {
         const int slot = 64 * h + lane;  // 4-byte slot in the row
-        const int col = n0 + 4 * ((slot >> 2) ^ swz_b(krow0)) + (slot & 3);
+        const int col = n0 + 4 * ((slot >> 2) ^ swz_b<T>(krow0)) + (slot & 3);
         cols[h] = o.columns_of(p, col);
     }
     static_assert(8 % ROWS == 0, "a wave's rows lie in one 8-row half: they share swz_b");
@@ -208,7 +208,7 @@ __global__ __launch_bounds__(T::NT) void conv_direct_kernel(GemmArgs p, Im2colOp
             for (int i = 0; i < T::A4; ++i) {
                 const int ob = (T::A4 * w + i) * 256 + 4 * lane;
                 const int row = ob / 64, slot = (ob % 64) / 4;
-                const int k = k0 + 4 * ((slot >> 2) ^ swz_a(row)) + (slot & 3);
+                const int k = k0 + 4 * ((slot >> 2) ^ swz_a<T>(row)) + (slot & 3);
                 const float *src = k < p.K ? p.A + (int64_t)min(m0 + row, p.M - 1) * p.lda + k : zeros;
                 load_to_lds<4>(st + (T::A4 * w + i) * 256, src);
             }
@@ -254,7 +254,7 @@ __global__ __launch_bounds__(T::NT) void conv_direct_kernel(GemmArgs p, Im2colOp
         }
     };
 
-    int a_off[2][T::FM], b_off[2][4][T::FN];
+    int a_off[T::QN][T::FM], b_off[T::QN][4][T::FN];
     direct_operand_offsets<T>(lane, wm0, wn0, a_off, b_off);
     f32x16 acc[T::FM][T::FN];
 #pragma unroll

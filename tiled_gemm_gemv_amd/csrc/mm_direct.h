@@ -1,19 +1,22 @@
 // mm_direct.h -- building blocks of the fp32 tiles whose panels the LDS DMA moves from
 // HBM straight into LDS (the GEMM of mm_gemm_direct.hip and the convolution of
-// mm_conv_direct.hip): tile parameters, the LDS layout's permutations, the DMA and wait
+// mm_conv.hip): tile parameters, the LDS layout's permutations, the DMA and wait
 // primitives, and the MFMA step on one stage.
 //
-// LDS layout of a stage (BK = 16):
-//   * A panel: BM rows of 64 bytes. The 16-byte chunk c of row r sits in slot
+// LDS layout of a stage (BK = 16 or 32 k per K-step):
+//   * A panel: BM rows of 4 BK bytes. The 16-byte chunk c of row r sits in slot
 //     c ^ swz_a(r), so that a wave's reads of 32 rows at one k hit distinct banks; each
 //     lane reads 4 consecutive k of its row with one 16-byte read.
-//   * B panel: 16 rows of BN floats, row-major. v_mfma_f32_32x32x2_f32 takes one B value
+//   * B panel: BK rows of BN floats, row-major. v_mfma_f32_32x32x2_f32 takes one B value
 //     per lane per step, so a lane reads its column's value of the step's k row with a
-//     4-byte read; rows r and r + 8 (read by the two wave halves at once) are put on
+//     4-byte read; rows r and r + BK/2 (read by the two wave halves at once) are put on
 //     opposite halves of the banks by swz_b (chunk index ^ 8).
-//   * k order: lanes 0-31 take k = 4 q + j and lanes 32-63 k = 8 + 4 q + j at step j of
-//     group q, so each k of the K-step is added once, in the register-staged kernel's
-//     order (the same bits).
+//   * k order: lanes 0-31 take k = 4 q + j and lanes 32-63 k = BK/2 + 4 q + j at step j
+//     of group q (q < BK/8), so each k of the K-step is added once, in the order of the
+//     register-staged kernel with the same BK (the same bits).
+// BK = 32 makes each A row of a K-step one whole 128-byte line (at BK = 16 a load of A
+// touches 16 half-used lines); on the 256 x 256 tile it measured 0.9% faster, with two
+// 64 KB stages.
 #pragma once
 #include "mm_gemm_tile.h"
 
@@ -25,9 +28,11 @@ typedef __attribute__((address_space(3))) float lds_float;
 
 // GEN: every shape (4-byte lanes where needed); otherwise K % 16 == 0 and N % 4 == 0 only
 // (direct_f32_wide_ok), which keeps the narrow-lane code out of the kernel.
-template <int BM_, int BN_, int WM_, int WN_, int NS_, bool GEN_>
+template <int BM_, int BN_, int WM_, int WN_, int NS_, bool GEN_, int BK_ = 16>
 struct DirectF32 {
-    static constexpr int BM = BM_, BN = BN_, BK = 16, NS = NS_, WM = WM_, WN = WN_;
+    static constexpr int BM = BM_, BN = BN_, BK = BK_, NS = NS_, WM = WM_, WN = WN_;
+    static constexpr int QN = BK / 8;      // groups of 4 k per wave half and K-step
+    static constexpr int A_ROW = BK * 4;   // bytes per A row
     static constexpr bool GEN = GEN_;
     static constexpr int WAVES = (BM / WM) * (BN / WN), NT = WAVES * 64;
     static constexpr int FM = WM / 32, FN = WN / 32;
@@ -42,10 +47,19 @@ struct DirectF32 {
     static_assert(B_ROW >= 256 && B_ROW <= 1024, "B rows of 64 to 256 floats");
     static_assert(NS * STAGE <= 160 * 1024, "stages must fit the 160 KB LDS");
     static_assert((NS - 2) * LOADS_NARROW_B <= 63, "vmcnt range");
+    static_assert(BK == 16 || (BK == 32 && !GEN), "BK of 32 only for the lean build");
 };
 
-__device__ __forceinline__ int swz_a(int row) { return ((row >> 1) ^ (row >> 3)) & 3; }
-__device__ __forceinline__ int swz_b(int krow) { return ((krow >> 3) & 1) * 8; }
+// Rows of 64 bytes: two rows per 128 bytes of banks. Rows of 128 bytes: the 8 chunk slots
+// of any 8 (or, on 64 banks, 16) consecutive rows read at one k are distinct.
+template <class T>
+__device__ __forceinline__ int swz_a(int row)
+{
+    if constexpr (T::BK == 16) return ((row >> 1) ^ (row >> 3)) & 3;
+    else return ((row >> 1) & 7) ^ ((row & 1) << 2);
+}
+template <class T>
+__device__ __forceinline__ int swz_b(int krow) { return ((krow / (T::BK / 2)) & 1) * 8; }
 
 // VEC bytes per lane from src into LDS at lds_addr + VEC * lane (lds_addr wave-uniform).
 // M0 is set and used inside one asm statement and not declared clobbered: the kernels
@@ -86,35 +100,35 @@ __device__ __forceinline__ void wait_steps(int steps)
 // This lane's operand addresses inside a stage (bytes): A per group q and block i; B per
 // group q, step j and block jj (k = 8 (lane / 32) + 4 q + j, column wn0 + 32 jj + lane % 32).
 template <class T>
-__device__ __forceinline__ void direct_operand_offsets(int lane, int wm0, int wn0, int (&a_off)[2][T::FM],
-                                                       int (&b_off)[2][4][T::FN])
+__device__ __forceinline__ void direct_operand_offsets(int lane, int wm0, int wn0, int (&a_off)[T::QN][T::FM],
+                                                       int (&b_off)[T::QN][4][T::FN])
 {
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
+    for (int q = 0; q < T::QN; ++q) {
 #pragma unroll
         for (int i = 0; i < T::FM; ++i) {
             const int row = wm0 + 32 * i + (lane & 31);
-            a_off[q][i] = row * 64 + 16 * ((q + 2 * (lane >> 5)) ^ swz_a(row));
+            a_off[q][i] = row * T::A_ROW + 16 * ((q + T::QN * (lane >> 5)) ^ swz_a<T>(row));
         }
 #pragma unroll
         for (int j = 0; j < 4; ++j)
 #pragma unroll
             for (int jj = 0; jj < T::FN; ++jj) {
-                const int krow = 8 * (lane >> 5) + 4 * q + j;
+                const int krow = (T::BK / 2) * (lane >> 5) + 4 * q + j;
                 const int col = wn0 + 32 * jj + (lane & 31);
-                b_off[q][j][jj] = T::A_BYTES + krow * T::B_ROW + 16 * ((col >> 2) ^ swz_b(krow)) +
+                b_off[q][j][jj] = T::A_BYTES + krow * T::B_ROW + 16 * ((col >> 2) ^ swz_b<T>(krow)) +
                                   4 * (col & 3);
             }
     }
 }
 
-// The MFMAs of one K-step on stage st: two groups of 4 k per lane half.
+// The MFMAs of one K-step on stage st: BK / 8 groups of 4 k per lane half.
 template <class T>
-__device__ __forceinline__ void direct_multiply(const lds_char *st, const int (&a_off)[2][T::FM],
-                                                const int (&b_off)[2][4][T::FN], f32x16 (&acc)[T::FM][T::FN])
+__device__ __forceinline__ void direct_multiply(const lds_char *st, const int (&a_off)[T::QN][T::FM],
+                                                const int (&b_off)[T::QN][4][T::FN], f32x16 (&acc)[T::FM][T::FN])
 {
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
+    for (int q = 0; q < T::QN; ++q) {
         f32x4 a[T::FM];
         float b[4][T::FN];
 #pragma unroll

@@ -48,7 +48,7 @@ const ConfigEntry kConfigs[] = {
     {"narrow 16x64 (16x16x4 MFMA), K over 4 waves, 16/NB chunks", &gemm_skinny_launch<4, 16>, 16, 64, 4, 1, 0, 16},
     {"narrow 16x64 (16x16x4 MFMA), K over 16 waves, 4/NB chunks", &gemm_skinny_launch<16, 4>, 16, 64, 16, 1, 0, 16},
     {"columns <= 4: one wave per row, B rounds in LDS (8 x 4 per workgroup)", &gemm_cols_launch, 8, 4, 4, 1, 0, 16},
-    {"256x256x16 w128x64 direct-to-LDS 4 stages (8 waves)", &direct_or_staged_256, 256, 256, 8, 1, 142, 16},
+    {"256x256x32 w128x64 direct-to-LDS 2 stages (8 waves)", &direct_or_staged_256, 256, 256, 8, 1, 143, 32},
     {"128x128x16 w64x64 direct-to-LDS 4 stages (4 waves)", &direct<DirectTile::T128>, 128, 128, 4, 2, 135, 16},
     {"64x64x16 w32x32 direct-to-LDS 8 stages (4 waves)", &direct<DirectTile::T64S8>, 64, 64, 4, 2, 108, 16},
     {"64x64x16 w32x32 direct-to-LDS 4 stages (4 waves)", &direct<DirectTile::T64S4>, 64, 64, 4, 5, 116, 16},

@@ -6,9 +6,11 @@
 // global_load_lds_dword{,x4} writes each lane's 4 or 16 bytes to LDS at M0 + 4 * lane or
 // M0 + 16 * lane without passing through registers. The waves then never write LDS
 // themselves (except to clear a partial last K-step), so the end of a K-step is only a
-// wait and a barrier, and no registers hold staged data: the ring runs NS = 4 or 8
-// stages deep, step kt + NS - 1 loading while step kt is multiplied. The stage layout,
-// the k order and the MFMA step are in mm_direct.h.
+// wait and a barrier, and no registers hold staged data: the ring runs NS = 2, 4 or 8
+// stages deep, step kt + NS - 1 loading while step kt is multiplied (the 256 x 256 tile
+// takes K-steps of 32 in two 64 KB stages when K % 32 == 0, else of 16 in four; the
+// others take K-steps of 16). The stage layout, the k order and the MFMA step are in
+// mm_direct.h.
 //   * Load width. A lane's bytes land at a fixed place, so each lane fetches the
 //     element(s) the permutations put there, and 4- and 16-byte lanes build the same
 //     LDS image. Full K-steps load A with 16-byte lanes whatever its alignment (gfx950
@@ -58,8 +60,8 @@ __global__ __launch_bounds__(T::NT) void gemm_f32_direct_kernel(GemmArgs p)
 #pragma unroll
     for (int i = 0; i < T::A16; ++i) {
         const int o = (T::A16 * w + i) * 1024 + 16 * lane;  // panel byte
-        const int row = o / 64, chunk = (o % 64) / 16;
-        asrc[i] = p.A + (int64_t)min(m0 + row, p.M - 1) * p.lda + 4 * (chunk ^ swz_a(row));
+        const int row = o / T::A_ROW, chunk = (o % T::A_ROW) / 16;
+        asrc[i] = p.A + (int64_t)min(m0 + row, p.M - 1) * p.lda + 4 * (chunk ^ swz_a<T>(row));
     }
     // B chunks stay inside their row when N % 4 == 0 (clamped to the last chunk) or when
     // the whole tile lies left of the last partial chunk
@@ -68,26 +70,26 @@ __global__ __launch_bounds__(T::NT) void gemm_f32_direct_kernel(GemmArgs p)
     for (int i = 0; i < T::B16; ++i) {
         const int o = (T::B16 * w + i) * 1024 + 16 * lane;
         const int krow = o / T::B_ROW, chunk = (o % T::B_ROW) / 16;
-        const int col = n0 + 4 * (chunk ^ swz_b(krow));
+        const int col = n0 + 4 * (chunk ^ swz_b<T>(krow));
         bsrc[i] = p.B + (int64_t)krow * p.ldb + max(min(col, p.N - 4), 0);
     }
     // 4-byte lanes: source of load i at K-step k0, k clamped to K - 1 (partial step)
     auto a4_src = [&](int i, int k0) {
         const int o = (T::A4 * w + i) * 256 + 4 * lane;
-        const int row = o / 64, slot = (o % 64) / 4;
-        const int k = min(k0 + 4 * ((slot >> 2) ^ swz_a(row)) + (slot & 3), p.K - 1);
+        const int row = o / T::A_ROW, slot = (o % T::A_ROW) / 4;
+        const int k = min(k0 + 4 * ((slot >> 2) ^ swz_a<T>(row)) + (slot & 3), p.K - 1);
         return p.A + (int64_t)min(m0 + row, p.M - 1) * p.lda + k;
     };
     auto b4_src = [&](int i, int k0) {
         const int o = (T::B4 * w + i) * 256 + 4 * lane;
         const int krow = o / T::B_ROW, slot = (o % T::B_ROW) / 4;
-        const int col = n0 + 4 * ((slot >> 2) ^ swz_b(krow)) + (slot & 3);
+        const int col = n0 + 4 * ((slot >> 2) ^ swz_b<T>(krow)) + (slot & 3);
         return p.B + (int64_t)min(k0 + krow, p.K - 1) * p.ldb + min(col, p.N - 1);
     };
     const unsigned lds0 = (unsigned)(uintptr_t)(lds_char *)lds;  // LDS byte offset of the array
     const int nk_full = p.K / T::BK;  // full K-steps; a partial one follows if K % 16 != 0
 
-    int a_off[2][T::FM], b_off[2][4][T::FN];
+    int a_off[T::QN][T::FM], b_off[T::QN][4][T::FN];
     direct_operand_offsets<T>(lane, wm0, wn0, a_off, b_off);
 
     f32x16 acc[T::FM][T::FN];
@@ -160,7 +162,7 @@ __global__ __launch_bounds__(T::NT) void gemm_f32_direct_kernel(GemmArgs p)
             const int kr = p.K - nk_full * T::BK, nz = T::BK - kr;
             for (int e = threadIdx.x; e < T::BM * nz; e += T::NT) {
                 const int r = e / nz, k = kr + e % nz;
-                *(lds_float *)(st + r * 64 + 16 * ((k >> 2) ^ swz_a(r)) + 4 * (k & 3)) = 0.f;
+                *(lds_float *)(st + r * T::A_ROW + 16 * ((k >> 2) ^ swz_a<T>(r)) + 4 * (k & 3)) = 0.f;
             }
             for (int e = threadIdx.x; e < nz * T::BN; e += T::NT)
                 *(lds_float *)(st + T::A_BYTES + (kr + e / T::BN) * T::B_ROW + 4 * (e % T::BN)) = 0.f;
@@ -212,7 +214,9 @@ hipError_t gemm_direct_launch(DirectTile t, const GemmArgs &a, hipStream_t strea
 {
     switch (t) {
     case DirectTile::T256:
+        // K-steps of 32 (two 64 KB stages) where K allows, else of 16 (four 32 KB stages)
         if (!direct_f32_wide_ok(a)) return hipErrorInvalidValue;
+        if (a.K % 32 == 0) return launch_direct<DirectF32<256, 256, 128, 64, 2, false, 32>>(a, stream);
         return launch_direct<DirectF32<256, 256, 128, 64, 4, false>>(a, stream);
     case DirectTile::T128:
         return launch_lean_or_general<128, 128, 64, 64, 4>(a, stream);
