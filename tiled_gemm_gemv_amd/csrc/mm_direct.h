@@ -15,8 +15,9 @@
 //     of group q (q < BK/8), so each k of the K-step is added once, in the order of the
 //     register-staged kernel with the same BK (the same bits).
 // BK = 32 makes each A row of a K-step one whole 128-byte line (at BK = 16 a load of A
-// touches 16 half-used lines); on the 256 x 256 tile it measured 0.9% faster, with two
-// 64 KB stages.
+// touches 16 half-used lines, and the DMA's LDS writes of those rows count bank-conflict
+// cycles) and doubles the MFMAs per barrier; with half the stages in the same LDS it
+// measured 0.9% faster on the 256 x 256 tile and 1-8% on the 128 x 128 and 64 x 64 ones.
 #pragma once
 #include "mm_gemm_tile.h"
 
