@@ -65,15 +65,19 @@ __device__ __forceinline__ int swz_b(int krow) { return ((krow / (T::BK / 2)) & 
 // VEC bytes per lane from src into LDS at lds_addr + VEC * lane (lds_addr wave-uniform).
 // M0 is set and used inside one asm statement and not declared clobbered: the kernels
 // built on this header use M0 nowhere else (every M0 reference in their code is this
-// s_mov_b32 followed by its load), which their ISA was checked for.
+// s_mov_b32 followed by its load), which their ISA was checked for. A global load with
+// LDS = 1 that reads M0 needs one wait state after the SALU write of M0 (CDNA's table of
+// manually inserted wait states); the hazard recognizer does not look inside an asm
+// string, so the s_nop is written here (the compiler's own builtin leaves at least one
+// instruction there too).
 template <int VEC>
 __device__ __forceinline__ void load_to_lds(unsigned lds_addr, const float *src)
 {
     if constexpr (VEC == 16)
-        asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
+        asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
                      :: "s"(__builtin_amdgcn_readfirstlane(lds_addr)), "v"(src) : "memory");
     else
-        asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off"
+        asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off"
                      :: "s"(__builtin_amdgcn_readfirstlane(lds_addr)), "v"(src) : "memory");
 }
 

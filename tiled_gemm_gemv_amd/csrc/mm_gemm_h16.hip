@@ -397,9 +397,11 @@ typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) char lds_char;
 
 // 16 bytes per lane from src into LDS at lds_addr + 16 * lane (lds_addr wave-uniform).
+// The s_nop is the one wait state a global load with LDS = 1 needs after an SALU write of
+// M0 (the hazard recognizer does not look inside an asm string).
 __device__ __forceinline__ void load_to_lds(unsigned lds_addr, const unsigned short *src)
 {
-    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
                  :: "s"(__builtin_amdgcn_readfirstlane(lds_addr)), "v"(src) : "memory");
 }
 
