@@ -89,14 +89,15 @@ def test_workloads(dev, fmt, cfg, name):
 
 
 # Shapes the direct HBM -> LDS pipeline takes (K % 32 == 0, N % 8 == 0, aligned): one,
-# two, three and many K-steps (its prologue fills up to three stages), M and N that
-# are not tile multiples (clamped loads, masked stores), a single row.
-DIRECT_SHAPES = [(1, 8, 32), (37, 8, 64), (300, 264, 96), (257, 520, 128), (129, 136, 4096),
-                 (1000, 1528, 800)]
+# two, three and many K-steps of 32 (four stages: the prologue fills up to three) and,
+# where K % 64 == 0, of 64 (two stages), M and N that are not tile multiples (clamped
+# loads, masked stores), a single row.
+DIRECT_SHAPES = [(1, 8, 32), (37, 8, 64), (300, 264, 96), (257, 520, 128), (300, 264, 192),
+                 (129, 136, 4096), (1000, 1528, 800)]
 
 
 @pytest.mark.parametrize("fmt", list(FORMATS))
-@pytest.mark.parametrize("cfg", [5, 6, None])
+@pytest.mark.parametrize("cfg", [5, 6, 7, None])
 @pytest.mark.parametrize("shape", DIRECT_SHAPES)
 def test_direct_pipeline_shapes(dev, fmt, cfg, shape):
     M, N, K = shape

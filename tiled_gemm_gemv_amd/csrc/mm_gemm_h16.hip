@@ -351,12 +351,17 @@ hipError_t launch16(const Gemm16Args &a, hipStream_t stream)
 // LDS (lane l's bytes land at M0 + 16 l), with no staging registers. That frees the
 // registers the loop above spends on staged data, so the pipeline can run NS = 4 LDS
 // stages deep: the loads for K-step kt + 3 are issued while step kt's MFMAs run, which
-// covers three K-steps of MFMA time instead of one. BK = 32 (64-byte A rows).
-//   * A panel (BM rows x 32 k): stored as loaded, 64 bytes per row; the four 16-byte
+// covers three K-steps of MFMA time instead of one. BK = 32 (64-byte A rows); where
+// K % 64 == 0, BK = 64 in two stages of twice the size (the same LDS): each A row of a
+// step is then one whole 128-byte line (a 64-byte row is half a line, and the DMA's LDS
+// writes of such rows count bank-conflict cycles), with twice the MFMAs per barrier
+// (measured +2-5% on the 256 x 256 tile, +5-17% on the 128 x 128 one, +17-30% on the
+// 64 x 64 one).
+//   * A panel (BM rows x BK k): stored as loaded, 2 BK bytes per row; the 16-byte
 //     chunks of row r sit in slots c ^ swz_a(r), so that the MFMA operand reads of 32
 //     rows at one k fall in distinct banks (no padding; the load pattern applies the
 //     permutation by choosing which chunk each lane fetches).
-//   * B panel (32 k rows x BN): stored row-major as loaded, chunks of row k in slots
+//   * B panel (BK k rows x BN): stored row-major as loaded, chunks of row k in slots
 //     c ^ swz_b(k). The MFMA wants 8 consecutive k of one column per lane; gfx950's
 //     ds_read_b64_tr_b16 provides them: in each group of 16 lanes, result lane i,
 //     element c is element i % 4 of the 4 values lane 4 c + i / 4 addressed. Lane j of a
@@ -365,27 +370,40 @@ hipError_t launch16(const Gemm16Args &a, hipStream_t stream)
 //   * One barrier per K-step, after an explicit wait for the step's loads (vmcnt
 //     counts the loads of the steps issued after it). The loads are issued from inline
 //     asm so that the compiler does not add a wait for all of them before every LDS read.
-//   * Requirements (checked on the host): K % 32 == 0, N % 8 == 0, lda and ldb
+//   * Requirements (checked on the host): K % 32 == 0 (K % 64 == 0 for BK = 64), N % 8 == 0, lda and ldb
 //     multiples of 8 elements, A and B 16-byte aligned. Rows past M and column chunks
 //     past N are clamped to in-range ones; they only feed C elements that are not
 //     stored. K needs no mask (whole K-steps).
-template <int BM_, int BN_, int WM_, int WN_>
+template <int BM_, int BN_, int WM_, int WN_, int BK_ = 32, int NS_ = 4>
 struct Direct16 {
-    static constexpr int BM = BM_, BN = BN_, BK = 32, NS = 4, WM = WM_, WN = WN_;
+    static constexpr int BM = BM_, BN = BN_, BK = BK_, NS = NS_, WM = WM_, WN = WN_;
     static constexpr int WAVES = (BM / WM) * (BN / WN), NT = WAVES * 64;
-    static constexpr int FM = WM / 32, FN = WN / 32;
-    static constexpr int A_BYTES = BM * BK * 2, B_BYTES = BK * BN * 2;
+    static constexpr int FM = WM / 32, FN = WN / 32, KS = BK / 16;  // KS: 16-k MFMA steps
+    static constexpr int A_ROW = BK * 2, A_CPR = A_ROW / 16;        // A row bytes, 16-byte chunks
+    static constexpr int A_ROWS_PER_LOAD = 1024 / A_ROW;
+    static constexpr int A_BYTES = BM * A_ROW, B_BYTES = BK * BN * 2;
     static constexpr int STAGE = A_BYTES + B_BYTES;
     static constexpr int B_ROW = BN * 2;                      // bytes per B row
-    static constexpr int A_LOADS = BM / 16 / WAVES;           // 1 KB loads per wave per step
-    static constexpr int B_LOADS = BN / 16 / WAVES;
+    static constexpr int A_LOADS = A_BYTES / 1024 / WAVES;    // 1 KB loads per wave per step
+    static constexpr int B_LOADS = B_BYTES / 1024 / WAVES;
     static constexpr int B_ROWS_PER_LOAD = 1024 / B_ROW;
-    static_assert(BM % (16 * WAVES) == 0 && BN % (16 * WAVES) == 0, "whole 1 KB loads per wave");
+    static_assert(BK == 32 || BK == 64, "K-steps of 32 or 64");
+    static_assert(A_BYTES % (1024 * WAVES) == 0 && B_BYTES % (1024 * WAVES) == 0,
+                  "whole 1 KB loads per wave");
+    static_assert((NS - 2) * (A_LOADS + B_LOADS) <= 63, "vmcnt range");
     static_assert(BN >= 64 && BN % 32 == 0 && WN % 32 == 0 && WM % 32 == 0, "tile shape");
     static_assert(NS * STAGE <= 160 * 1024, "stages must fit the 160 KB LDS");
 };
 
-__device__ __forceinline__ int swz_a16(int row) { return ((row >> 1) ^ (row >> 3)) & 3; }
+// A rows of 64 bytes (BK = 32): two rows per 128 bytes of banks. Rows of 128 bytes
+// (BK = 64): the 8 chunk slots of any 8 (or, on 64 banks, 16) consecutive rows read at
+// one k are distinct.
+template <class T>
+__device__ __forceinline__ int swz_a16(int row)
+{
+    if constexpr (T::A_CPR == 4) return ((row >> 1) ^ (row >> 3)) & 3;
+    else return ((row >> 1) & 7) ^ ((row & 1) << 2);
+}
 
 template <class T>
 __device__ __forceinline__ int swz_b16(int krow)
@@ -412,6 +430,18 @@ __device__ __forceinline__ void wait_vmcnt()
     asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
 }
 
+// Wait until at most min(later, S) K-steps of L loads each are outstanding.
+template <int L, int S>
+__device__ __forceinline__ void wait_later(int later)
+{
+    if constexpr (S == 0) {
+        wait_vmcnt<0>();
+    } else {
+        if (later >= S) wait_vmcnt<S * L>();
+        else wait_later<L, S - 1>(later);
+    }
+}
+
 template <class T, bool BF16>
 __global__ __launch_bounds__(T::NT) void gemm_h16_direct_kernel(Gemm16Args p)
 {
@@ -434,8 +464,8 @@ __global__ __launch_bounds__(T::NT) void gemm_h16_direct_kernel(Gemm16Args p)
     const unsigned short *bsrc[T::B_LOADS];
 #pragma unroll
     for (int i = 0; i < T::A_LOADS; ++i) {
-        const int row = 16 * (T::A_LOADS * w + i) + (lane >> 2);
-        const int chunk = (lane & 3) ^ swz_a16(row);
+        const int row = T::A_ROWS_PER_LOAD * (T::A_LOADS * w + i) + lane / T::A_CPR;
+        const int chunk = (lane % T::A_CPR) ^ swz_a16<T>(row);
         asrc[i] = p.A + (int64_t)min(m0 + row, p.M - 1) * p.lda + 8 * chunk;
     }
 #pragma unroll
@@ -457,14 +487,14 @@ __global__ __launch_bounds__(T::NT) void gemm_h16_direct_kernel(Gemm16Args p)
                         bsrc[i] + (int64_t)kt * T::BK * p.ldb);
     };
 
-    // operand addresses inside a stage (bytes), for the two 16-k halves of a K-step
-    int a_off[2][T::FM], b_off[2][2][T::FN];
+    // operand addresses inside a stage (bytes), for the 16-k MFMA steps of a K-step
+    int a_off[T::KS][T::FM], b_off[T::KS][2][T::FN];
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
+    for (int ks = 0; ks < T::KS; ++ks) {
 #pragma unroll
         for (int i = 0; i < T::FM; ++i) {
             const int row = wm0 + 32 * i + (lane & 31);
-            a_off[ks][i] = row * 64 + 16 * ((2 * ks + (lane >> 5)) ^ swz_a16(row));
+            a_off[ks][i] = row * T::A_ROW + 16 * ((2 * ks + (lane >> 5)) ^ swz_a16<T>(row));
         }
         const int g = lane >> 4, j16 = lane & 15;
 #pragma unroll
@@ -490,17 +520,14 @@ __global__ __launch_bounds__(T::NT) void gemm_h16_direct_kernel(Gemm16Args p)
     for (int s = 0; s < T::NS - 1 && s < nk; ++s) issue(s);
     for (int kt = 0; kt < nk; ++kt) {
         // step kt's loads are done when at most the later steps' loads are outstanding
-        const int later = nk - 1 - kt;
-        if (later >= 2) wait_vmcnt<2 * LOADS>();
-        else if (later == 1) wait_vmcnt<LOADS>();
-        else wait_vmcnt<0>();
+        wait_later<LOADS, T::NS - 2>(nk - 1 - kt);
         // every wave's loads for stage kt are in LDS, and every wave is done with the
         // stage the next issue overwrites (read in step kt - 1)
         __syncthreads();
         if (kt + T::NS - 1 < nk) issue(kt + T::NS - 1);
         const lds_char *st = (const lds_char *)lds + (kt % T::NS) * T::STAGE;
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
+        for (int ks = 0; ks < T::KS; ++ks) {
             u32x4 a[T::FM], b[T::FN];
 #pragma unroll
             for (int i = 0; i < T::FM; ++i)
@@ -545,6 +572,7 @@ template <class T, bool BF16>
 hipError_t launch16_direct(const Gemm16Args &a, hipStream_t stream)
 {
     const int64_t tiles = (int64_t)((a.M + T::BM - 1) / T::BM) * ((a.N + T::BN - 1) / T::BN);
+    if (a.K % T::BK) return hipErrorInvalidValue;
     if (tiles > 0x7fffffff) return hipErrorInvalidConfiguration;
     unsigned gx, gy;
     if (!grid_for(tiles, gx, gy)) return hipErrorInvalidConfiguration;
@@ -557,6 +585,16 @@ hipError_t launch16_direct(const Gemm16Args &a, hipStream_t stream)
 using D16L = Direct16<256, 256, 128, 64>;
 using D16M = Direct16<128, 128, 64, 64>;
 using D16S = Direct16<64, 64, 32, 32>;
+// K-steps of 64 in half the stages (the same LDS), for K % 64 == 0
+using D16L64 = Direct16<256, 256, 128, 64, 64, 2>;
+using D16M64 = Direct16<128, 128, 64, 64, 64, 2>;
+using D16S64 = Direct16<64, 64, 32, 32, 64, 2>;
+
+template <class T, class T64, bool BF16>
+hipError_t launch16_direct_k(const Gemm16Args &a, hipStream_t stream)
+{
+    return a.K % 64 == 0 ? launch16_direct<T64, BF16>(a, stream) : launch16_direct<T, BF16>(a, stream);
+}
 
 using T16L = Tile16<256, 256, 128, 64>;
 using T16M = Tile16<128, 128, 64, 64>;
@@ -573,9 +611,9 @@ const char *gemm16_config_name(int cfg)
     static const char *names[] = {"256x256x64 w128x64 pf1 (8 waves)", "128x128x64 w64x64 pf1 (4 waves)",
                                   "64x64x64 w32x32 pf1 (4 waves)", "128x128x64 w64x64 pf2 (4 waves)",
                                   "64x64x64 w32x32 pf2 (4 waves)",
-                                  "256x256x32 w128x64 direct-to-LDS 4 stages (8 waves)",
-                                  "128x128x32 w64x64 direct-to-LDS 4 stages (4 waves)",
-                                  "64x64x32 w32x32 direct-to-LDS 4 stages (4 waves)"};
+                                  "256x256x32 w128x64 direct-to-LDS 4 stages (8 waves; K % 64 == 0: K-steps of 64, 2 stages)",
+                                  "128x128x32 w64x64 direct-to-LDS 4 stages (4 waves; K % 64 == 0: K-steps of 64, 2 stages)",
+                                  "64x64x32 w32x32 direct-to-LDS 4 stages (4 waves; K % 64 == 0: K-steps of 64, 2 stages)"};
     return (cfg >= 0 && cfg < 8) ? names[cfg] : nullptr;
 }
 
@@ -614,13 +652,13 @@ hipError_t gemm16_launch(int cfg, bool bf16, const void *A, int64_t lda, const v
     // through registers
     case 5:
         if (!direct_ok(a)) return gemm16_launch(0, bf16, A, lda, B, ldb, C, ldc, M, N, K, stream);
-        return bf16 ? launch16_direct<D16L, true>(a, stream) : launch16_direct<D16L, false>(a, stream);
+        return bf16 ? launch16_direct_k<D16L, D16L64, true>(a, stream) : launch16_direct_k<D16L, D16L64, false>(a, stream);
     case 6:
         if (!direct_ok(a)) return gemm16_launch(3, bf16, A, lda, B, ldb, C, ldc, M, N, K, stream);
-        return bf16 ? launch16_direct<D16M, true>(a, stream) : launch16_direct<D16M, false>(a, stream);
+        return bf16 ? launch16_direct_k<D16M, D16M64, true>(a, stream) : launch16_direct_k<D16M, D16M64, false>(a, stream);
     default:
         if (!direct_ok(a)) return gemm16_launch(4, bf16, A, lda, B, ldb, C, ldc, M, N, K, stream);
-        return bf16 ? launch16_direct<D16S, true>(a, stream) : launch16_direct<D16S, false>(a, stream);
+        return bf16 ? launch16_direct_k<D16S, D16S64, true>(a, stream) : launch16_direct_k<D16S, D16S64, false>(a, stream);
     }
 }
 
