@@ -53,7 +53,7 @@ struct Im2colOperands {
     static constexpr bool kMatrixB = false;
     int H, W, R, S, sh, sw, ph, pw, dh, dw;
     int Q, PQ, HW, RS, CHW;
-    int s16, r16, c16;  // 16 rows of the im2col matrix: s += s16, r += r16, c += c16 (with carries)
+    int sK, rK, cK;  // one K-step (BK rows) of the im2col matrix: s += sK, r += rK, c += cK (with carries)
     int64_t KPQ;
 
     // Output column (n, p, q): input row h0 and column w0 under the filter's first
@@ -178,7 +178,7 @@ __global__ __launch_bounds__(T::NT) void conv_direct_kernel(GemmArgs p, Im2colOp
 #pragma unroll
     for (int i = 0; i < T::A16; ++i) {
         const int ob = (T::A16 * w + i) * 1024 + 16 * lane;
-        const int row = ob / 64, chunk = (ob % 64) / 16;
+        const int row = ob / T::A_ROW, chunk = (ob % T::A_ROW) / 16;
         asrc[i] = p.A + (int64_t)min(m0 + row, p.M - 1) * p.lda + 4 * (chunk ^ swz_a<T>(row));
     }
     // B: the wave loads rows ROWS * w .. ROWS * w + ROWS - 1 of each K-step, PER_ROW loads
@@ -191,7 +191,7 @@ __global__ __launch_bounds__(T::NT) void conv_direct_kernel(GemmArgs p, Im2colOp
         const int col = n0 + 4 * ((slot >> 2) ^ swz_b<T>(krow0)) + (slot & 3);
         cols[h] = o.columns_of(p, col);
     }
-    static_assert(8 % ROWS == 0, "a wave's rows lie in one 8-row half: they share swz_b");
+    static_assert((T::BK / 2) % ROWS == 0, "a wave's rows lie in one half of the K-step: they share swz_b");
 
     const unsigned lds0 = (unsigned)(uintptr_t)(lds_char *)lds;
     // (c, r, s) of row krow0 of the next K-step to issue (one division, here)
@@ -207,7 +207,7 @@ __global__ __launch_bounds__(T::NT) void conv_direct_kernel(GemmArgs p, Im2colOp
 #pragma unroll
             for (int i = 0; i < T::A4; ++i) {
                 const int ob = (T::A4 * w + i) * 256 + 4 * lane;
-                const int row = ob / 64, slot = (ob % 64) / 4;
+                const int row = ob / T::A_ROW, slot = (ob % T::A_ROW) / 4;
                 const int k = k0 + 4 * ((slot >> 2) ^ swz_a<T>(row)) + (slot & 3);
                 const float *src = k < p.K ? p.A + (int64_t)min(m0 + row, p.M - 1) * p.lda + k : zeros;
                 load_to_lds<4>(st + (T::A4 * w + i) * 256, src);
@@ -219,14 +219,14 @@ __global__ __launch_bounds__(T::NT) void conv_direct_kernel(GemmArgs p, Im2colOp
         int r = fr, s = fs;
         int dy = r * o.dh, dx = s * o.dw;
         int rowoff = fc * o.HW + dy * o.W + dx;
-        // advance the first row by one K-step (16 rows) for the next issue
-        fs += o.s16;
+        // advance the first row by one K-step (BK rows) for the next issue
+        fs += o.sK;
         const int cs = fs >= o.S;
         fs -= cs ? o.S : 0;
-        fr += o.r16 + cs;
+        fr += o.rK + cs;
         const int cr = fr >= o.R;
         fr -= cr ? o.R : 0;
-        fc += o.c16 + cr;
+        fc += o.cK + cr;
 #pragma unroll
         for (int rr = 0; rr < ROWS; ++rr) {
 #pragma unroll
@@ -320,6 +320,9 @@ const ConvConfig kConvConfigs[] = {
     {"64x64x64 w32x32 pf2 ks1 (4 waves)", &launch_im2col<T64x64k64p2>, 3, 64, 64, 4, 2, 90, 64},
     {"64x64x64 w32x32 pf2 ks2 (8 waves)", &launch_im2col<T64x64k64p2s2>, 4, 64, 64, 8, 2, 86, 64},
     {"128x64x64 w64x32 pf1 ks2 (8 waves)", &launch_im2col<T128x64k64s2>, 5, 128, 64, 8, 1, 80, 64},
+    // K-steps of 16 in 4 stages: K-steps of 32 in 2 stages (the GEMM's choice where K % 32
+    // == 0) measured +2-4% on the 3 x 3 layers but -3% on the 7 x 7 input layer (C R S =
+    // 147), which is the one these tiles are chosen for
     {"64x64x16 w32x32 direct-to-LDS gather 4 stages (4 waves)", &launch_conv_direct<DirectF32<64, 64, 32, 32, 4, false>>,
      13, 64, 64, 4, 5, 85, 16},
     {"128x128x16 w64x64 direct-to-LDS gather 4 stages (4 waves)",
@@ -436,9 +439,10 @@ hipError_t conv_launch(int cfg, const ConvArgs &a, hipStream_t stream)
     o.HW = (int)HW;
     o.RS = (int)(a.R * a.S);
     o.CHW = (int)CHW;
-    o.s16 = (int)(16 % a.S);
-    o.r16 = (int)((16 / a.S) % a.R);
-    o.c16 = (int)(16 / (a.R * a.S));
+    const int bk = kConvConfigs[cfg].bk;  // the direct gather steps (c, r, s) by whole K-steps
+    o.sK = (int)(bk % a.S);
+    o.rK = (int)((bk / a.S) % a.R);
+    o.cK = (int)(bk / (a.R * a.S));
     o.KPQ = KPQ;
     // images per launch: x offsets below 2^30, product columns below 2^31
     int64_t per = kMaxRun / CHW;
