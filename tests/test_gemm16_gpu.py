@@ -153,6 +153,34 @@ def test_strided_unaligned(dev, fmt, cfg, lds, offs):
     assert r, str(r)
 
 
+@pytest.mark.parametrize("fmt", list(FORMATS))
+@pytest.mark.parametrize("cfg", [5, 6, 7])
+@pytest.mark.parametrize("K", [96, 192])
+def test_direct_strided_views(dev, fmt, cfg, K):
+    """The direct pipeline addresses its loads from the tile's corner plus a fixed offset
+    per lane: leading dimensions beyond the width (multiples of 8, as it requires) with
+    NaN around the views, K-steps of 32 (K = 96) and 64 (K = 192)."""
+    M, N = 300, 264
+    A = wl.random_matrix(53, M, K, "int4")
+    B = wl.random_matrix(54, K, N, "int4")
+    C, Af, Bf = run(A, B, fmt, dev, cfg, lda=K + 24, ldb=N + 40, offs=(8, 16))
+    C64, _ = oracle.gemm(Af, Bf)
+    r = verify.exact(C, C64)
+    assert r, str(r)
+
+
+@pytest.mark.parametrize("cfg", [5, 6, 7])
+def test_direct_huge_leading_dimension(dev, cfg):
+    """lda of 9M elements: 255 rows of it exceed the 32-bit lane offsets of the direct
+    pipeline, so the register-staged tile of the same size runs; still exact."""
+    A = wl.random_matrix(55, 3, 64, "int4")
+    B = wl.random_matrix(56, 64, 64, "int4")
+    C, Af, Bf = run(A, B, "bf16", dev, cfg, lda=9_000_000)
+    C64, _ = oracle.gemm(Af, Bf)
+    r = verify.exact(C, C64)
+    assert r, str(r)
+
+
 def test_k_zero(dev):
     for fmt in FORMATS:
         tdtype = FORMATS[fmt][2]

@@ -196,6 +196,41 @@ def test_strided_poisoned_views(dev, cfg, offsets):
     assert outside_untouched(Cbuf, M, N)
 
 
+@pytest.mark.parametrize("cfg", [10, 11, 12, 13])
+@pytest.mark.parametrize("K", [96, 112])
+@pytest.mark.parametrize("offsets", [(0, 0), (1, 2)])
+def test_direct_lean_strided_poisoned_views(dev, cfg, K, offsets):
+    """The lean direct builds (K % 16 == 0, N % 4 == 0; K-steps of 32 at K = 96, of 16 at
+    K = 112) address their loads from the tile's corner plus a fixed offset per lane:
+    leading dimensions beyond the width with NaN in every gap and starts that are only
+    4-byte aligned must still read only the matrices."""
+    M, N = 300, 264
+    A = wl.random_matrix(41, M, K, "int4")
+    B = wl.random_matrix(42, K, N, "int4")
+    _, Av = strided_on_device(A, K + 5, dev, offset=offsets[0])
+    _, Bv = strided_on_device(B, N + 12, dev, offset=offsets[1])
+    Cbuf, Cv = nan_output(M, N, N + 7, dev)
+    mm.gemm(Av, Bv, out=Cv, config=cfg)
+    torch.cuda.synchronize()
+    assert_exact(Cv.cpu().numpy(), A, B)
+    assert outside_untouched(Cbuf, M, N)
+
+
+@pytest.mark.parametrize("cfg", [10, 11, 12, 13])
+def test_direct_huge_leading_dimension(dev, cfg):
+    """lda of 5M floats: 255 rows of it exceed the 32-bit lane offsets the lean builds
+    use, so those shapes take the general build (or, for the 256 x 256 tile, the
+    register-staged one); the result is still exact."""
+    M, N, K, lda = 3, 64, 32, 5_000_000
+    A = wl.random_matrix(43, M, K, "int4")
+    B = wl.random_matrix(44, K, N, "int4")
+    _, Av = strided_on_device(A, lda, dev)
+    Bd = to_device(B, dev)
+    C = mm.gemm(Av, Bd, config=cfg)
+    torch.cuda.synchronize()
+    assert_exact(C.cpu().numpy(), A, B)
+
+
 @pytest.mark.parametrize("cfg", CONFIGS)
 def test_k_zero_writes_zeros_and_empty_is_noop(dev, cfg):
     Cbuf, Cv = nan_output(37, 45, 50, dev)

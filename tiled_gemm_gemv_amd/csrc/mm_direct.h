@@ -81,6 +81,17 @@ __device__ __forceinline__ void load_to_lds(unsigned lds_addr, const float *src)
                      :: "s"(__builtin_amdgcn_readfirstlane(lds_addr)), "v"(src) : "memory");
 }
 
+// 16 bytes per lane from base + voff into LDS at lds_addr + 16 * lane: base and lds_addr
+// wave-uniform (scalar registers), voff the lane's byte offset. With the base stepped by
+// scalar arithmetic and fixed lane offsets, a load takes no vector instruction (the
+// pointer form above needs a 64-bit address add and a readfirstlane per load; measured
+// 1.7% of the 256 x 256 tile's time at the projection shape).
+__device__ __forceinline__ void load_to_lds_s16(unsigned lds_addr, const float *base, unsigned voff)
+{
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+                 :: "s"(lds_addr), "v"(voff), "s"(base) : "memory");
+}
+
 template <int N>
 __device__ __forceinline__ void wait_vmcnt()
 {

@@ -34,7 +34,7 @@ struct ConfigEntry {
     int wg_per_cu;   // workgroups a CU holds (registers and LDS)
     double tflops;   // measured on large shapes, for the choice below
     int bk;          // K-step depth
-    int fill_waves = 8;  // waves per CU at which the tile runs at `tflops` (tile_time)
+    double fill_waves = 8;  // waves per CU at which the tile runs at `tflops` (tile_time)
 };
 
 // name: BMxBNxBK, wave tile, prefetch depth, waves per output block (K split).
@@ -49,10 +49,10 @@ const ConfigEntry kConfigs[] = {
     {"narrow 16x64 (16x16x4 MFMA), K over 4 waves, 16/NB chunks", &gemm_skinny_launch<4, 16>, 16, 64, 4, 1, 0, 16},
     {"narrow 16x64 (16x16x4 MFMA), K over 16 waves, 4/NB chunks", &gemm_skinny_launch<16, 4>, 16, 64, 16, 1, 0, 16},
     {"columns <= 4: one wave per row, B rounds in LDS (8 x 4 per workgroup)", &gemm_cols_launch, 8, 4, 4, 1, 0, 16},
-    {"256x256x32 w128x64 direct-to-LDS 2 stages (8 waves; K % 32 != 0: K-steps of 16, 4 stages)", &direct_or_staged_256, 256, 256, 8, 1, 143, 32, 4},
-    {"128x128x16 w64x64 direct-to-LDS 4 stages (4 waves; K % 32 == 0: K-steps of 32, 2 stages)", &direct<DirectTile::T128>, 128, 128, 4, 2, 135, 16, 4},
-    {"64x64x16 w32x32 direct-to-LDS 8 stages (4 waves; K % 32 == 0: K-steps of 32, 4 stages)", &direct<DirectTile::T64S8>, 64, 64, 4, 2, 108, 16},
-    {"64x64x16 w32x32 direct-to-LDS 4 stages (4 waves; K % 32 == 0: K-steps of 32, 2 stages)", &direct<DirectTile::T64S4>, 64, 64, 4, 5, 116, 16},
+    {"256x256x32 w128x64 direct-to-LDS 2 stages (8 waves; K % 32 != 0: K-steps of 16, 4 stages)", &direct_or_staged_256, 256, 256, 8, 1, 146, 32, 4},
+    {"128x128x16 w64x64 direct-to-LDS 4 stages (4 waves; K % 32 == 0: K-steps of 32, 2 stages)", &direct<DirectTile::T128>, 128, 128, 4, 2, 148, 16, 5},
+    {"64x64x16 w32x32 direct-to-LDS 8 stages (4 waves; K % 32 == 0: K-steps of 32, 4 stages)", &direct<DirectTile::T64S8>, 64, 64, 4, 2, 136, 16, 5.5},
+    {"64x64x16 w32x32 direct-to-LDS 4 stages (4 waves; K % 32 == 0: K-steps of 32, 2 stages)", &direct<DirectTile::T64S4>, 64, 64, 4, 5, 140, 16, 5.5},
 };
 constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
 

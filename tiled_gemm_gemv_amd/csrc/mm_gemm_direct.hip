@@ -50,9 +50,30 @@ __global__ __launch_bounds__(T::NT) void gemm_f32_direct_kernel(GemmArgs p)
     p.B += blockIdx.z * p.sb;
     p.C += blockIdx.z * p.sc;
 
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave index, in a scalar register
     const int wm0 = (w / (T::BN / T::WN)) * T::WM, wn0 = (w % (T::BN / T::WN)) * T::WN;
     const int nk = (p.K + T::BK - 1) / T::BK;
+
+    // Lean builds address their 16-byte lanes from the tile's corner at the K-step (a
+    // scalar base) plus a fixed byte offset per lane; direct_f32_wide_ok keeps those
+    // offsets below 2^32.
+    unsigned aoff[T::A16], boff[T::B16];
+    if constexpr (!T::GEN) {
+#pragma unroll
+        for (int i = 0; i < T::A16; ++i) {
+            const int o = (T::A16 * w + i) * 1024 + 16 * lane;
+            const int row = o / T::A_ROW, chunk = (o % T::A_ROW) / 16;
+            aoff[i] = (unsigned)(((int64_t)(min(m0 + row, p.M - 1) - m0) * p.lda + 4 * (chunk ^ swz_a<T>(row))) * 4);
+        }
+#pragma unroll
+        for (int i = 0; i < T::B16; ++i) {
+            const int o = (T::B16 * w + i) * 1024 + 16 * lane;
+            const int krow = o / T::B_ROW, chunk = (o % T::B_ROW) / 16;
+            const int col = n0 + 4 * (chunk ^ swz_b<T>(krow));  // N % 4 == 0: min(col, N - 4) >= n0
+            boff[i] = (unsigned)(((int64_t)krow * p.ldb + (min(col, p.N - 4) - n0)) * 4);
+        }
+    }
 
     // Each load's lane lands at a fixed panel byte; the element(s) stored there are this
     // lane's source. 16-byte lanes of full K-steps: asrc/bsrc address them at k0 = 0.
@@ -113,6 +134,16 @@ __global__ __launch_bounds__(T::NT) void gemm_f32_direct_kernel(GemmArgs p)
         auto issue_full = [&](int kt) {
             const unsigned st = lds0 + (kt % T::NS) * T::STAGE;
             const int k0 = kt * T::BK;
+            if constexpr (!T::GEN) {
+                const float *abase = p.A + (int64_t)m0 * p.lda + k0;
+                const float *bbase = p.B + (int64_t)k0 * p.ldb + n0;
+#pragma unroll
+                for (int i = 0; i < T::A16; ++i) load_to_lds_s16(st + (T::A16 * w + i) * 1024, abase, aoff[i]);
+#pragma unroll
+                for (int i = 0; i < T::B16; ++i)
+                    load_to_lds_s16(st + T::A_BYTES + (T::B16 * w + i) * 1024, bbase, boff[i]);
+                return;
+            }
 #pragma unroll
             for (int i = 0; i < T::A16; ++i) load_to_lds<16>(st + (T::A16 * w + i) * 1024, asrc[i] + k0);
             if constexpr (WIDE) {
@@ -194,7 +225,11 @@ hipError_t launch_direct(const GemmArgs &a, hipStream_t stream)
 
 bool direct_f32_wide_ok(const GemmArgs &a)
 {
-    return a.K % 16 == 0 && a.N >= 4 && a.N % 4 == 0;
+    // the lean builds' per-lane byte offsets (below 256 rows of A, 32 rows of B and 256
+    // columns from the tile's corner) must fit 32 bits
+    constexpr int64_t kOffMax = int64_t(1) << 32;
+    return a.K % 16 == 0 && a.N >= 4 && a.N % 4 == 0 && 4 * (255 * a.lda + 32) < kOffMax &&
+           4 * (31 * a.ldb + 256) < kOffMax;
 }
 
 namespace {

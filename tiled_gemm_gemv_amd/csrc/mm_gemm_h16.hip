@@ -414,13 +414,14 @@ __device__ __forceinline__ int swz_b16(int krow)
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) char lds_char;
 
-// 16 bytes per lane from src into LDS at lds_addr + 16 * lane (lds_addr wave-uniform).
-// The s_nop is the one wait state a global load with LDS = 1 needs after an SALU write of
-// M0 (the hazard recognizer does not look inside an asm string).
-__device__ __forceinline__ void load_to_lds(unsigned lds_addr, const unsigned short *src)
+// 16 bytes per lane from base + voff into LDS at lds_addr + 16 * lane (lds_addr and base
+// wave-uniform, in scalar registers; voff the lane's byte offset), so that a load takes no
+// vector instruction. The s_nop is the one wait state a global load with LDS = 1 needs
+// after an SALU write of M0 (the hazard recognizer does not look inside an asm string).
+__device__ __forceinline__ void load_to_lds_s(unsigned lds_addr, const unsigned short *base, unsigned voff)
 {
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
-                 :: "s"(__builtin_amdgcn_readfirstlane(lds_addr)), "v"(src) : "memory");
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+                 :: "s"(lds_addr), "v"(voff), "s"(base) : "memory");
 }
 
 template <int N>
@@ -455,36 +456,38 @@ __global__ __launch_bounds__(T::NT) void gemm_h16_direct_kernel(Gemm16Args p)
     tile_of_block16((int)bid, (int)tiles, tiles_m, tiles_n, tm, tn);
     const int m0 = tm * T::BM, n0 = tn * T::BN;
 
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave index, in a scalar register
     const int wm0 = (w / (T::BN / T::WN)) * T::WM, wn0 = (w % (T::BN / T::WN)) * T::WN;
     const int nk = p.K / T::BK;
 
-    // this lane's sources for the wave's loads of every K-step (advanced by BK per step)
-    const unsigned short *asrc[T::A_LOADS];
-    const unsigned short *bsrc[T::B_LOADS];
+    // this lane's byte offsets from the tile's corner at the K-step (the loads' scalar
+    // base, advanced by BK per step); direct_ok keeps them below 2^32
+    unsigned aoff[T::A_LOADS], boff[T::B_LOADS];
 #pragma unroll
     for (int i = 0; i < T::A_LOADS; ++i) {
         const int row = T::A_ROWS_PER_LOAD * (T::A_LOADS * w + i) + lane / T::A_CPR;
         const int chunk = (lane % T::A_CPR) ^ swz_a16<T>(row);
-        asrc[i] = p.A + (int64_t)min(m0 + row, p.M - 1) * p.lda + 8 * chunk;
+        aoff[i] = (unsigned)(((int64_t)(min(m0 + row, p.M - 1) - m0) * p.lda + 8 * chunk) * 2);
     }
 #pragma unroll
     for (int i = 0; i < T::B_LOADS; ++i) {
         constexpr int CPR = T::B_ROW / 16;  // 16-byte chunks per B row
         const int krow = T::B_ROWS_PER_LOAD * (T::B_LOADS * w + i) + lane / CPR;
         const int chunk = (lane % CPR) ^ swz_b16<T>(krow);
-        bsrc[i] = p.B + (int64_t)krow * p.ldb + min(n0 + 8 * chunk, p.N - 8);
+        // N % 8 == 0: min(n0 + 8 chunk, N - 8) >= n0
+        boff[i] = (unsigned)(((int64_t)krow * p.ldb + (min(n0 + 8 * chunk, p.N - 8) - n0)) * 2);
     }
     const unsigned lds0 = (unsigned)(uintptr_t)(lds_char *)lds;  // LDS byte offset of the array
     auto issue = [&](int kt) {
         const unsigned st = lds0 + (kt % T::NS) * T::STAGE;
+        const unsigned short *abase = p.A + (int64_t)m0 * p.lda + (int64_t)kt * T::BK;
+        const unsigned short *bbase = p.B + (int64_t)kt * T::BK * p.ldb + n0;
 #pragma unroll
-        for (int i = 0; i < T::A_LOADS; ++i)
-            load_to_lds(st + (T::A_LOADS * w + i) * 1024, asrc[i] + (int64_t)kt * T::BK);
+        for (int i = 0; i < T::A_LOADS; ++i) load_to_lds_s(st + (T::A_LOADS * w + i) * 1024, abase, aoff[i]);
 #pragma unroll
         for (int i = 0; i < T::B_LOADS; ++i)
-            load_to_lds(st + T::A_BYTES + (T::B_LOADS * w + i) * 1024,
-                        bsrc[i] + (int64_t)kt * T::BK * p.ldb);
+            load_to_lds_s(st + T::A_BYTES + (T::B_LOADS * w + i) * 1024, bbase, boff[i]);
     };
 
     // operand addresses inside a stage (bytes), for the 16-k MFMA steps of a K-step
@@ -564,8 +567,12 @@ __global__ __launch_bounds__(T::NT) void gemm_h16_direct_kernel(Gemm16Args p)
 // The direct pipeline's requirements (see above).
 bool direct_ok(const Gemm16Args &a)
 {
+    // the per-lane byte offsets from a tile's corner (below 256 rows of A, 64 rows of B
+    // and 256 columns) must fit 32 bits
+    constexpr int64_t kOffMax = int64_t(1) << 32;
     return a.K % 32 == 0 && a.N >= 8 && a.N % 8 == 0 && a.lda % 8 == 0 && a.ldb % 8 == 0 &&
-           (uintptr_t)a.A % 16 == 0 && (uintptr_t)a.B % 16 == 0;
+           (uintptr_t)a.A % 16 == 0 && (uintptr_t)a.B % 16 == 0 && 2 * (255 * a.lda + 64) < kOffMax &&
+           2 * (63 * a.ldb + 256) < kOffMax;
 }
 
 template <class T, bool BF16>

@@ -58,13 +58,13 @@ struct GemvArgs {
 
 // Time model for choosing a tile shape (arbitrary units): a CU computes a BM x BN tile
 // at `tflops` when fill_waves or more waves share it, and proportionally slower with
-// fewer (latency is then exposed; 8 for register-staged tiles, 4 for the 256 x 256 and
-// 128 x 128 tiles whose panels the LDS DMA loads: one workgroup of 4 waves of the
-// latter measured 86% of its full rate, at 2048^3). The busiest CU gets ceil(tiles / 256) tiles; it runs them in
+// fewer (latency is then exposed; 8 for register-staged tiles, fewer for the tiles whose
+// panels the LDS DMA loads: one 4-wave workgroup per CU of the 128 x 128 direct tile
+// measured about 80% of its full rate, of the 64 x 64 ones about 70%). The busiest CU gets ceil(tiles / 256) tiles; it runs them in
 // sets of at most wg_per_cu concurrent workgroups, and a last, smaller set runs at its
 // own occupancy.
 inline double tile_time(int64_t tiles, int bm, int bn, int waves, int wg_per_cu, double tflops,
-                        int fill_waves = 8)
+                        double fill_waves = 8)
 {
     constexpr int64_t kCus = 256;
     const int64_t t = (tiles + kCus - 1) / kCus;
