@@ -22,6 +22,11 @@
 //     C elements that are not stored. A partial last K-step (K % 16 != 0) loads both
 //     panels with 4-byte lanes at k clamped to K - 1, then the workgroup writes zeros
 //     over the k >= K entries of both panels between two barriers.
+//   * Addressing. Lean builds (K % 16 == 0, N % 4 == 0, leading dimensions that keep the
+//     offsets below 2^32) take the load's scalar-base form: the tile's corner at the
+//     K-step in scalar registers plus a byte offset per lane fixed for the whole K loop,
+//     so a load needs no vector instruction. General builds keep a 64-bit pointer per
+//     lane.
 //   * One barrier per K-step, after an explicit s_waitcnt vmcnt that counts the loads of
 //     the steps issued after it (a partial last step issues more loads than a full one,
 //     which only makes that count conservative). The loads are issued from inline asm
@@ -75,8 +80,9 @@ __global__ __launch_bounds__(T::NT) void gemm_f32_direct_kernel(GemmArgs p)
         }
     }
 
-    // Each load's lane lands at a fixed panel byte; the element(s) stored there are this
-    // lane's source. 16-byte lanes of full K-steps: asrc/bsrc address them at k0 = 0.
+    // General builds: each load's lane lands at a fixed panel byte; the element(s) stored
+    // there are this lane's source. 16-byte lanes of full K-steps: asrc/bsrc address them
+    // at k0 = 0 (unused, and dropped by the compiler, in lean builds).
     const float *asrc[T::A16];
     const float *bsrc[T::B16];
 #pragma unroll
