@@ -401,6 +401,17 @@ def main():
         r = verify.within_tol(yvs[i].cpu().numpy(), y64, s64, 1e-5)
         gemv_ok = gemv_ok and bool(r)
     cpu_tflops = rl.gemm_flops(len(rows), N, K) / t_cpu / 1e12
+    # the oracle on one thread: the small GEMM (128^3, best of 5) and the full GEMV
+    w1 = wl.WORKLOADS["gemm128"]
+    A1, B1 = wl.gemm_inputs(w1)
+    t1g = []
+    for _ in range(5):
+        tc = time.perf_counter()
+        oracle.gemm(A1, B1, threads=1)
+        t1g.append(time.perf_counter() - tc)
+    tc = time.perf_counter()
+    oracle.gemv(Av_h, xv_h, threads=1)
+    t1v = time.perf_counter() - tc
 
     result = {
         "metric": METRIC,
@@ -465,6 +476,12 @@ def main():
             "kind": "oracle",
             "sample": f"{len(rows)} sampled rows (all 14336 columns, K=4096) of the projection "
                       f"GEMM, fp64 accumulation, {t_cpu:.2f} s on {cpu_model()}",
+        },
+        "cpu_single_thread": {
+            "gemm128": {"value": round(rl.gemm_flops(128, 128, 128) / min(t1g) / 1e9, 3), "unit": "GFLOP/s",
+                        "ms": round(min(t1g) * 1e3, 3)},
+            "gemv4096": {"value": round(gemv_bytes / t1v / 1e9, 3), "unit": "GB/s", "ms": round(t1v * 1e3, 3)},
+            "kind": "oracle", "cores": 1,
         },
         "verified": bool(gemm_check) and gemv_ok,
     }
