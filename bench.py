@@ -443,6 +443,7 @@ def main():
         "gemm": {
             "kernel_ms_mean": round(float(np.mean(gemm_ms)), 4),
             "kernel_ms_min": round(float(np.min(gemm_ms)), 4),
+            "kernel_ms_median": round(float(np.median(gemm_ms)), 4),
             "tflops": round(gemm_tflops, 3),
             "frac_fp32_mfma_peak": round(gemm_tflops / (rl.MI355X_FP32_MFMA_PEAK / 1e12), 4),
             "algorithmic_bytes": rl.gemm_algorithmic_bytes(M, N, K),
@@ -476,6 +477,7 @@ def main():
             "kind": "oracle",
             "sample": f"{len(rows)} sampled rows (all 14336 columns, K=4096) of the projection "
                       f"GEMM, fp64 accumulation, {t_cpu:.2f} s on {cpu_model()}",
+            "full_matrix_s_extrapolated": round(t_cpu * M / len(rows), 1),
         },
         "cpu_single_thread": {
             "gemm128": {"value": round(rl.gemm_flops(128, 128, 128) / min(t1g) / 1e9, 3), "unit": "GFLOP/s",
