@@ -38,9 +38,12 @@
 namespace mm {
 namespace {
 
-template <class T>
+// SB: address the 16-byte lanes of full K-steps from a scalar base (the host checked that
+// the per-lane offsets fit 32 bits; lean builds always do).
+template <class T, bool SB>
 __global__ __launch_bounds__(T::NT) void gemm_f32_direct_kernel(GemmArgs p)
 {
+    constexpr bool SADDR = !T::GEN || SB;
     __shared__ __attribute__((aligned(1024))) char lds[T::NS * T::STAGE];
     const int tiles_m = (p.M + T::BM - 1) / T::BM;
     const int tiles_n = (p.N + T::BN - 1) / T::BN;
@@ -60,11 +63,12 @@ __global__ __launch_bounds__(T::NT) void gemm_f32_direct_kernel(GemmArgs p)
     const int wm0 = (w / (T::BN / T::WN)) * T::WM, wn0 = (w % (T::BN / T::WN)) * T::WN;
     const int nk = (p.K + T::BK - 1) / T::BK;
 
-    // Lean builds address their 16-byte lanes from the tile's corner at the K-step (a
-    // scalar base) plus a fixed byte offset per lane; direct_f32_wide_ok keeps those
-    // offsets below 2^32.
+    // The 16-byte lanes of full K-steps are addressed from the tile's corner at the K-step
+    // (a scalar base) plus a fixed byte offset per lane; direct_f32_offsets_fit keeps those
+    // offsets below 2^32. (B's are used only by tiles whose chunks all take 16-byte lanes,
+    // for which min(col, N - 4) >= n0.)
     unsigned aoff[T::A16], boff[T::B16];
-    if constexpr (!T::GEN) {
+    if constexpr (SADDR) {
 #pragma unroll
         for (int i = 0; i < T::A16; ++i) {
             const int o = (T::A16 * w + i) * 1024 + 16 * lane;
@@ -80,9 +84,9 @@ __global__ __launch_bounds__(T::NT) void gemm_f32_direct_kernel(GemmArgs p)
         }
     }
 
-    // General builds: each load's lane lands at a fixed panel byte; the element(s) stored
-    // there are this lane's source. 16-byte lanes of full K-steps: asrc/bsrc address them
-    // at k0 = 0 (unused, and dropped by the compiler, in lean builds).
+    // Without the scalar base: each load's lane lands at a fixed panel byte; the
+    // element(s) stored there are this lane's source. 16-byte lanes of full K-steps:
+    // asrc/bsrc address them at k0 = 0 (unused, and dropped by the compiler, with it).
     const float *asrc[T::A16];
     const float *bsrc[T::B16];
 #pragma unroll
@@ -140,19 +144,20 @@ __global__ __launch_bounds__(T::NT) void gemm_f32_direct_kernel(GemmArgs p)
         auto issue_full = [&](int kt) {
             const unsigned st = lds0 + (kt % T::NS) * T::STAGE;
             const int k0 = kt * T::BK;
-            if constexpr (!T::GEN) {
+            if constexpr (SADDR) {
                 const float *abase = p.A + (int64_t)m0 * p.lda + k0;
-                const float *bbase = p.B + (int64_t)k0 * p.ldb + n0;
 #pragma unroll
                 for (int i = 0; i < T::A16; ++i) load_to_lds_s16(st + (T::A16 * w + i) * 1024, abase, aoff[i]);
+            } else {
+#pragma unroll
+                for (int i = 0; i < T::A16; ++i) load_to_lds<16>(st + (T::A16 * w + i) * 1024, asrc[i] + k0);
+            }
+            if constexpr (WIDE && SADDR) {
+                const float *bbase = p.B + (int64_t)k0 * p.ldb + n0;
 #pragma unroll
                 for (int i = 0; i < T::B16; ++i)
                     load_to_lds_s16(st + T::A_BYTES + (T::B16 * w + i) * 1024, bbase, boff[i]);
-                return;
-            }
-#pragma unroll
-            for (int i = 0; i < T::A16; ++i) load_to_lds<16>(st + (T::A16 * w + i) * 1024, asrc[i] + k0);
-            if constexpr (WIDE) {
+            } else if constexpr (WIDE) {
 #pragma unroll
                 for (int i = 0; i < T::B16; ++i)
                     load_to_lds<16>(st + T::A_BYTES + (T::B16 * w + i) * 1024, bsrc[i] + (int64_t)k0 * p.ldb);
@@ -214,7 +219,7 @@ __global__ __launch_bounds__(T::NT) void gemm_f32_direct_kernel(GemmArgs p)
     direct_store<T>(p, m0, n0, wm0, wn0, lane, acc, [](int gn) { return gn; });
 }
 
-template <class T>
+template <class T, bool SB = true>
 hipError_t launch_direct(const GemmArgs &a, hipStream_t stream)
 {
     const int64_t tiles = (int64_t)((a.M + T::BM - 1) / T::BM) * ((a.N + T::BN - 1) / T::BN);
@@ -223,19 +228,23 @@ hipError_t launch_direct(const GemmArgs &a, hipStream_t stream)
     if (!grid_for(tiles, gx, gy)) return hipErrorInvalidConfiguration;
     GemmArgs arg = a;
     void *args[] = {&arg};
-    return hipLaunchKernel(reinterpret_cast<const void *>(&gemm_f32_direct_kernel<T>),
+    return hipLaunchKernel(reinterpret_cast<const void *>(&gemm_f32_direct_kernel<T, SB>),
                            dim3(gx, gy, (unsigned)a.batch), dim3(T::NT), args, 0, stream);
 }
 
 }  // namespace
 
+// The per-lane byte offsets from a tile's corner (below 256 rows of A, 32 rows of B and
+// 256 columns) fit 32 bits.
+static bool direct_f32_offsets_fit(const GemmArgs &a)
+{
+    constexpr int64_t kOffMax = int64_t(1) << 32;
+    return 4 * (255 * a.lda + 32) < kOffMax && 4 * (31 * a.ldb + 256) < kOffMax;
+}
+
 bool direct_f32_wide_ok(const GemmArgs &a)
 {
-    // the lean builds' per-lane byte offsets (below 256 rows of A, 32 rows of B and 256
-    // columns from the tile's corner) must fit 32 bits
-    constexpr int64_t kOffMax = int64_t(1) << 32;
-    return a.K % 16 == 0 && a.N >= 4 && a.N % 4 == 0 && 4 * (255 * a.lda + 32) < kOffMax &&
-           4 * (31 * a.ldb + 256) < kOffMax;
+    return a.K % 16 == 0 && a.N >= 4 && a.N % 4 == 0 && direct_f32_offsets_fit(a);
 }
 
 namespace {
@@ -250,8 +259,9 @@ hipError_t launch_lean_or_general(const GemmArgs &a, hipStream_t stream)
 {
     if (direct_f32_wide_ok(a) && a.K % 32 == 0)
         return launch_direct<DirectF32<BM, BN, WM, WN, NS / 2, false, 32>>(a, stream);
-    return direct_f32_wide_ok(a) ? launch_direct<DirectF32<BM, BN, WM, WN, NS, false>>(a, stream)
-                                 : launch_direct<DirectF32<BM, BN, WM, WN, NS, true>>(a, stream);
+    if (direct_f32_wide_ok(a)) return launch_direct<DirectF32<BM, BN, WM, WN, NS, false>>(a, stream);
+    return direct_f32_offsets_fit(a) ? launch_direct<DirectF32<BM, BN, WM, WN, NS, true>, true>(a, stream)
+                                     : launch_direct<DirectF32<BM, BN, WM, WN, NS, true>, false>(a, stream);
 }
 
 }  // namespace
