@@ -632,6 +632,30 @@ def sweep(kind, torch, mm, dev):
             print(f"{batch:6d} {M:6d} {N:6d} {K:6d} {flop / tb / 1e9:9.1f} {flop / ts / 1e9:9.1f}",
                   flush=True)
             del A, B, C
+        print("# few output tiles: mm_gemm_f32 vs mm_gemm_f32_ws (K split over 2-8 chunks of the "
+              "64 x 64 tile, partial products in a workspace, then a sum kernel), TFLOP/s")
+        print(f"{'M':>6s} {'N':>6s} {'K':>6s} {'chunks':>7s} {'gemm':>9s} {'gemm_ws':>9s}")
+        for M, N, K in ((4096, 32, 4096), (4096, 48, 4096), (4096, 64, 4096), (4096, 128, 4096),
+                        (4096, 256, 4096), (1024, 128, 4096), (8192, 64, 8192), (1024, 64, 8192)):
+            A = torch.randn(M, K, device=dev)
+            B = torch.randn(K, N, device=dev)
+            C = torch.empty(M, N, device=dev)
+            ws = mm.gemm_workspace(M, N, K, dev)
+            wsb = 0 if ws is None else ws.numel()
+            chunks = wsb // (4 * M * N)
+            flop = rl.gemm_flops(M, N, K)
+            reps = max(3, min(200, int(2e11 / flop)))
+
+            def plain(i, st):
+                mm.mm_gemm_f32(M, N, K, A, K, B, N, C, N, st)
+
+            def split(i, st):
+                mm.mm_gemm_f32_ws(M, N, K, A, K, B, N, C, N, ws, wsb, st)
+            tp = burst_time_ms(torch, plain, reps)
+            tw = burst_time_ms(torch, split, reps)
+            print(f"{M:6d} {N:6d} {K:6d} {chunks:7d} {flop / tp / 1e9:9.1f} {flop / tw / 1e9:9.1f}",
+                  flush=True)
+            del A, B, C, ws
     elif kind == "h16":
         shapes = [(w.M, w.N, w.K, w.name) for w in wl.WORKLOADS.values() if w.op == "gemm"]
         shapes += [(2048, 2048, 2048, ""), (4096, 4096, 4096, ""), (8192, 8192, 8192, "")]

@@ -166,6 +166,34 @@ int mm_gemm_f32_batched(int64_t batch, int64_t M, int64_t N, int64_t K,
                         float *C, int64_t ldc, int64_t stride_c, void *stream);
 
 /*
+ * mm_gemm_f32_ws: C = A x B as mm_gemm_f32, with a caller-owned device workspace that
+ * lets products with few output tiles (the fully-connected layer on a batch of 25 to
+ * 256 input vectors, "Matrix Operations", "Performance Considerations": batch
+ * processing) split K across workgroups: each of `chunks` (2 to 8) K ranges is
+ * multiplied into its own M x N slice of the
+ * workspace, and a second launch on the same stream adds the slices in chunk order
+ * into C, so results are deterministic (they may differ from mm_gemm_f32's in the last
+ * bits: the summation order differs).
+ *   workspace        device memory of at least mm_gemm_f32_workspace_bytes(M, N, K)
+ *                    bytes, 16-byte aligned; its contents on entry do not matter and
+ *                    are overwritten. May be NULL when that size is 0. It must not
+ *                    overlap A, B or C.
+ *   workspace_bytes  its size in bytes.
+ * Calls that share a workspace must not run at the same time (e.g. keep them on one
+ * stream). Shapes the split does not serve (N <= 24, N > 256, N % 4 != 0, K < 2048,
+ * more than 256 output tiles of 64 x 64, K without a whole number of 16-deep steps per
+ * chunk) run mm_gemm_f32's kernels and leave the workspace untouched. Other arguments and errors: as for mm_gemm_f32;
+ * MM_ERR_INVALID_ARG also for a workspace that is missing, too small or misaligned.
+ *
+ * mm_gemm_f32_workspace_bytes: bytes of workspace mm_gemm_f32_ws needs for (M, N, K)
+ * (0 when it needs none), or -1 for a negative or too large size.
+ */
+int64_t mm_gemm_f32_workspace_bytes(int64_t M, int64_t N, int64_t K);
+int mm_gemm_f32_ws(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda,
+                   const float *B, int64_t ldb, float *C, int64_t ldc,
+                   void *workspace, int64_t workspace_bytes, void *stream);
+
+/*
  * mm_gemm_bf16 / mm_gemm_f16: C = A x B with 16-bit inputs and fp32 accumulation
  * and output ("Matrix Operations", "Performance Considerations": half precision
  * and matrix engines). A and B hold bf16 (mm_gemm_bf16) or IEEE binary16

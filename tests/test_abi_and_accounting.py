@@ -136,6 +136,39 @@ def test_gemv_t_workspace_sizes_and_checks(lib):
     assert f(7, 0, None, FAKE, None, None, 0, None) == mm.MM_OK
 
 
+def test_gemm_workspace_sizes_and_checks(lib):
+    ws = mm.mm_gemm_f32_workspace_bytes
+    assert ws(4096, 64, 4096) == 8 * 4096 * 64 * 4   # 64 tiles of 64 x 64: 8 K chunks
+    assert ws(4096, 32, 4096) == 8 * 4096 * 32 * 4
+    assert ws(16384, 48, 8192) == 2 * 16384 * 48 * 4  # 256 tiles: 2 chunks make ~512 workgroups
+    assert ws(4096, 64, 2064) == 0                    # 2064 = 129 x 16: no whole 16-k chunks of 2064 / 2
+    assert ws(4096, 64, 2080) == 2 * 4096 * 64 * 4    # 2080 = 2 x 65 x 16: 2 chunks
+    assert ws(4096, 128, 4096) == 4 * 4096 * 128 * 4  # 128 tiles: 4 chunks
+    assert ws(4096, 256, 4096) == 2 * 4096 * 256 * 4  # 256 tiles: 2 chunks
+    for M, N, K in [(4096, 24, 4096), (4096, 25, 4096), (4096, 260, 4096), (8192, 256, 4096),
+                    (4096, 64, 1024), (0, 64, 4096), (64, 0, 4096), (64, 64, 0)]:
+        assert ws(M, N, K) == 0, (M, N, K)            # served by mm_gemm_f32's kernels
+    assert ws(-1, 3, 3) == -1 and ws(3, 3, 1 << 31) == -1
+    need = ws(4096, 64, 4096)
+    f = lib.mm_gemm_f32_ws
+    base = (4096, 64, 4096, FAKE, 4096, FAKE, 64, FAKE, 64)
+    for args, why in [((None, need), "workspace is NULL"), ((FAKE + 4, need), "16-byte"),
+                      ((FAKE, need - 4), "smaller")]:
+        assert f(*base, *args, None) == mm.MM_ERR_INVALID_ARG
+        assert why in mm.mm_last_error()
+    for i, why in [(3, "A is NULL"), (5, "B is NULL"), (7, "C is NULL")]:
+        bad = list(base)
+        bad[i] = None
+        assert f(*bad, FAKE, need, None) == mm.MM_ERR_INVALID_ARG
+        assert why in mm.mm_last_error()
+    bad = list(base)
+    bad[4] = 100  # lda < K
+    assert f(*bad, FAKE, need, None) == mm.MM_ERR_INVALID_ARG and "lda" in mm.mm_last_error()
+    # no workspace needed: the checks of mm_gemm_f32, and nothing enqueued for M == 0
+    assert f(64, 8, 64, None, 64, FAKE, 8, FAKE, 8, None, 0, None) == mm.MM_ERR_INVALID_ARG
+    assert f(0, 8, 64, None, 64, FAKE, 8, None, 8, None, 0, None) == mm.MM_OK
+
+
 def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     import importlib
     monkeypatch.setattr(mm, "_lib", None)

@@ -322,3 +322,74 @@ def test_small_batch_columns_equal_gemv(dev):
         y = mm.gemv(Ad, to_device(np.ascontiguousarray(X[:, j]), dev))
         torch.cuda.synchronize()
         assert np.array_equal(C[:, j], y.cpu().numpy()), j
+
+
+def run_gemm_ws(A, B, dev, ws=None, a_offset=0, ldb_pad=0):
+    """mm_gemm_f32_ws through the binding: a NaN-filled workspace (its contents on entry
+    must not matter), A possibly only 4-byte aligned, B possibly with padded rows, and C
+    inside a NaN buffer that must stay untouched outside the product."""
+    M, K = A.shape
+    N = B.shape[1]
+    _, Ad = strided_on_device(A, K, dev, offset=a_offset)
+    _, Bd = strided_on_device(B, N + ldb_pad, dev)
+    if ws is None:
+        ws = mm.gemm_workspace(M, N, K, dev)
+        if ws is not None:
+            ws.view(torch.float32).fill_(float("nan"))
+    Cbuf, Cv = nan_output(M, N, N + 3, dev)
+    mm.gemm(Ad, Bd, out=Cv, workspace=ws)
+    torch.cuda.synchronize()
+    assert outside_untouched(Cbuf, M, N)
+    return Cv.cpu().numpy()
+
+
+# K split into 2-8 chunks (N of 28-256, ragged M and N % 64 != 0, K % 32 != 0 per chunk)
+# and shapes that need no workspace (N <= 24, N % 4 != 0, N > 256, more than 256 tiles,
+# K < 2048, K with no whole 16-k chunks) and take mm_gemm_f32's kernels
+WS_SHAPES = [(4096, 64, 4096), (4096, 32, 4096), (1000, 48, 2048), (777, 60, 2080), (4096, 40, 8192),
+             (130, 28, 3072), (4096, 128, 4096), (1000, 200, 2048), (4096, 256, 4096), (64, 256, 8192),
+             (4096, 24, 4096), (4096, 25, 4096), (512, 260, 2048), (8192, 256, 2048), (300, 64, 1024),
+             (300, 64, 2064)]
+
+
+@pytest.mark.parametrize("M,N,K", WS_SHAPES)
+@pytest.mark.parametrize("layout", [(0, 0), (1, 8)])  # (A offset in floats, B row padding)
+def test_split_k_workspace(dev, M, N, K, layout):
+    A = wl.random_matrix(1100 + M, M, K, "int4")
+    B = wl.random_matrix(1200 + N, K, N, "int4")
+    assert_exact(run_gemm_ws(A, B, dev, a_offset=layout[0], ldb_pad=layout[1]), A, B)
+    A = wl.random_matrix(1300 + M, M, K, "u11")
+    B = wl.random_matrix(1400 + N, K, N, "u11")
+    assert_tol(run_gemm_ws(A, B, dev, a_offset=layout[0], ldb_pad=layout[1]), A, B)
+
+
+def test_split_k_workspace_reuse_and_determinism(dev):
+    """One workspace for calls in a row (the second smaller, the third needing none):
+    each overwrites what it reads; repeated calls give the same bits."""
+    ws = mm.gemm_workspace(4096, 64, 4096, dev)
+    assert ws is not None
+    for M, N, K in [(4096, 64, 4096), (1000, 40, 2048), (300, 16, 4096), (4096, 64, 4096)]:
+        A = wl.random_matrix(1500 + M, M, K, "int4")
+        B = wl.random_matrix(1600 + N, K, N, "int4")
+        assert_exact(run_gemm_ws(A, B, dev, ws=ws), A, B)
+    A = to_device(wl.random_matrix(97, 4096, 4096, "u11"), dev)
+    B = to_device(wl.random_matrix(98, 4096, 48, "u11"), dev)
+    C1 = mm.gemm(A, B, workspace=ws)
+    C2 = mm.gemm(A, B, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(C1.view(torch.int32), C2.view(torch.int32))
+
+
+def test_split_k_workspace_on_stream(dev):
+    """Both kernels of the split run on the caller's stream, in order."""
+    A = wl.random_matrix(99, 2048, 4096, "int4")
+    B = wl.random_matrix(100, 4096, 56, "int4")
+    Ad, Bd = to_device(A, dev), to_device(B, dev)
+    ws = mm.gemm_workspace(2048, 56, 4096, dev)
+    s = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):
+        C = torch.empty((2048, 56), dtype=torch.float32, device=dev)
+        mm.gemm(Ad, Bd, out=C, workspace=ws)
+    s.synchronize()
+    assert_exact(C.cpu().numpy(), A, B)

@@ -85,6 +85,10 @@ def load():
     lib.mm_gemv_f32.argtypes = [i64, i64, vp, vp, vp, vp]
     lib.mm_gemv_t_f32.argtypes = [i64, i64, vp, vp, vp, vp]
     lib.mm_gemv_t_f32.restype = ci
+    lib.mm_gemm_f32_workspace_bytes.argtypes = [i64, i64, i64]
+    lib.mm_gemm_f32_workspace_bytes.restype = i64
+    lib.mm_gemm_f32_ws.argtypes = [i64, i64, i64, vp, i64, vp, i64, vp, i64, vp, i64, vp]
+    lib.mm_gemm_f32_ws.restype = ci
     lib.mm_gemv_t_f32_workspace_bytes.argtypes = [i64, i64]
     lib.mm_gemv_t_f32_workspace_bytes.restype = i64
     lib.mm_gemv_t_f32_ws.argtypes = [i64, i64, vp, vp, vp, vp, i64, vp]
@@ -217,6 +221,19 @@ def mm_gemv_t_f32(M, N, A, x, y, stream=None):
            "mm_gemv_t_f32")
 
 
+def mm_gemm_f32_workspace_bytes(M, N, K):
+    """Bytes of workspace mm_gemm_f32_ws needs for (M, N, K); -1 for invalid sizes."""
+    return load().mm_gemm_f32_workspace_bytes(M, N, K)
+
+
+def mm_gemm_f32_ws(M, N, K, A, lda, B, ldb, C, ldc, workspace, workspace_bytes, stream=None):
+    """C = A B, splitting K across workgroups through `workspace` where that pays.
+    Raises MMError."""
+    lib = load()
+    _check(lib.mm_gemm_f32_ws(M, N, K, _addr(A), lda, _addr(B), ldb, _addr(C), ldc, _addr(workspace),
+                              workspace_bytes, _stream(stream)), "mm_gemm_f32_ws")
+
+
 def mm_gemv_t_f32_workspace_bytes(M, N):
     """Bytes of workspace mm_gemv_t_f32_ws needs for (M, N); -1 for invalid sizes."""
     return load().mm_gemv_t_f32_workspace_bytes(M, N)
@@ -303,8 +320,19 @@ def _matrix(t, name, dtypes=None):
     return ld
 
 
-def gemm(A, B, out=None, config=None, stream=None):
-    """out = A @ B for fp32 GPU tensors (any row strides, unit column stride)."""
+def gemm_workspace(M, N, K, device):
+    """A device buffer of the size mm_gemm_f32_ws needs for (M, N, K) (None if none)."""
+    import torch
+    n = mm_gemm_f32_workspace_bytes(M, N, K)
+    if n < 0:
+        raise ValueError(f"invalid sizes {M} x {N} x {K}")
+    return torch.empty(n, dtype=torch.uint8, device=device) if n > 0 else None
+
+
+def gemm(A, B, out=None, config=None, stream=None, workspace=None):
+    """out = A @ B for fp32 GPU tensors (any row strides, unit column stride). With
+    `workspace` (a device tensor of at least mm_gemm_f32_workspace_bytes bytes, e.g. from
+    gemm_workspace) it runs mm_gemm_f32_ws."""
     import torch
     lda = _matrix(A, "A")
     ldb = _matrix(B, "B")
@@ -319,8 +347,13 @@ def gemm(A, B, out=None, config=None, stream=None):
     if tuple(out.shape) != (M, N):
         raise ValueError(f"out has shape {tuple(out.shape)}, expected {(M, N)}")
     ldc = _matrix(out, "out")
+    if workspace is not None and config is not None:
+        raise ValueError("a workspace and a forced config do not go together")
     with torch.cuda.device(A.device):
-        if config is None:
+        if workspace is not None:
+            mm_gemm_f32_ws(M, N, K, A, lda, B, ldb, out, ldc, workspace,
+                           workspace.numel() * workspace.element_size(), stream)
+        elif config is None:
             mm_gemm_f32(M, N, K, A, lda, B, ldb, out, ldc, stream)
         else:
             mm_gemm_f32_config(config, M, N, K, A, lda, B, ldb, out, ldc, stream)

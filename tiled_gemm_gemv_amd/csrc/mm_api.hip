@@ -249,6 +249,39 @@ int mm_gemm_f32(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda, co
     return run_gemm(-1, M, N, K, A, lda, B, ldb, C, ldc, stream);
 }
 
+int64_t mm_gemm_f32_workspace_bytes(int64_t M, int64_t N, int64_t K)
+{
+    if (M < 0 || N < 0 || K < 0 || M > kMaxDim || N > kMaxDim || K > kMaxDim) return -1;
+    if (M == 0 || N == 0 || K == 0) return 0;
+    return 4 * mm::gemm_split_ws_floats(M, N, K);
+}
+
+int mm_gemm_f32_ws(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda, const float *B,
+                   int64_t ldb, float *C, int64_t ldc, void *workspace, int64_t workspace_bytes, void *stream)
+{
+    const int64_t need = mm_gemm_f32_workspace_bytes(M, N, K);
+    if (need > 0) {
+        if (!workspace) return invalid("workspace is NULL");
+        if ((uintptr_t)workspace % 16) return invalid("workspace not 16-byte aligned");
+        if (workspace_bytes < need) return invalid("workspace smaller than mm_gemm_f32_workspace_bytes");
+    }
+    if (need <= 0) return run_gemm(-1, M, N, K, A, lda, B, ldb, C, ldc, stream);
+    const int st = check_gemm(M, N, K, A, lda, B, ldb, C, ldc);
+    if (st != MM_OK) return st;
+    mm::GemmArgs a;
+    a.A = A;
+    a.B = B;
+    a.C = C;
+    a.lda = lda;
+    a.ldb = ldb;
+    a.ldc = ldc;
+    a.M = (int)M;
+    a.N = (int)N;
+    a.K = (int)K;
+    return from_hip("split gemm launch", mm::gemm_split_launch(a, static_cast<float *>(workspace),
+                                                                static_cast<hipStream_t>(stream)));
+}
+
 int mm_gemm_f32_config(int cfg, int64_t M, int64_t N, int64_t K, const float *A, int64_t lda,
                        const float *B, int64_t ldb, float *C, int64_t ldc, void *stream)
 {

@@ -112,4 +112,78 @@ hipError_t gemm_launch(int cfg, const GemmArgs &a, hipStream_t stream)
     return kConfigs[cfg].launch(a, stream);
 }
 
+// ---------------------------------------------------------------------------
+// K split across workgroups, for products with few output tiles and long K (the
+// fully-connected layer on a batch of 25 to 256 vectors). With at most 256 tiles of
+// 64 x 64 the chip holds under one workgroup per CU, and the narrow kernel (16 rows and
+// all of K per workgroup) reads all of B from L2 in each workgroup. Split into `chunks`
+// K ranges, the product is a strided batch of GEMMs over the chunks (A + c Kc columns,
+// B + c Kc rows) on the 64 x 64 direct tile, each writing its own M x N slice of the
+// workspace; a second kernel adds the slices in chunk order. Measured against
+// mm_gemm_f32 (TFLOP/s): 4096 x 64 x 4096 58 -> 87, 4096 x 128 x 4096 55 -> 102,
+// 4096 x 256 x 4096 109 -> 118, 1024 x 128 x 4096 28 -> 63, 4096 x 32 x 4096 42 -> 45.
+// With N % 4 != 0 the chunks run the general (4-byte lane) build of the tile and the
+// split lost (4096 x 25 x 4096: 33 -> 28), so those shapes are not split.
+namespace {
+
+constexpr int kSplitCfg = 13;  // 64 x 64 direct tile, 4 stages
+
+__global__ __launch_bounds__(256) void sum_chunks_kernel(const float *ws, float *C, int64_t ldc, int M, int N,
+                                                         int chunks)
+{
+    const int64_t MN = (int64_t)M * N;
+    for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < MN; e += (int64_t)gridDim.x * blockDim.x) {
+        float s = ws[e];
+        for (int c = 1; c < chunks; ++c) s += ws[c * MN + e];
+        const int64_t i = e / N, j = e - i * N;
+        C[i * ldc + j] = s;
+    }
+}
+
+}  // namespace
+
+int gemm_split_chunks(int64_t M, int64_t N, int64_t K)
+{
+    if (N <= 24 || N > 256 || N % 4 != 0 || K < 2048 || M < 1) return 0;
+    const int64_t tiles = (M + 63) / 64 * ((N + 63) / 64);
+    if (tiles > 256) return 0;  // at least one workgroup per CU without a split
+    int chunks = 1;
+    while (chunks < 8 && tiles * chunks < 512) chunks *= 2;
+    while (chunks > 1 && (K % (16 * chunks) != 0)) chunks /= 2;  // whole 16-k steps per chunk
+    return chunks >= 2 ? chunks : 0;
+}
+
+int64_t gemm_split_ws_floats(int64_t M, int64_t N, int64_t K)
+{
+    const int chunks = gemm_split_chunks(M, N, K);
+    return chunks ? chunks * M * N : 0;
+}
+
+hipError_t gemm_split_launch(const GemmArgs &a, float *ws, hipStream_t stream)
+{
+    const int chunks = gemm_split_chunks(a.M, a.N, a.K);
+    if (!chunks) return hipErrorInvalidValue;
+    const int kc = a.K / chunks;
+    GemmArgs b = a;
+    b.K = kc;
+    b.C = ws;
+    b.ldc = a.N;
+    b.batch = chunks;
+    b.sa = kc;
+    b.sb = (int64_t)kc * a.ldb;
+    b.sc = (int64_t)a.M * a.N;
+    hipError_t e = gemm_launch(kSplitCfg, b, stream);
+    if (e != hipSuccess) return e;
+    const int64_t MN = (int64_t)a.M * a.N;
+    int64_t blocks = (MN + 255) / 256;
+    if (blocks > 4096) blocks = 4096;
+    const float *wsc = ws;
+    float *C = a.C;
+    int64_t ldc = a.ldc;
+    int M = a.M, N = a.N, ch = chunks;
+    void *args[] = {&wsc, &C, &ldc, &M, &N, &ch};
+    return hipLaunchKernel(reinterpret_cast<const void *>(&sum_chunks_kernel), dim3((unsigned)blocks), dim3(256),
+                           args, 0, stream);
+}
+
 }  // namespace mm

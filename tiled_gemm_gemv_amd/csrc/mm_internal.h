@@ -92,6 +92,12 @@ int gemm_select_config(int64_t M, int64_t N, int64_t K, int64_t batch = 1);
 double gemm_config_time(int cfg, int64_t M, int64_t N, int64_t K, int64_t batch);
 // Enqueue config `cfg` of the GEMM (K >= 1, M >= 1, N >= 1).
 hipError_t gemm_launch(int cfg, const GemmArgs &a, hipStream_t stream);
+// K split across workgroups through a caller workspace (mm_gemm.hip): the number of K
+// chunks for (M, N, K) (0: no split), the workspace it needs (floats) and the launch
+// (the product per chunk into the workspace, then the sum in chunk order into C).
+int gemm_split_chunks(int64_t M, int64_t N, int64_t K);
+int64_t gemm_split_ws_floats(int64_t M, int64_t N, int64_t K);
+hipError_t gemm_split_launch(const GemmArgs &a, float *ws, hipStream_t stream);
 
 // Narrow-C GEMM (mm_gemm_skinny.hip): 16 x 64 tiles of C, K split over W waves
 // per workgroup, L / (column blocks) 16-deep chunks per wave per round. Correct for
