@@ -726,6 +726,21 @@ def sweep(kind, torch, mm, dev):
         rate = 1e3 / slope                      # bytes per second
         print(f"# cold fit over M >= 2048: fixed {t0 * 1e3:.2f} us per launch + streaming at "
               f"{rate / 1e9:.0f} GB/s ({100 * rate / rl.MI355X_HBM_PEAK:.1f}% of 8 TB/s)")
+        # What another implementation's single cold launch over the same bytes reaches: the
+        # framework's row-sum reduction reads a 4096 x 4096 matrix once and writes 4096
+        # floats, the GEMV's traffic without x (not part of the path, a reference point).
+        sets = (512 << 20) // (4096 * VN * 4)
+        As = [torch.rand(4096, VN, device=dev) for _ in range(sets)]
+        ys = [torch.empty(4096, device=dev) for _ in range(sets)]
+
+        def rowsum(i, st):
+            torch.sum(As[i % sets], dim=1, out=ys[i % sets])
+        tr = burst_time_ms(torch, rowsum, 8 * sets)
+        rb = 4 * 4096 * (VN + 1)
+        print(f"# reference read, cold, same rotation: torch.sum(A, dim=1) over 4096 x {VN}: "
+              f"{tr * 1e3:.2f} us, {rb / tr / 1e6:.0f} GB/s ({100 * rb / (tr * 1e-3) / rl.MI355X_HBM_PEAK:.1f}% of 8 TB/s)",
+              flush=True)
+        del As, ys
         print("# transposed GEMV y = A^T x, same timing, cold: mm_gemv_t_f32 (16-column strips) and "
               "mm_gemv_t_f32_ws (row blocks, partial sums in a workspace, two launches)")
         for TM, TN in ((4096, 4096), (8192, 8192), (16384, 4096), (4096, 16384)):
