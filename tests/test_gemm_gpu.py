@@ -393,3 +393,18 @@ def test_split_k_workspace_on_stream(dev):
         mm.gemm(Ad, Bd, out=C, workspace=ws)
     s.synchronize()
     assert_exact(C.cpu().numpy(), A, B)
+
+
+def test_split_k_workspace_binding_checks(dev):
+    """The binding rejects a workspace on the host or not contiguous before any launch."""
+    A = torch.zeros((4096, 4096), device=dev)
+    B = torch.zeros((4096, 64), device=dev)
+    n = mm.mm_gemm_f32_workspace_bytes(4096, 64, 4096)
+    with pytest.raises(ValueError, match="workspace is on"):
+        mm.gemm(A, B, workspace=torch.empty(n, dtype=torch.uint8))
+    with pytest.raises(ValueError, match="contiguous"):
+        mm.gemm(A, B, workspace=torch.empty(2 * n, dtype=torch.uint8, device=dev)[::2])
+    with pytest.raises(ValueError, match="forced config"):
+        mm.gemm(A, B, workspace=torch.empty(n, dtype=torch.uint8, device=dev), config=0)
+    with pytest.raises(mm.MMError, match="smaller"):
+        mm.gemm(A, B, workspace=torch.empty(n - 16, dtype=torch.uint8, device=dev))

@@ -131,3 +131,16 @@ def test_workspace_reuse_and_determinism(dev):
     y2 = mm.gemv_t(A, x, workspace=ws)
     torch.cuda.synchronize()
     assert torch.equal(y1.view(torch.int32), y2.view(torch.int32))
+
+
+def test_workspace_binding_checks(dev):
+    """The binding rejects a workspace on the host or not contiguous before any launch."""
+    A = torch.zeros((4096, 4096), device=dev)
+    x = torch.zeros(4096, device=dev)
+    n = mm.mm_gemv_t_f32_workspace_bytes(4096, 4096)
+    with pytest.raises(ValueError, match="workspace is on"):
+        mm.gemv_t(A, x, workspace=torch.empty(n, dtype=torch.uint8))
+    with pytest.raises(ValueError, match="contiguous"):
+        mm.gemv_t(A, x, workspace=torch.empty(2 * n, dtype=torch.uint8, device=dev)[::2])
+    with pytest.raises(mm.MMError, match="smaller"):
+        mm.gemv_t(A, x, workspace=torch.empty(n - 16, dtype=torch.uint8, device=dev))

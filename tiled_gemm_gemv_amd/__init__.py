@@ -300,6 +300,17 @@ def mm_last_error():
 
 # ----------------------------------------------------- torch-tensor front ends
 
+def _workspace_bytes(ws, device):
+    """Size in bytes of a workspace tensor, which must be contiguous and on `device`."""
+    if not hasattr(ws, "data_ptr"):
+        raise TypeError(f"workspace must be a torch.Tensor, got {type(ws).__name__}")
+    if ws.device != device:
+        raise ValueError(f"workspace is on {ws.device}, the operands on {device}")
+    if not ws.is_contiguous():
+        raise ValueError("workspace must be contiguous")
+    return ws.numel() * ws.element_size()
+
+
 def _matrix(t, name, dtypes=None):
     import torch
     if not isinstance(t, torch.Tensor):
@@ -347,12 +358,14 @@ def gemm(A, B, out=None, config=None, stream=None, workspace=None):
     if tuple(out.shape) != (M, N):
         raise ValueError(f"out has shape {tuple(out.shape)}, expected {(M, N)}")
     ldc = _matrix(out, "out")
+    if out.device != A.device:
+        raise ValueError("out is on another device than A")
     if workspace is not None and config is not None:
         raise ValueError("a workspace and a forced config do not go together")
     with torch.cuda.device(A.device):
         if workspace is not None:
             mm_gemm_f32_ws(M, N, K, A, lda, B, ldb, out, ldc, workspace,
-                           workspace.numel() * workspace.element_size(), stream)
+                           _workspace_bytes(workspace, A.device), stream)
         elif config is None:
             mm_gemm_f32(M, N, K, A, lda, B, ldb, out, ldc, stream)
         else:
@@ -458,9 +471,7 @@ def gemv_t(A, x, out=None, workspace=None, stream=None):
         if workspace is None:
             mm_gemv_t_f32(M, N, A, x, out, stream)
         else:
-            if workspace.device != A.device:
-                raise ValueError("workspace is on another device")
-            mm_gemv_t_f32_ws(M, N, A, x, out, workspace, workspace.numel() * workspace.element_size(), stream)
+            mm_gemv_t_f32_ws(M, N, A, x, out, workspace, _workspace_bytes(workspace, A.device), stream)
     return out
 
 
