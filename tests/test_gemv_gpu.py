@@ -105,3 +105,17 @@ def test_deterministic(dev):
     y2 = mm.gemv(Ad, xd)
     torch.cuda.synchronize()
     assert torch.equal(y1.view(torch.int32), y2.view(torch.int32))
+
+
+def test_host_tensors_rejected(dev):
+    """A host x or out is refused by the binding before any launch (its address would be
+    a host pointer)."""
+    A = torch.zeros((64, 32), device=dev)
+    with pytest.raises(ValueError, match="out is on cpu"):
+        mm.gemv(A, torch.zeros(32, device=dev), out=torch.empty(64))
+    with pytest.raises(ValueError, match="x is on cpu"):
+        mm.gemv(A, torch.zeros(32))
+    with pytest.raises(ValueError, match="out is on cpu"):
+        mm.gemv_t(A, torch.zeros(64, device=dev), out=torch.empty(32))
+    with pytest.raises(ValueError, match="x is on cpu"):
+        mm.gemv_t(A, torch.zeros(64))

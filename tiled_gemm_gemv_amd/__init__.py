@@ -300,6 +300,14 @@ def mm_last_error():
 
 # ----------------------------------------------------- torch-tensor front ends
 
+def _on_device(device, **tensors):
+    """Raise ValueError unless every given tensor is on `device` (a host tensor's address
+    handed to a kernel would fault the GPU)."""
+    for name, t in tensors.items():
+        if t.device != device:
+            raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
 def _workspace_bytes(ws, device):
     """Size in bytes of a workspace tensor, which must be contiguous and on `device`."""
     if not hasattr(ws, "data_ptr"):
@@ -358,8 +366,7 @@ def gemm(A, B, out=None, config=None, stream=None, workspace=None):
     if tuple(out.shape) != (M, N):
         raise ValueError(f"out has shape {tuple(out.shape)}, expected {(M, N)}")
     ldc = _matrix(out, "out")
-    if out.device != A.device:
-        raise ValueError("out is on another device than A")
+    _on_device(A.device, out=out)
     if workspace is not None and config is not None:
         raise ValueError("a workspace and a forced config do not go together")
     with torch.cuda.device(A.device):
@@ -391,6 +398,7 @@ def gemm_batched(A, B, out=None, stream=None):
     lda = _matrix(A[0] if batch else A.new_empty((M, K)), "A")
     ldb = _matrix(B[0] if batch else B.new_empty((K, N)), "B")
     ldc = _matrix(out[0] if batch else out.new_empty((M, N)), "out")
+    _on_device(A.device, B=B, out=out)
     with torch.cuda.device(A.device):
         mm_gemm_f32_batched(batch, M, N, K, A, lda, A.stride(0), B, ldb, B.stride(0), out, ldc,
                             out.stride(0), stream)
@@ -413,6 +421,7 @@ def gemm16(A, B, out=None, config=None, stream=None):
     if tuple(out.shape) != (M, N):
         raise ValueError(f"out has shape {tuple(out.shape)}, expected {(M, N)}")
     ldc = _matrix(out, "out")
+    _on_device(A.device, out=out)
     bf = A.dtype == torch.bfloat16
     with torch.cuda.device(A.device):
         if config is None:
@@ -432,12 +441,11 @@ def gemv(A, x, out=None, stream=None):
         raise ValueError("A must have packed rows (contiguous)")
     if x.dtype != torch.float32 or x.dim() != 1 or x.shape[0] != N or not x.is_contiguous():
         raise ValueError(f"x must be a contiguous float32 vector of {N} entries")
-    if x.device != A.device:
-        raise ValueError("A and x are on different devices")
     if out is None:
         out = torch.empty(M, dtype=torch.float32, device=A.device)
     if out.dtype != torch.float32 or tuple(out.shape) != (M,) or not out.is_contiguous():
         raise ValueError(f"out must be a contiguous float32 vector of {M} entries")
+    _on_device(A.device, x=x, out=out)
     with torch.cuda.device(A.device):
         mm_gemv_f32(M, N, A, x, out, stream)
     return out
@@ -467,6 +475,7 @@ def gemv_t(A, x, out=None, workspace=None, stream=None):
         out = torch.empty(N, dtype=torch.float32, device=A.device)
     if out.dtype != torch.float32 or tuple(out.shape) != (N,) or not out.is_contiguous():
         raise ValueError(f"out must be a contiguous float32 vector of {N} entries")
+    _on_device(A.device, x=x, out=out)
     with torch.cuda.device(A.device):
         if workspace is None:
             mm_gemv_t_f32(M, N, A, x, out, stream)
