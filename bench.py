@@ -636,13 +636,15 @@ def sweep(kind, torch, mm, dev):
               "64 x 64 tile, partial products in a workspace, then a sum kernel), TFLOP/s")
         print(f"{'M':>6s} {'N':>6s} {'K':>6s} {'chunks':>7s} {'gemm':>9s} {'gemm_ws':>9s}")
         for M, N, K in ((4096, 32, 4096), (4096, 48, 4096), (4096, 64, 4096), (4096, 128, 4096),
-                        (4096, 256, 4096), (1024, 128, 4096), (8192, 64, 8192), (1024, 64, 8192)):
+                        (4096, 256, 4096), (1024, 128, 4096), (8192, 64, 8192), (1024, 64, 8192),
+                        (4096, 45, 4096), (4096, 99, 4096), (4096, 127, 4096)):
             A = torch.randn(M, K, device=dev)
             B = torch.randn(K, N, device=dev)
             C = torch.empty(M, N, device=dev)
             ws = mm.gemm_workspace(M, N, K, dev)
             wsb = 0 if ws is None else ws.numel()
-            chunks = wsb // (4 * M * N)
+            N4 = -(-N // 4) * 4       # slices of N rounded up to 4, then B padded to N4 if N % 4
+            chunks = (wsb // 4 - (K * N4 if N4 != N else 0)) // (M * N4) if wsb else 0
             flop = rl.gemm_flops(M, N, K)
             reps = max(3, min(200, int(2e11 / flop)))
 

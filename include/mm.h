@@ -180,9 +180,11 @@ int mm_gemm_f32_batched(int64_t batch, int64_t M, int64_t N, int64_t K,
  *                    overlap A, B or C.
  *   workspace_bytes  its size in bytes.
  * Calls that share a workspace must not run at the same time (e.g. keep them on one
- * stream). Shapes the split does not serve (N <= 24, N > 256, N % 4 != 0, K < 2048,
- * more than 256 output tiles of 64 x 64, K without a whole number of 16-deep steps per
- * chunk) run mm_gemm_f32's kernels and leave the workspace untouched. Other arguments and errors: as for mm_gemm_f32;
+ * stream). With N % 4 != 0, B is first copied into the workspace with its rows padded
+ * to a multiple of 4 floats. Shapes the split does not serve (N <= 24, N % 4 != 0 with
+ * N <= 32, N > 256, K < 2048, more than 256 output tiles of 64 x 64, K without a whole
+ * number of 16-deep steps per chunk) run mm_gemm_f32's kernels and leave the workspace
+ * untouched. Other arguments and errors: as for mm_gemm_f32;
  * MM_ERR_INVALID_ARG also for a workspace that is missing, too small or misaligned.
  *
  * mm_gemm_f32_workspace_bytes: bytes of workspace mm_gemm_f32_ws needs for (M, N, K)

@@ -145,7 +145,11 @@ def test_gemm_workspace_sizes_and_checks(lib):
     assert ws(4096, 64, 2080) == 2 * 4096 * 64 * 4    # 2080 = 2 x 65 x 16: 2 chunks
     assert ws(4096, 128, 4096) == 4 * 4096 * 128 * 4  # 128 tiles: 4 chunks
     assert ws(4096, 256, 4096) == 2 * 4096 * 256 * 4  # 256 tiles: 2 chunks
-    for M, N, K in [(4096, 24, 4096), (4096, 25, 4096), (4096, 260, 4096), (8192, 256, 4096),
+    # N % 4 != 0 above 32 columns: slices of N rounded up to 4, then B padded to that width
+    assert ws(4096, 45, 4096) == (8 * 4096 * 48 + 4096 * 48) * 4
+    assert ws(1000, 99, 2048) == (8 * 1000 * 100 + 2048 * 100) * 4
+    assert ws(4096, 255, 4096) == (2 * 4096 * 256 + 4096 * 256) * 4
+    for M, N, K in [(4096, 24, 4096), (4096, 25, 4096), (4096, 31, 4096), (4096, 260, 4096), (8192, 256, 4096),
                     (4096, 64, 1024), (0, 64, 4096), (64, 0, 4096), (64, 64, 0)]:
         assert ws(M, N, K) == 0, (M, N, K)            # served by mm_gemm_f32's kernels
     assert ws(-1, 3, 3) == -1 and ws(3, 3, 1 << 31) == -1

@@ -343,13 +343,15 @@ def run_gemm_ws(A, B, dev, ws=None, a_offset=0, ldb_pad=0):
     return Cv.cpu().numpy()
 
 
-# K split into 2-8 chunks (N of 28-256, ragged M and N % 64 != 0, K % 32 != 0 per chunk)
-# and shapes that need no workspace (N <= 24, N % 4 != 0, N > 256, more than 256 tiles,
-# K < 2048, K with no whole 16-k chunks) and take mm_gemm_f32's kernels
+# K split into 2-8 chunks (N of 28-256, ragged M and N % 64 != 0, K % 32 != 0 per chunk;
+# N % 4 != 0 through the padded copy of B) and shapes that need no workspace (N <= 24,
+# N % 4 != 0 up to 32, N > 256, more than 256 tiles, K < 2048, K with no whole 16-k
+# chunks) and take mm_gemm_f32's kernels
 WS_SHAPES = [(4096, 64, 4096), (4096, 32, 4096), (1000, 48, 2048), (777, 60, 2080), (4096, 40, 8192),
              (130, 28, 3072), (4096, 128, 4096), (1000, 200, 2048), (4096, 256, 4096), (64, 256, 8192),
-             (4096, 24, 4096), (4096, 25, 4096), (512, 260, 2048), (8192, 256, 2048), (300, 64, 1024),
-             (300, 64, 2064)]
+             (4096, 45, 4096), (777, 61, 2080), (1000, 99, 2048), (130, 33, 3072), (4096, 255, 4096),
+             (4096, 24, 4096), (4096, 25, 4096), (4096, 31, 4096), (512, 260, 2048), (8192, 256, 2048),
+             (300, 64, 1024), (300, 64, 2064)]
 
 
 @pytest.mark.parametrize("M,N,K", WS_SHAPES)
@@ -368,7 +370,7 @@ def test_split_k_workspace_reuse_and_determinism(dev):
     each overwrites what it reads; repeated calls give the same bits."""
     ws = mm.gemm_workspace(4096, 64, 4096, dev)
     assert ws is not None
-    for M, N, K in [(4096, 64, 4096), (1000, 40, 2048), (300, 16, 4096), (4096, 64, 4096)]:
+    for M, N, K in [(4096, 64, 4096), (1000, 40, 2048), (1000, 99, 2048), (300, 16, 4096), (4096, 64, 4096)]:
         A = wl.random_matrix(1500 + M, M, K, "int4")
         B = wl.random_matrix(1600 + N, K, N, "int4")
         assert_exact(run_gemm_ws(A, B, dev, ws=ws), A, B)

@@ -118,33 +118,58 @@ hipError_t gemm_launch(int cfg, const GemmArgs &a, hipStream_t stream)
 // 64 x 64 the chip holds under one workgroup per CU, and the narrow kernel (16 rows and
 // all of K per workgroup) reads all of B from L2 in each workgroup. Split into `chunks`
 // K ranges, the product is a strided batch of GEMMs over the chunks (A + c Kc columns,
-// B + c Kc rows) on the 64 x 64 direct tile, each writing its own M x N slice of the
-// workspace; a second kernel adds the slices in chunk order. Measured against
-// mm_gemm_f32 (TFLOP/s): 4096 x 64 x 4096 58 -> 87, 4096 x 128 x 4096 55 -> 102,
-// 4096 x 256 x 4096 109 -> 118, 1024 x 128 x 4096 28 -> 63, 4096 x 32 x 4096 42 -> 45.
-// With N % 4 != 0 the chunks run the general (4-byte lane) build of the tile and the
-// split lost (4096 x 25 x 4096: 33 -> 28), so those shapes are not split.
+// B + c Kc rows) on the 64 x 64 direct tile, each writing its own M x N4 slice of the
+// workspace (N4 = N rounded up to a multiple of 4); a second kernel adds the slices in
+// chunk order and writes the N columns of C. Measured against mm_gemm_f32 (TFLOP/s):
+// 4096 x 64 x 4096 58 -> 87, 4096 x 128 x 4096 55 -> 102, 4096 x 256 x 4096 109 -> 118,
+// 1024 x 128 x 4096 28 -> 63, 4096 x 32 x 4096 42 -> 45.
+// With N % 4 != 0, B's rows are not whole 16-byte lanes: run directly, the chunks took the
+// tile's general (4-byte lane) build and the split lost (4096 x 25 x 4096: 33 -> 28). B
+// is first copied into the workspace as K x N4 with zero columns after N (one more
+// launch, K N4 floats), so the chunks run the lean build; below 33 columns that copy
+// eats the gain and such shapes are not split.
 namespace {
 
 constexpr int kSplitCfg = 13;  // 64 x 64 direct tile, 4 stages
 
-__global__ __launch_bounds__(256) void sum_chunks_kernel(const float *ws, float *C, int64_t ldc, int M, int N,
-                                                         int chunks)
+int64_t round4(int64_t n) { return (n + 3) & ~int64_t(3); }
+
+// Bp (K x N4, packed) = B (K x N, leading dimension ldb) with zeros in columns N .. N4 - 1.
+__global__ __launch_bounds__(256) void pad_columns_kernel(const float *B, int64_t ldb, float *Bp, int K, int N,
+                                                          int N4)
 {
-    const int64_t MN = (int64_t)M * N;
+    const int64_t total = (int64_t)K * N4;
+    for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < total; e += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t k = e / N4, j = e - k * N4;
+        Bp[e] = j < N ? B[k * ldb + j] : 0.f;
+    }
+}
+
+// C (M x N, leading dimension ldc) = the sum of the `chunks` M x N4 slices of ws, in
+// slice order.
+__global__ __launch_bounds__(256) void sum_chunks_kernel(const float *ws, float *C, int64_t ldc, int M, int N,
+                                                         int N4, int chunks)
+{
+    const int64_t MN = (int64_t)M * N, slice = (int64_t)M * N4;
     for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < MN; e += (int64_t)gridDim.x * blockDim.x) {
-        float s = ws[e];
-        for (int c = 1; c < chunks; ++c) s += ws[c * MN + e];
-        const int64_t i = e / N, j = e - i * N;
+        const int64_t i = e / N, j = e - i * N, w = i * N4 + j;
+        float s = ws[w];
+        for (int c = 1; c < chunks; ++c) s += ws[c * slice + w];
         C[i * ldc + j] = s;
     }
+}
+
+int64_t grid_blocks(int64_t elements)
+{
+    const int64_t blocks = (elements + 255) / 256;
+    return blocks < 4096 ? blocks : 4096;
 }
 
 }  // namespace
 
 int gemm_split_chunks(int64_t M, int64_t N, int64_t K)
 {
-    if (N <= 24 || N > 256 || N % 4 != 0 || K < 2048 || M < 1) return 0;
+    if (N <= 24 || N > 256 || (N % 4 != 0 && N <= 32) || K < 2048 || M < 1) return 0;
     const int64_t tiles = (M + 63) / 64 * ((N + 63) / 64);
     if (tiles > 256) return 0;  // at least one workgroup per CU without a split
     int chunks = 1;
@@ -153,37 +178,53 @@ int gemm_split_chunks(int64_t M, int64_t N, int64_t K)
     return chunks >= 2 ? chunks : 0;
 }
 
+// Layout: the chunks' M x N4 slices, then (N % 4 != 0 only) the padded copy of B, which
+// starts 16-byte aligned (the slices hold a multiple of 4 floats).
 int64_t gemm_split_ws_floats(int64_t M, int64_t N, int64_t K)
 {
     const int chunks = gemm_split_chunks(M, N, K);
-    return chunks ? chunks * M * N : 0;
+    if (!chunks) return 0;
+    const int64_t N4 = round4(N);
+    return chunks * M * N4 + (N4 != N ? K * N4 : 0);
 }
 
 hipError_t gemm_split_launch(const GemmArgs &a, float *ws, hipStream_t stream)
 {
     const int chunks = gemm_split_chunks(a.M, a.N, a.K);
     if (!chunks) return hipErrorInvalidValue;
+    const int N4 = (int)round4(a.N);
     const int kc = a.K / chunks;
     GemmArgs b = a;
+    if (N4 != a.N) {
+        float *Bp = ws + (int64_t)chunks * a.M * N4;
+        const float *B = a.B;
+        int64_t ldb = a.ldb;
+        int K = a.K, N = a.N, n4 = N4;
+        void *pargs[] = {&B, &ldb, &Bp, &K, &N, &n4};
+        const hipError_t e = hipLaunchKernel(reinterpret_cast<const void *>(&pad_columns_kernel),
+                                             dim3((unsigned)grid_blocks((int64_t)a.K * N4)), dim3(256), pargs, 0,
+                                             stream);
+        if (e != hipSuccess) return e;
+        b.B = Bp;
+        b.ldb = N4;
+        b.N = N4;
+    }
     b.K = kc;
     b.C = ws;
-    b.ldc = a.N;
+    b.ldc = N4;
     b.batch = chunks;
     b.sa = kc;
-    b.sb = (int64_t)kc * a.ldb;
-    b.sc = (int64_t)a.M * a.N;
+    b.sb = (int64_t)kc * b.ldb;
+    b.sc = (int64_t)a.M * N4;
     hipError_t e = gemm_launch(kSplitCfg, b, stream);
     if (e != hipSuccess) return e;
-    const int64_t MN = (int64_t)a.M * a.N;
-    int64_t blocks = (MN + 255) / 256;
-    if (blocks > 4096) blocks = 4096;
     const float *wsc = ws;
     float *C = a.C;
     int64_t ldc = a.ldc;
-    int M = a.M, N = a.N, ch = chunks;
-    void *args[] = {&wsc, &C, &ldc, &M, &N, &ch};
-    return hipLaunchKernel(reinterpret_cast<const void *>(&sum_chunks_kernel), dim3((unsigned)blocks), dim3(256),
-                           args, 0, stream);
+    int M = a.M, N = a.N, n4 = N4, ch = chunks;
+    void *args[] = {&wsc, &C, &ldc, &M, &N, &n4, &ch};
+    return hipLaunchKernel(reinterpret_cast<const void *>(&sum_chunks_kernel),
+                           dim3((unsigned)grid_blocks((int64_t)a.M * a.N)), dim3(256), args, 0, stream);
 }
 
 }  // namespace mm
