@@ -585,16 +585,19 @@ def sweep(kind, torch, mm, dev):
         shapes += [(1000, 1532, 784, "ragged M, aligned rows (N, K multiples of 4 and 16)"),
                    (512, 512, 512, ""), (1536, 1536, 1536, ""), (2048, 2048, 2048, ""),
                    (3072, 3072, 3072, ""), (4096, 4096, 4096, ""), (1024, 4096, 4096, ""),
-                   (8192, 1792, 4096, "projection, 1/8 of N")]
+                   (8192, 1792, 4096, "projection, 1/8 of N"),
+                   (4096, 128, 4096, "128 tiles of 64 x 64: K in two halves"),
+                   (1024, 512, 8192, "K in two halves"), (2048, 512, 8192, "K in two halves")]
         shapes += [(4096, n, 4096, f"FC layer 4096x4096, batch of {n}") for n in (1, 2, 4, 8, 16, 32, 64)]
         nc = mm.mm_gemm_f32_num_configs()
         print("# fp32 GEMM, TFLOP/s per tile configuration (back-to-back launches between two "
               "events, inputs N(0,1))")
         for c in range(nc):
             print(f"#   cfg {c}: {mm.mm_gemm_f32_config_name(c)}")
-        print("#   * = the configuration mm_gemm_f32 selects for the shape")
+        print("#   * = the configuration mm_gemm_f32 selects for the shape; default = mm_gemm_f32 itself "
+              "(differs from the starred column where it runs K as two halves)")
         print(f"{'M':>6s} {'N':>6s} {'K':>6s}  " + " ".join(f"{'cfg' + str(c):>8s}" for c in range(nc))
-              + "  workload")
+              + f" {'default':>8s}  workload")
         for M, N, K, name in shapes:
             A = torch.randn(M, K, device=dev)
             B = torch.randn(K, N, device=dev)
@@ -608,6 +611,10 @@ def sweep(kind, torch, mm, dev):
                     mm.mm_gemm_f32_config(c, M, N, K, A, K, B, N, C, N, st)
                 ms = burst_time_ms(torch, launch, reps)
                 cells.append(f"{flop / ms / 1e9:7.1f}" + ("*" if c == sel else " "))
+
+            def default(i, st):
+                mm.mm_gemm_f32(M, N, K, A, K, B, N, C, N, st)
+            cells.append(f"{flop / burst_time_ms(torch, default, reps) / 1e9:8.1f}")
             print(f"{M:6d} {N:6d} {K:6d}  " + " ".join(cells) + f"  {name}", flush=True)
             del A, B, C
         print("# strided batched GEMM (one mm_gemm_f32_batched launch) vs the same problems as "

@@ -28,9 +28,12 @@
  *     only written. Outputs must not overlap inputs (undefined, not checked).
  *     Wider alignment (16 bytes, leading dimensions that are multiples of 4) lets
  *     the kernels use 16-byte loads; it is never required.
- *   - Output: only the logical output elements are written (each exactly once);
- *     bytes in leading-dimension gaps and beyond are left untouched. The output
- *     is overwritten: there is no scaling of, or accumulation into, its old value.
+ *   - Output: only the logical output elements are written; bytes in
+ *     leading-dimension gaps and beyond are left untouched. The output is
+ *     overwritten: there is no scaling of, or accumulation into, its old value.
+ *     Each element is stored once, except where mm_gemm_f32 splits K in two
+ *     halves (below): it then zeroes C and adds the halves into it with device
+ *     atomics, so C must be ordinary device memory (not host or managed memory).
  *   - Stream: a hipStream_t passed as void*; NULL means the default stream. Calls
  *     only enqueue work and return; they never synchronise and never allocate.
  *     Errors raised by the device while the work runs surface at the caller's
@@ -67,6 +70,11 @@ typedef enum mm_status {
  * M == 0 or N == 0: nothing is enqueued and MM_OK is returned.
  * K == 0: C is filled with zeros (the empty sum; the pages' kernels write a
  * zero-initialised sum when the k loop does not run).
+ * Products whose C has 128 to 256 tiles of 64 x 64 with N >= 64, N % 4 == 0,
+ * K % 32 == 0 and K >= 4096 (K >= 2048 at 128 tiles) run as two K halves, which
+ * doubles the workgroups: C is zeroed, then each half adds its tiles into C
+ * atomically. With two partial sums the result does not depend on their order, so
+ * it is deterministic; it may differ in the last bits from the unsplit kernel's.
  * Errors: MM_ERR_INVALID_ARG (negative or too-large size, leading dimension too
  * small, NULL pointer with a non-empty extent, byte offset overflow),
  * MM_ERR_NO_DEVICE, MM_ERR_LAUNCH.
@@ -134,7 +142,8 @@ int mm_gemv_t_f32_ws(int64_t M, int64_t N, const float *A, const float *x, float
  *   mm_gemm_f32_num_configs: number of configurations, >= 1.
  *   mm_gemm_f32_config_name: static NUL-terminated description of config `cfg`
  *     (e.g. "256x256x32 w128x64"), or NULL if cfg is out of range.
- *   mm_gemm_f32_select: the config mm_gemm_f32 would use for (M, N, K).
+ *   mm_gemm_f32_select: the config mm_gemm_f32 would use for (M, N, K) (for the
+ *     shapes it runs as two K halves, the config of the halves' tile).
  *   mm_gemm_f32_config: mm_gemm_f32 forced to config `cfg`; same arguments and
  *     errors, plus MM_ERR_INVALID_ARG for cfg out of range. Every config gives a
  *     correct product for every shape.

@@ -410,3 +410,47 @@ def test_split_k_workspace_binding_checks(dev):
         mm.gemm(A, B, workspace=torch.empty(n, dtype=torch.uint8, device=dev), config=0)
     with pytest.raises(mm.MMError, match="smaller"):
         mm.gemm(A, B, workspace=torch.empty(n - 16, dtype=torch.uint8, device=dev))
+
+
+# mm_gemm_f32's two-K-halves path (C zeroed, then both halves added into it atomically):
+# 128 to 256 tiles of 64 x 64, ragged M and N, K of 2048 at 128 tiles
+SPLIT2_SHAPES = [(4096, 128, 4096), (1000, 500, 2048), (2000, 300, 4096), (1024, 1024, 4096),
+                 (8192, 64, 8192), (520, 1000, 4096)]
+
+
+def run_default(A, B, dev, a_offset=0):
+    M, K = A.shape
+    N = B.shape[1]
+    _, Ad = strided_on_device(A, K, dev, offset=a_offset)
+    Bd = to_device(B, dev)
+    Cbuf, Cv = nan_output(M, N, N + 3, dev)
+    mm.gemm(Ad, Bd, out=Cv)
+    torch.cuda.synchronize()
+    assert outside_untouched(Cbuf, M, N), "wrote into the gaps of C"
+    return Cv.cpu().numpy()
+
+
+@pytest.mark.parametrize("M,N,K", SPLIT2_SHAPES)
+@pytest.mark.parametrize("a_offset", [0, 1])
+def test_two_k_halves(dev, M, N, K, a_offset):
+    assert mm.mm_gemm_f32_select(M, N, K) == 13  # the halves' tile: 64 x 64 direct
+    A = wl.random_matrix(1700 + M, M, K, "int4")
+    B = wl.random_matrix(1800 + N, K, N, "int4")
+    assert_exact(run_default(A, B, dev, a_offset), A, B)
+    A = wl.random_matrix(1900 + M, M, K, "u11")
+    B = wl.random_matrix(2000 + N, K, N, "u11")
+    assert_tol(run_default(A, B, dev, a_offset), A, B)
+
+
+def test_two_k_halves_deterministic_on_stream(dev):
+    """Random inputs: repeated calls on a non-default stream give the same bits, whichever
+    half adds first."""
+    A = to_device(wl.random_matrix(2101, 4096, 4096, "normal"), dev)
+    B = to_device(wl.random_matrix(2102, 4096, 128, "normal"), dev)
+    s = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):
+        outs = [mm.gemm(A, B) for _ in range(4)]
+    s.synchronize()
+    for C in outs[1:]:
+        assert torch.equal(C.view(torch.int32), outs[0].view(torch.int32))

@@ -90,6 +90,7 @@ int run_gemm(int cfg, int64_t M, int64_t N, int64_t K, const float *A, int64_t l
     a.M = (int)M;
     a.N = (int)N;
     a.K = (int)K;
+    if (cfg < 0 && mm::gemm_split2_ok(M, N, K)) return from_hip("gemm launch", mm::gemm_split2_launch(a, s));
     if (cfg < 0) cfg = mm::gemm_select_config(M, N, K);
     return from_hip("gemm launch", mm::gemm_launch(cfg, a, s));
 }
@@ -296,6 +297,7 @@ const char *mm_gemm_f32_config_name(int cfg) { return mm::gemm_config_name(cfg);
 int mm_gemm_f32_select(int64_t M, int64_t N, int64_t K)
 {
     if (M < 0 || N < 0 || K < 0) return 0;
+    if (mm::gemm_split2_ok(M, N, K)) return mm::gemm_split2_config();
     return mm::gemm_select_config(M, N, K);
 }
 

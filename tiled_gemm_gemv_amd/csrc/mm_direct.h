@@ -184,5 +184,25 @@ __device__ __forceinline__ void direct_store(const GemmArgs &p, int m0, int n0, 
             }
 }
 
+// As direct_store, but adding each element to C with an atomic add (C + gm * ldc + gn):
+// for two K halves of one product summed into a zeroed C, where the result does not
+// depend on which half arrives first (0 + x is exact and x + y == y + x).
+template <class T>
+__device__ __forceinline__ void direct_store_add(const GemmArgs &p, int m0, int n0, int wm0, int wn0, int lane,
+                                                 const f32x16 (&acc)[T::FM][T::FN])
+{
+    const int col_l = lane & 31, row_l = 4 * (lane >> 5);
+#pragma unroll
+    for (int i = 0; i < T::FM; ++i)
+#pragma unroll
+        for (int jj = 0; jj < T::FN; ++jj)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int gm = m0 + wm0 + i * 32 + 8 * (r >> 2) + row_l + (r & 3);
+                const int gn = n0 + wn0 + jj * 32 + col_l;
+                if (gm < p.M && gn < p.N) atomicAdd(p.C + (int64_t)gm * p.ldc + gn, acc[i][jj][r]);
+            }
+}
+
 }  // namespace
 }  // namespace mm

@@ -227,4 +227,40 @@ hipError_t gemm_split_launch(const GemmArgs &a, float *ws, hipStream_t stream)
                            dim3((unsigned)grid_blocks((int64_t)a.M * a.N)), dim3(256), args, 0, stream);
 }
 
+// Without a workspace, K split in two halves added into C: C is zeroed (a fill kernel over
+// its M x N elements), then the two halves run as a batch of two products on the 64 x 64
+// direct tile that both add their tiles into C atomically. With exactly two partial sums
+// the result does not depend on their order (0 + x == x exactly, x + y == y + x), so it
+// is deterministic. Taken where C has 128 to 256 tiles of 64 x 64 (half a workgroup to
+// one per CU unsplit) and each half is long. Measured against the unsplit choice
+// (TFLOP/s): 4096 x 128 x 4096 53 -> 90, 8192 x 64 x 8192 60 -> 93, 16384 x 64 x 4096
+// 60 -> 109, 1024 x 512 x 8192 56 -> 102, 1024 x 1024 x 4096 109 -> 119, 2048 x 512 x 8192
+// 112 -> 129. At 64 tiles or fewer two halves still leave most CUs idle (forced through
+// the workspace path, 4096 x 64 x 4096 lost, 58 -> 50).
+bool gemm_split2_ok(int64_t M, int64_t N, int64_t K)
+{
+    // halves on the lean build; N < 64 stays on the narrow kernels
+    if (K < 2048 || K % 32 != 0 || N < 64 || N % 4 != 0) return false;
+    const int64_t tiles = (M + 63) / 64 * ((N + 63) / 64);
+    // halves of 1024-1040 k on 129-256 tiles measured 1-2% slower (4096 x 256 x 2048,
+    // 2000 x 300 x 2080); on 128 tiles still faster (1000 x 500 x 2048: 51 -> 72)
+    if (K < 4096 && tiles > 128) return false;
+    return tiles >= 128 && tiles <= 256;
+}
+
+int gemm_split2_config() { return kSplitCfg; }
+
+hipError_t gemm_split2_launch(const GemmArgs &a, hipStream_t stream)
+{
+    hipError_t e = zero_fill_launch(a.C, a.M, a.N, a.ldc, stream);
+    if (e != hipSuccess) return e;
+    GemmArgs b = a;
+    b.K = a.K / 2;
+    b.batch = 2;
+    b.sa = b.K;
+    b.sb = (int64_t)b.K * a.ldb;
+    b.sc = 0;
+    return gemm_direct64_add_launch(b, stream);
+}
+
 }  // namespace mm

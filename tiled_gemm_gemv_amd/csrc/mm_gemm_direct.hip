@@ -40,7 +40,8 @@ namespace {
 
 // SB: address the 16-byte lanes of full K-steps from a scalar base (the host checked that
 // the per-lane offsets fit 32 bits; lean builds always do).
-template <class T, bool SB>
+// ADD: add the tile into C atomically instead of storing it (gemm_direct64_add_launch).
+template <class T, bool SB, bool ADD>
 __global__ __launch_bounds__(T::NT) void gemm_f32_direct_kernel(GemmArgs p)
 {
     constexpr bool SADDR = !T::GEN || SB;
@@ -216,10 +217,11 @@ __global__ __launch_bounds__(T::NT) void gemm_f32_direct_kernel(GemmArgs p)
     if (!T::GEN || wide_b) k_loop(std::true_type{});
     else k_loop(std::false_type{});
 
-    direct_store<T>(p, m0, n0, wm0, wn0, lane, acc, [](int gn) { return gn; });
+    if constexpr (ADD) direct_store_add<T>(p, m0, n0, wm0, wn0, lane, acc);
+    else direct_store<T>(p, m0, n0, wm0, wn0, lane, acc, [](int gn) { return gn; });
 }
 
-template <class T, bool SB = true>
+template <class T, bool SB = true, bool ADD = false>
 hipError_t launch_direct(const GemmArgs &a, hipStream_t stream)
 {
     const int64_t tiles = (int64_t)((a.M + T::BM - 1) / T::BM) * ((a.N + T::BN - 1) / T::BN);
@@ -228,7 +230,7 @@ hipError_t launch_direct(const GemmArgs &a, hipStream_t stream)
     if (!grid_for(tiles, gx, gy)) return hipErrorInvalidConfiguration;
     GemmArgs arg = a;
     void *args[] = {&arg};
-    return hipLaunchKernel(reinterpret_cast<const void *>(&gemm_f32_direct_kernel<T, SB>),
+    return hipLaunchKernel(reinterpret_cast<const void *>(&gemm_f32_direct_kernel<T, SB, ADD>),
                            dim3(gx, gy, (unsigned)a.batch), dim3(T::NT), args, 0, stream);
 }
 
@@ -254,14 +256,14 @@ namespace {
 // 8 MFMAs per K-step). Where K % 32 == 0 too, K-steps of 32 in half as many stages (the
 // same LDS): whole 128-byte A lines and twice the MFMAs per barrier, 1-8% faster on the
 // 128 x 128 and 64 x 64 tiles.
-template <int BM, int BN, int WM, int WN, int NS>
+template <int BM, int BN, int WM, int WN, int NS, bool ADD = false>
 hipError_t launch_lean_or_general(const GemmArgs &a, hipStream_t stream)
 {
     if (direct_f32_wide_ok(a) && a.K % 32 == 0)
-        return launch_direct<DirectF32<BM, BN, WM, WN, NS / 2, false, 32>>(a, stream);
-    if (direct_f32_wide_ok(a)) return launch_direct<DirectF32<BM, BN, WM, WN, NS, false>>(a, stream);
-    return direct_f32_offsets_fit(a) ? launch_direct<DirectF32<BM, BN, WM, WN, NS, true>, true>(a, stream)
-                                     : launch_direct<DirectF32<BM, BN, WM, WN, NS, true>, false>(a, stream);
+        return launch_direct<DirectF32<BM, BN, WM, WN, NS / 2, false, 32>, true, ADD>(a, stream);
+    if (direct_f32_wide_ok(a)) return launch_direct<DirectF32<BM, BN, WM, WN, NS, false>, true, ADD>(a, stream);
+    return direct_f32_offsets_fit(a) ? launch_direct<DirectF32<BM, BN, WM, WN, NS, true>, true, ADD>(a, stream)
+                                     : launch_direct<DirectF32<BM, BN, WM, WN, NS, true>, false, ADD>(a, stream);
 }
 
 }  // namespace
@@ -282,6 +284,11 @@ hipError_t gemm_direct_launch(DirectTile t, const GemmArgs &a, hipStream_t strea
         return launch_lean_or_general<64, 64, 32, 32, 4>(a, stream);
     }
     return hipErrorInvalidValue;
+}
+
+hipError_t gemm_direct64_add_launch(const GemmArgs &a, hipStream_t stream)
+{
+    return launch_lean_or_general<64, 64, 32, 32, 4, true>(a, stream);
 }
 
 }  // namespace mm

@@ -98,6 +98,11 @@ hipError_t gemm_launch(int cfg, const GemmArgs &a, hipStream_t stream);
 int gemm_split_chunks(int64_t M, int64_t N, int64_t K);
 int64_t gemm_split_ws_floats(int64_t M, int64_t N, int64_t K);
 hipError_t gemm_split_launch(const GemmArgs &a, float *ws, hipStream_t stream);
+// K split in two halves without a workspace (mm_gemm.hip): true where mm_gemm_f32 takes
+// it, and the launch (C zeroed, then both halves added into it).
+bool gemm_split2_ok(int64_t M, int64_t N, int64_t K);
+int gemm_split2_config();  // the config index of the halves' tile
+hipError_t gemm_split2_launch(const GemmArgs &a, hipStream_t stream);
 
 // Narrow-C GEMM (mm_gemm_skinny.hip): 16 x 64 tiles of C, K split over W waves
 // per workgroup, L / (column blocks) 16-deep chunks per wave per round. Correct for
@@ -111,6 +116,9 @@ hipError_t gemm_skinny_launch(const GemmArgs &a, hipStream_t stream);
 enum class DirectTile { T256, T128, T64S8, T64S4 };
 bool direct_f32_wide_ok(const GemmArgs &a);
 hipError_t gemm_direct_launch(DirectTile t, const GemmArgs &a, hipStream_t stream);
+// The 64 x 64 direct tile (4 stages) with an epilogue that adds each tile into C
+// atomically; a.batch problems may share C (sc = 0).
+hipError_t gemm_direct64_add_launch(const GemmArgs &a, hipStream_t stream);
 
 // GEMM for C with few columns (mm_gemm_cols.hip): one wave per row, B staged in LDS;
 // correct for any shape, meant for N <= 4.
