@@ -180,17 +180,21 @@ class ClockProbe:
         self.samples = [v for t, v in timed if t >= total / 2]
 
     def summary(self, tflops, peak_tflops_at_max):
+        """The clock readings and the peak they imply; with a measured rate `tflops`
+        (None: no rate was timed), also that rate's share of the peak at this clock."""
         if not self.samples:
             return {"gfxclk_mhz": None, "why": self.why or "no sample taken"}
         f = float(np.median(self.samples))
         peak = peak_tflops_at_max * (f * 1e6 / rl.MI355X_PEAK_SCLK_HZ)
-        return {"gfxclk_mhz": round(f, 1), "gfxclk_mhz_min": round(min(self.samples), 1),
-                "gfxclk_mhz_max": round(max(self.samples), 1), "samples": len(self.samples),
-                "source": f"amdsmi GPU metrics (current clock of each XCD, averaged), sampled "
-                          f"in the second half of {self.seconds:.1f} s of the same kernel run "
-                          f"back to back after the timed steps",
-                "peak_at_clock": round(peak, 2),
-                "frac_at_clock": round(tflops / peak, 4)}
+        out = {"gfxclk_mhz": round(f, 1), "gfxclk_mhz_min": round(min(self.samples), 1),
+               "gfxclk_mhz_max": round(max(self.samples), 1), "samples": len(self.samples),
+               "source": f"amdsmi GPU metrics (current clock of each XCD, averaged), sampled "
+                         f"in the second half of {self.seconds:.1f} s of the same kernel run "
+                         f"back to back after the timed steps",
+               "peak_at_clock": round(peak, 2)}
+        if tflops is not None:
+            out["frac_at_clock"] = round(tflops / peak, 4)
+        return out
 
     def close(self):
         if self.inited:
@@ -266,7 +270,7 @@ def main():
             clock.measure(torch, stream, lambda: mm.mm_gemm_bf16(M, N, K, A16, K, B16, N, C, N, stream),
                           args.clock_seconds, 1e-3)
             torch.cuda.synchronize()
-            c = clock.summary(0.0, rl.MI355X_16BIT_MFMA_PEAK / 1e12)
+            c = clock.summary(None, rl.MI355X_16BIT_MFMA_PEAK / 1e12)  # no rate timed here
             clock.close()
             log(f"h16 clock: {json.dumps(c)}")
         return

@@ -63,6 +63,12 @@ def test_clock_summary_scales_the_peak():
     assert s["gfxclk_mhz_min"] == 1200.0 and s["gfxclk_mhz_max"] == 2400.0
 
 
+def test_clock_summary_without_a_rate_has_no_fraction():
+    s = make_probe([1900.0, 1900.0]).summary(None, 2500.0)
+    assert s["gfxclk_mhz"] == 1900.0 and "frac_at_clock" not in s
+    assert s["peak_at_clock"] == pytest.approx(2500.0 * 1900 / 2400, abs=0.01)  # rounded to 0.01
+
+
 def test_clock_summary_without_samples_says_why():
     assert make_probe([], why="amdsmi: no device") .summary(1.0, 157.3) == \
         {"gfxclk_mhz": None, "why": "amdsmi: no device"}
