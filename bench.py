@@ -213,7 +213,7 @@ def main():
     ap.add_argument("--gemv-reps", type=int, default=400)
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="target length of the oracle's timed sample")
-    ap.add_argument("--only", choices=["gemm", "gemv", "copy", "h16", "conv"], default=None,
+    ap.add_argument("--only", choices=["gemm", "gemv", "copy", "h16", "conv", "split"], default=None,
                     help="profiling helper: launch only this kernel --steps times")
     ap.add_argument("--clock-seconds", type=float, default=None,
                     help="length of the clock phase (default 2.5 s after the timed steps; "
@@ -273,6 +273,22 @@ def main():
             c = clock.summary(None, rl.MI355X_16BIT_MFMA_PEAK / 1e12)  # no rate timed here
             clock.close()
             log(f"h16 clock: {json.dumps(c)}")
+        return
+
+    if args.only == "split":
+        # the fully-connected layer on a batch of 128 (4096 x 128 x 4096): mm_gemm_f32 (two K
+        # halves added into a zeroed C) and mm_gemm_f32_ws (4 chunks, then the sum)
+        SM, SN, SK = 4096, 128, 4096
+        A = torch.randn(SM, SK, device=dev)
+        B = torch.randn(SK, SN, device=dev) / 64.0
+        C = torch.empty((SM, SN), dtype=torch.float32, device=dev)
+        ws = mm.gemm_workspace(SM, SN, SK, dev)
+        for _ in range(args.steps):
+            mm.mm_gemm_f32(SM, SN, SK, A, SK, B, SN, C, SN, stream)
+        for _ in range(args.steps):
+            mm.mm_gemm_f32_ws(SM, SN, SK, A, SK, B, SN, C, SN, ws, ws.numel(), stream)
+        torch.cuda.synchronize()
+        log(f"split: {args.steps} mm_gemm_f32 and {args.steps} mm_gemm_f32_ws calls at {SM}x{SN}x{SK}")
         return
 
     if args.only == "conv":
