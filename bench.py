@@ -105,12 +105,21 @@ def cpu_model():
     return platform.processor() or "unknown"
 
 
-def host_threads():
+# A GPU host shares its cores among its GPUs; one GPU's share is 16 threads, whatever
+# the affinity mask of the process shows. The oracle runs on the smaller of the two, and
+# the bench line states both.
+HOST_SHARE = 16
+
+
+def affinity_cpus():
     try:
-        n = len(os.sched_getaffinity(0))
+        return len(os.sched_getaffinity(0))
     except AttributeError:
-        n = os.cpu_count() or 1
-    return max(1, min(n, 16))
+        return os.cpu_count() or 1
+
+
+def host_threads():
+    return max(1, min(affinity_cpus(), HOST_SHARE))
 
 
 class ClockProbe:
@@ -494,6 +503,8 @@ def main():
             "value": round(cpu_tflops, 5),
             "unit": "TFLOP/s",
             "cores": threads,
+            "affinity_cpus": affinity_cpus(),
+            "threads_rule": f"min(len(os.sched_getaffinity(0)), {HOST_SHARE}): the host's per-GPU share",
             "kind": "oracle",
             "sample": f"{len(rows)} sampled rows (all 14336 columns, K=4096) of the projection "
                       f"GEMM, fp64 accumulation, {t_cpu:.2f} s on {cpu_model()}",

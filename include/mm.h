@@ -260,8 +260,9 @@ int mm_gemm_f16_config(int cfg, int64_t M, int64_t N, int64_t K,
  *   y              N x K x P x Q, packed, written. May be NULL if it has no elements.
  * Products are fp32, accumulated in fp32 on the matrix cores in an order of the
  * kernel's choosing; the im2col matrix is gathered on the fly, never stored, so no
- * workspace is used. C == 0: y is filled with zeros. No output elements: nothing is
- * enqueued.
+ * workspace is used. C == 0, H == 0 or W == 0 (x has no elements; padding may still give
+ * P, Q >= 1, and every tap then reads the padding): y is filled with zeros. No output
+ * elements: nothing is enqueued.
  * Errors: MM_ERR_INVALID_ARG for a negative size, a stride, dilation or filter size
  * below 1, negative padding, a filter that does not fit the padded input (P or Q
  * would be below 1), a NULL or unaligned pointer that is used, or sizes beyond the

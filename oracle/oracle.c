@@ -289,7 +289,9 @@ int oracle_conv2d_f64(int64_t N, int64_t C, int64_t H, int64_t W, int64_t K, int
     if (H + 2 * ph - dh * (R - 1) - 1 < 0 || W + 2 * pw - dw * (S - 1) - 1 < 0) return ORACLE_BAD_ARG;
     const int64_t pairs = N * K;
     if (pairs == 0 || P * Q == 0) return ORACLE_OK;
-    if (!y || (C > 0 && (!x || !w))) return ORACLE_BAD_ARG;
+    /* x may be absent when it has no elements (C, H or W is 0): every tap then reads
+     * the zero padding */
+    if (!y || (C > 0 && !w) || (C * H * W > 0 && !x)) return ORACLE_BAD_ARG;
     if (threads < 1) threads = 1;
     if (threads > pairs) threads = (int)pairs;
 

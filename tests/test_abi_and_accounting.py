@@ -314,3 +314,24 @@ def test_conv_accounting():
     assert rl.im2col_matrix_bytes(1, 2, 3, 3, 3, 3) == 4 * 18 * 9
     # a 1x1 convolution of one image is the GEMM of its filters with its C x HW matrix
     assert rl.conv_flops(1, 256, 64, 1, 1, 56, 56) == rl.gemm_flops(64, 56 * 56, 256)
+
+
+@pytest.mark.skipif(os.path.exists("/dev/kfd"),
+                    reason="a GPU is present: the call would launch; the GPU suite checks its zeros")
+def test_conv_empty_input_plane_returns_a_status(lib):
+    # H = W = 0 with padding: P, Q >= 1 and every tap reads padding. The call must come
+    # back with a status (here, without a GPU, the zero fill's launch error), not end the
+    # process. It runs in a child process so that a crash fails this test alone.
+    import subprocess
+    import sys
+    code = (
+        "import ctypes, sys\n"
+        f"lib = ctypes.CDLL({mm_build.LIB!r})\n"
+        "f = lib.mm_conv2d_f32\n"
+        "f.restype = ctypes.c_int\n"
+        "f.argtypes = [ctypes.c_int64] * 13 + [ctypes.c_void_p] * 4\n"
+        f"st = f(1, 1, 0, 0, 1, 1, 1, 1, 1, 1, 1, 1, 1, None, {FAKE}, {FAKE}, None)\n"
+        "print(st)\n")
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0, f"the call ended the process: rc {r.returncode}, {r.stderr[-500:]}"
+    assert int(r.stdout.split()[-1]) in (mm.MM_OK, mm.MM_ERR_NO_DEVICE, mm.MM_ERR_LAUNCH)

@@ -179,3 +179,22 @@ def test_repeated_calls_identical(dev):
         again = mm.conv2d(xd, wd, cw.stride, cw.pad, cw.dilation)
         torch.cuda.synchronize()
         assert torch.equal(first, again)
+
+
+@pytest.mark.parametrize("H,W", [(0, 0), (0, 4), (3, 0)])
+def test_empty_input_plane_gives_zeros(dev, H, W):
+    # an input plane with no pixels but padding that still gives outputs: every tap of
+    # the sum lands in the zero padding, so y is all zeros, as the oracle computes
+    N, C, K, R, S, pad = 2, 3, 4, 3, 3, (2, 2)
+    x = np.zeros((N, C, H, W), np.float32)
+    w = wl.random_matrix(2104, K, C * R * S, "int4").reshape(K, C, R, S)
+    y64, _ = oracle.conv2d(x, w, (1, 1), pad, (1, 1))
+    P, Q = y64.shape[2:]
+    assert P >= 1 and Q >= 1
+    y = torch.full((N, K, P, Q), float("nan"), dtype=torch.float32, device=dev)
+    mm.conv2d(torch.empty((N, C, H, W), dtype=torch.float32, device=dev), to_device(w, dev),
+              pad=pad, out=y)
+    torch.cuda.synchronize()
+    r = verify.exact(y.cpu().numpy(), y64)
+    assert r, r
+    assert (y == 0).all().item()

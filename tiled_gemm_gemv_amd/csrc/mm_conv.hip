@@ -392,12 +392,13 @@ int conv_choose_config(const ConvArgs &a)
     return conv_select_config(a.K, a.N * a.P * a.Q, a.C * a.R * a.S);
 }
 
-// Shapes are validated by the caller: every size >= 1 (C may be 0: then y is zeroed),
-// P and Q as the definition gives them, and the limits stated for Im2colOperands.
+// Shapes are validated by the caller: N, K, P, Q >= 1, P and Q as the definition gives
+// them, and the limits stated for Im2colOperands. C, H or W may be 0: every tap of the
+// sum then reads padding (or there is none), so y is zeroed.
 hipError_t conv_launch(int cfg, const ConvArgs &a, hipStream_t stream)
 {
     const int64_t PQ = a.P * a.Q, HW = a.H * a.W, CHW = a.C * HW, KPQ = a.K * PQ;
-    if (a.C == 0) return zero_fill_launch(a.y, a.N * a.K, PQ, PQ, stream);
+    if (CHW == 0) return zero_fill_launch(a.y, a.N * a.K, PQ, PQ, stream);
 
     if (cfg < 0) cfg = conv_choose_config(a);
     if (conv_is_batched_gemm(a)) {

@@ -63,22 +63,21 @@ template <class T>
 __device__ __forceinline__ int swz_b(int krow) { return ((krow / (T::BK / 2)) & 1) * 8; }
 
 // VEC bytes per lane from src into LDS at lds_addr + VEC * lane (lds_addr wave-uniform).
-// M0 is set and used inside one asm statement and not declared clobbered: the kernels
-// built on this header use M0 nowhere else (every M0 reference in their code is this
-// s_mov_b32 followed by its load), which their ISA was checked for. A global load with
-// LDS = 1 that reads M0 needs one wait state after the SALU write of M0 (CDNA's table of
-// manually inserted wait states); the hazard recognizer does not look inside an asm
-// string, so the s_nop is written here (the compiler's own builtin leaves at least one
-// instruction there too).
+// The LDS address travels in M0 as an operand of the asm statement ("{m0}"), so the
+// compiler writes M0 itself right before each load and knows the load reads it. A global
+// load with LDS = 1 that reads M0 needs one wait state after the SALU write of M0 (CDNA's
+// table of manually inserted wait states); the hazard recognizer does not look inside an
+// asm string, so the s_nop is written at its start (the compiler's own builtin leaves at
+// least one instruction there too).
 template <int VEC>
 __device__ __forceinline__ void load_to_lds(unsigned lds_addr, const float *src)
 {
     if constexpr (VEC == 16)
-        asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
-                     :: "s"(__builtin_amdgcn_readfirstlane(lds_addr)), "v"(src) : "memory");
+        asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                     :: "v"(src), "{m0}"(__builtin_amdgcn_readfirstlane(lds_addr)) : "memory");
     else
-        asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off"
-                     :: "s"(__builtin_amdgcn_readfirstlane(lds_addr)), "v"(src) : "memory");
+        asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, off"
+                     :: "v"(src), "{m0}"(__builtin_amdgcn_readfirstlane(lds_addr)) : "memory");
 }
 
 // 16 bytes per lane from base + voff into LDS at lds_addr + 16 * lane: base and lds_addr
@@ -88,8 +87,8 @@ __device__ __forceinline__ void load_to_lds(unsigned lds_addr, const float *src)
 // 1.7% of the 256 x 256 tile's time at the projection shape).
 __device__ __forceinline__ void load_to_lds_s16(unsigned lds_addr, const float *base, unsigned voff)
 {
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
-                 :: "s"(lds_addr), "v"(voff), "s"(base) : "memory");
+    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+                 :: "v"(voff), "s"(base), "{m0}"(lds_addr) : "memory");
 }
 
 template <int N>

@@ -416,12 +416,14 @@ typedef __attribute__((address_space(3))) char lds_char;
 
 // 16 bytes per lane from base + voff into LDS at lds_addr + 16 * lane (lds_addr and base
 // wave-uniform, in scalar registers; voff the lane's byte offset), so that a load takes no
-// vector instruction. The s_nop is the one wait state a global load with LDS = 1 needs
-// after an SALU write of M0 (the hazard recognizer does not look inside an asm string).
+// vector instruction. The LDS address is the asm statement's M0 operand ("{m0}"), which
+// the compiler writes right before the load; the s_nop is the one wait state a global load
+// with LDS = 1 needs after an SALU write of M0 (the hazard recognizer does not look inside
+// an asm string).
 __device__ __forceinline__ void load_to_lds_s(unsigned lds_addr, const unsigned short *base, unsigned voff)
 {
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
-                 :: "s"(lds_addr), "v"(voff), "s"(base) : "memory");
+    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+                 :: "v"(voff), "s"(base), "{m0}"(lds_addr) : "memory");
 }
 
 template <int N>
