@@ -38,8 +38,10 @@
  *     only enqueue work and return; they never synchronise and never allocate.
  *     Errors raised by the device while the work runs surface at the caller's
  *     next synchronisation of that stream.
- *   - Threads: the library keeps no mutable global state; calls from several
- *     host threads, on any streams, are safe.
+ *   - Threads: the library keeps no mutable global state (except the per-device
+ *     address of mm_gemm_f32_ws_static's scratch, looked up once under a lock); calls
+ *     from several host threads, on any streams, are safe (mm_gemm_f32_ws_static:
+ *     see there).
  *   - Return value: an mm_status. Arguments are checked on the host before any
  *     HIP call; an invalid call enqueues nothing.
  */
@@ -203,6 +205,29 @@ int64_t mm_gemm_f32_workspace_bytes(int64_t M, int64_t N, int64_t K);
 int mm_gemm_f32_ws(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda,
                    const float *B, int64_t ldb, float *C, int64_t ldc,
                    void *workspace, int64_t workspace_bytes, void *stream);
+
+/*
+ * mm_gemm_f32_ws_static: mm_gemm_f32_ws without a caller workspace, for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation). The K split runs in the library's own static device
+ * scratch of MM_STATIC_SCRATCH_BYTES, one per GPU, held until the process ends; the call
+ * itself allocates nothing. Results are bit-identical to mm_gemm_f32_ws's for the same
+ * arguments (the same kernels in the same order).
+ *   Arguments, layout, ownership and zero-size cases as for mm_gemm_f32. `stream` must
+ *   belong to the current device (NULL: the current device's default stream).
+ * Shapes that mm_gemm_f32_ws serves without its workspace (mm_gemm_f32_workspace_bytes is
+ * 0) run mm_gemm_f32's kernels and touch no scratch.
+ * Every call on one GPU shares that GPU's scratch, and it keeps the last call's contents
+ * (each call overwrites what it reads): calls on one GPU that may overlap in time (on
+ * different streams, or from several host threads without ordering) race and give wrong
+ * results. Keep them on one stream.
+ * Errors: as for mm_gemm_f32, plus MM_ERR_INVALID_ARG when the split needs more than
+ * MM_STATIC_SCRATCH_BYTES (mm_gemm_f32_workspace_bytes above it; checked before any HIP
+ * call), a stream of another device than the current one, or a device index above 63.
+ */
+#define MM_STATIC_SCRATCH_BYTES (16 * 1024 * 1024)
+int mm_gemm_f32_ws_static(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda,
+                          const float *B, int64_t ldb, float *C, int64_t ldc, void *stream);
 
 /*
  * mm_gemm_bf16 / mm_gemm_f16: C = A x B with 16-bit inputs and fp32 accumulation

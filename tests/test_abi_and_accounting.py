@@ -335,3 +335,28 @@ def test_conv_empty_input_plane_returns_a_status(lib):
     r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=120)
     assert r.returncode == 0, f"the call ended the process: rc {r.returncode}, {r.stderr[-500:]}"
     assert int(r.stdout.split()[-1]) in (mm.MM_OK, mm.MM_ERR_NO_DEVICE, mm.MM_ERR_LAUNCH)
+
+
+def test_static_scratch_checks_before_any_launch(lib):
+    f = lib.mm_gemm_f32_ws_static
+    # a split that needs more than the static scratch (B padded to 256 columns)
+    assert mm.mm_gemm_f32_workspace_bytes(4096, 255, 16384) > mm.MM_STATIC_SCRATCH_BYTES
+    assert f(4096, 255, 16384, FAKE, 16384, FAKE, 255, FAKE, 255, None) == mm.MM_ERR_INVALID_ARG
+    assert "static scratch" in mm.mm_last_error()
+    # the argument checks of mm_gemm_f32, on split and unsplit shapes
+    for i, why in [(3, "A is NULL"), (5, "B is NULL"), (7, "C is NULL")]:
+        for shape in ((4096, 64, 4096), (300, 16, 4096)):
+            args = [*shape, FAKE, shape[2], FAKE, shape[1], FAKE, shape[1]]
+            args[i] = None
+            assert f(*args, None) == mm.MM_ERR_INVALID_ARG
+            assert why in mm.mm_last_error()
+    assert f(4096, 64, 4096, FAKE, 100, FAKE, 64, FAKE, 64, None) == mm.MM_ERR_INVALID_ARG
+    assert "lda" in mm.mm_last_error()
+    # nothing to compute: no HIP call
+    assert f(0, 64, 4096, None, 4096, FAKE, 64, None, 64, None) == mm.MM_OK
+    # the header's size and the binding's agree; every split of N % 4 == 0 fits
+    text = open(os.path.join(ROOT, "include", "mm.h")).read()
+    m = re.search(r"#define MM_STATIC_SCRATCH_BYTES \((\d+) \* (\d+) \* (\d+)\)", text)
+    assert m and int(m[1]) * int(m[2]) * int(m[3]) == mm.MM_STATIC_SCRATCH_BYTES
+    for M, N, K in [(16320, 64, 2048), (4096, 256, 4096), (4096, 128, 8192), (255 * 64, 28, 2048)]:
+        assert 0 < mm.mm_gemm_f32_workspace_bytes(M, N, K) <= mm.MM_STATIC_SCRATCH_BYTES

@@ -89,6 +89,8 @@ def load():
     lib.mm_gemm_f32_workspace_bytes.restype = i64
     lib.mm_gemm_f32_ws.argtypes = [i64, i64, i64, vp, i64, vp, i64, vp, i64, vp, i64, vp]
     lib.mm_gemm_f32_ws.restype = ci
+    lib.mm_gemm_f32_ws_static.argtypes = [i64, i64, i64, vp, i64, vp, i64, vp, i64, vp]
+    lib.mm_gemm_f32_ws_static.restype = ci
     lib.mm_gemv_t_f32_workspace_bytes.argtypes = [i64, i64]
     lib.mm_gemv_t_f32_workspace_bytes.restype = i64
     lib.mm_gemv_t_f32_ws.argtypes = [i64, i64, vp, vp, vp, vp, i64, vp]
@@ -234,6 +236,18 @@ def mm_gemm_f32_ws(M, N, K, A, lda, B, ldb, C, ldc, workspace, workspace_bytes, 
                               workspace_bytes, _stream(stream)), "mm_gemm_f32_ws")
 
 
+def mm_gemm_f32_ws_static(M, N, K, A, lda, B, ldb, C, ldc, stream=None):
+    """mm_gemm_f32_ws with the library's static device scratch (MM_STATIC_SCRATCH_BYTES per
+    GPU) as its workspace: allocates nothing. Calls that overlap on one GPU race.
+    Raises MMError."""
+    lib = load()
+    _check(lib.mm_gemm_f32_ws_static(M, N, K, _addr(A), lda, _addr(B), ldb, _addr(C), ldc,
+                                     _stream(stream)), "mm_gemm_f32_ws_static")
+
+
+MM_STATIC_SCRATCH_BYTES = 16 * 1024 * 1024  # as include/mm.h defines it
+
+
 def mm_gemv_t_f32_workspace_bytes(M, N):
     """Bytes of workspace mm_gemv_t_f32_ws needs for (M, N); -1 for invalid sizes."""
     return load().mm_gemv_t_f32_workspace_bytes(M, N)
@@ -351,7 +365,8 @@ def gemm_workspace(M, N, K, device):
 def gemm(A, B, out=None, config=None, stream=None, workspace=None):
     """out = A @ B for fp32 GPU tensors (any row strides, unit column stride). With
     `workspace` (a device tensor of at least mm_gemm_f32_workspace_bytes bytes, e.g. from
-    gemm_workspace) it runs mm_gemm_f32_ws."""
+    gemm_workspace) it runs mm_gemm_f32_ws; with workspace="static", mm_gemm_f32_ws_static
+    (the library's own device scratch; calls that overlap on one GPU race)."""
     import torch
     lda = _matrix(A, "A")
     ldb = _matrix(B, "B")
@@ -370,7 +385,11 @@ def gemm(A, B, out=None, config=None, stream=None, workspace=None):
     if workspace is not None and config is not None:
         raise ValueError("a workspace and a forced config do not go together")
     with torch.cuda.device(A.device):
-        if workspace is not None:
+        if isinstance(workspace, str):
+            if workspace != "static":
+                raise ValueError(f"workspace must be a tensor or 'static', got {workspace!r}")
+            mm_gemm_f32_ws_static(M, N, K, A, lda, B, ldb, out, ldc, stream)
+        elif workspace is not None:
             mm_gemm_f32_ws(M, N, K, A, lda, B, ldb, out, ldc, workspace,
                            _workspace_bytes(workspace, A.device), stream)
         elif config is None:

@@ -283,6 +283,30 @@ int mm_gemm_f32_ws(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda,
                                                                 static_cast<hipStream_t>(stream)));
 }
 
+int mm_gemm_f32_ws_static(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda, const float *B,
+                          int64_t ldb, float *C, int64_t ldc, void *stream)
+{
+    const int64_t need = mm_gemm_f32_workspace_bytes(M, N, K);
+    if (need <= 0) return run_gemm(-1, M, N, K, A, lda, B, ldb, C, ldc, stream);  // no scratch used
+    const int st = check_gemm(M, N, K, A, lda, B, ldb, C, ldc);
+    if (st != MM_OK) return st;
+    if (need > MM_STATIC_SCRATCH_BYTES)
+        return invalid("the K split of this shape needs more than the MM_STATIC_SCRATCH_BYTES of static scratch");
+    mm::GemmArgs a;
+    a.A = A;
+    a.B = B;
+    a.C = C;
+    a.lda = lda;
+    a.ldb = ldb;
+    a.ldc = ldc;
+    a.M = (int)M;
+    a.N = (int)N;
+    a.K = (int)K;
+    const int r = mm::gemm_split_static_launch(a, static_cast<hipStream_t>(stream));
+    if (r != MM_OK) set_error_text(mm::static_ws_error());
+    return r;
+}
+
 int mm_gemm_f32_config(int cfg, int64_t M, int64_t N, int64_t K, const float *A, int64_t lda,
                        const float *B, int64_t ldb, float *C, int64_t ldc, void *stream)
 {

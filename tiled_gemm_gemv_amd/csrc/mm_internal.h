@@ -98,6 +98,10 @@ hipError_t gemm_launch(int cfg, const GemmArgs &a, hipStream_t stream);
 int gemm_split_chunks(int64_t M, int64_t N, int64_t K);
 int64_t gemm_split_ws_floats(int64_t M, int64_t N, int64_t K);
 hipError_t gemm_split_launch(const GemmArgs &a, float *ws, hipStream_t stream);
+// The K split with the library's static device scratch as its workspace
+// (mm_static_ws.hip): an mm_status (text of a failure from static_ws_error()).
+int gemm_split_static_launch(const GemmArgs &a, hipStream_t stream);
+const char *static_ws_error();
 // K split in two halves without a workspace (mm_gemm.hip): true where mm_gemm_f32 takes
 // it, and the launch (C zeroed, then both halves added into it).
 bool gemm_split2_ok(int64_t M, int64_t N, int64_t K);
