@@ -229,7 +229,9 @@ int oracle_gemv_f64(int64_t M, int64_t N, const float *A, int64_t lda,
  *   y[n][k][p][q] = sum over c < C, r < R, s < S of
  *                   x[n][c][p*sh + r*dh - ph][q*sw + s*dw - pw] * w[k][c][r][s]
  *
- * with x taken as 0 outside 0 <= h < H, 0 <= w < W, and P = (H + 2 ph - dh (R - 1) - 1)
+ * with x taken as 0 outside 0 <= h < H, 0 <= w < W (a padded tap still multiplies that
+ * zero by its filter value, as the matrix the layer is recast as holds it), and
+ * P = (H + 2 ph - dh (R - 1) - 1)
  * / sh + 1, Q likewise (integer division; P, Q >= 1 here). Layouts, all packed:
  * x is N x C x H x W, w is K x C x R x S, y and s_out are N x K x P x Q. Each output
  * is summed in fp64 in ascending (c, r, s) order; s_out gets the sum of |products|.
@@ -258,9 +260,13 @@ static void conv_pairs(const struct conv_job *jb)
                         for (int64_t s = 0; s < jb->S; ++s) {
                             const int64_t h = p * jb->sh + r * jb->dh - jb->ph;
                             const int64_t v = q * jb->sw + s * jb->dw - jb->pw;
-                            if (h < 0 || h >= jb->H || v < 0 || v >= jb->W) continue;
-                            const double prod = (double)xn[(c * jb->H + h) * jb->W + v] *
-                                                (double)wk[(c * jb->R + r) * jb->S + s];
+                            /* a tap in the padding reads a zero of the padded input (an
+                             * explicit zero of the matrix the convolution is recast as);
+                             * with finite filters it adds nothing, with an infinite or
+                             * NaN filter value the product is NaN (IEEE 0 * inf) */
+                            const int inside = h >= 0 && h < jb->H && v >= 0 && v < jb->W;
+                            const double xv = inside ? (double)xn[(c * jb->H + h) * jb->W + v] : 0.0;
+                            const double prod = xv * (double)wk[(c * jb->R + r) * jb->S + s];
                             acc += prod;
                             mag += fabs(prod);
                         }

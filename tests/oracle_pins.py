@@ -426,5 +426,25 @@ def pin_conv_all_ones_counts_taps(orc):
             assert y[0, 0, p, q] == C * rows * cols == s[0, 1, p, q]
 
 
+def pin_conv_ieee_specials_and_padding(orc):
+    """IEEE values through the convolution, read as the product of the filters with the
+    input's im2col matrix, whose padded entries are zeros: an infinite filter tap that
+    lands in the padding multiplies a zero (NaN), one that lands inside multiplies the
+    pixel (infinite); a NaN pixel makes every output whose window holds it NaN."""
+    x = np.full((1, 1, 1, 1), 5.0, np.float32)
+    w = np.ones((2, 1, 3, 3), np.float32)
+    w[0, 0, 0, 0] = np.inf   # the corner tap: in the padding for the only output
+    w[1, 0, 1, 1] = -np.inf  # the centre tap: on the pixel
+    y, _ = orc.conv2d(x, w, pad=(1, 1))
+    assert y.shape == (1, 2, 1, 1)
+    assert np.isnan(y[0, 0, 0, 0]) and y[0, 1, 0, 0] == -np.inf
+    x = np.arange(1 * 2 * 5 * 6, dtype=np.float32).reshape(1, 2, 5, 6) % 7 - 3
+    x[0, 1, 2, 3] = np.nan
+    y, _ = orc.conv2d(x, np.ones((1, 2, 3, 3), np.float32), pad=(1, 1))
+    for p in range(5):
+        for q in range(6):
+            assert np.isnan(y[0, 0, p, q]) == (abs(p - 2) <= 1 and abs(q - 3) <= 1), (p, q)
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]
 CHEAP_PINS = [p for p in ALL_PINS if p is not pin_page_operation_counts]

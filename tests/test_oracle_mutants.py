@@ -49,8 +49,11 @@ MUTANTS = [
     ("gemv_row_stride_n", "const float *arow = jb->A + i * jb->lda;",
      "const float *arow = jb->A + i * jb->N;"),
     ("gemv_subtracts", "acc += p;", "acc -= p;"),
-    ("conv_no_low_padding_check", "if (h < 0 || h >= jb->H || v < 0 || v >= jb->W) continue;",
-     "if (h >= jb->H || v >= jb->W || h < 0) continue;"),
+    ("conv_no_low_padding_check", "const int inside = h >= 0 && h < jb->H && v >= 0 && v < jb->W;",
+     "const int inside = h >= 0 && h < jb->H && v < jb->W;"),
+    ("conv_skips_padded_taps",
+     "const double xv = inside ? (double)xn[(c * jb->H + h) * jb->W + v] : 0.0;",
+     "if (!inside) continue;\n                            const double xv = (double)xn[(c * jb->H + h) * jb->W + v];"),
     ("conv_ignores_stride", "const int64_t h = p * jb->sh + r * jb->dh - jb->ph;",
      "const int64_t h = p + r * jb->dh - jb->ph;"),
     ("conv_ignores_dilation", "const int64_t v = q * jb->sw + s * jb->dw - jb->pw;",
