@@ -238,8 +238,9 @@ int mm_gemm_f32_ws_static(int64_t M, int64_t N, int64_t K, const float *A, int64
  * exact in fp32, so C is the fp32 GEMM of the inputs' exact values, summed on the
  * matrix cores in fp32.
  * Arguments, layout, ownership, stream, zero-size cases and errors as for
- * mm_gemm_f32, except: A and B must be 2-byte aligned (16-byte-aligned rows with
- * leading dimensions divisible by 8 for A and 4 for B take the fast loads).
+ * mm_gemm_f32, except: A and B must be 2-byte aligned. Shapes with K >= 32 and with
+ * N >= 64 or N % 8 == 0 take the pipeline that loads panels straight into LDS, at any
+ * 2-byte alignment and leading dimension; others take register-staged tiles.
  *   mm_gemm_h16_num_configs / mm_gemm_h16_config_name / mm_gemm_h16_select: the
  *     tile configurations of these two calls, as for the fp32 GEMM.
  *   mm_gemm_bf16_config / mm_gemm_f16_config: the calls with config `cfg` forced.

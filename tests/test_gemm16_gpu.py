@@ -13,7 +13,7 @@ import oracle
 from oracle import verify
 import tiled_gemm_gemv_amd as mm
 import workloads as wl
-from gpu_helpers import require_gpu
+from gpu_helpers import nan_output, outside_untouched, require_gpu
 
 pytestmark = pytest.mark.gpu
 
@@ -62,12 +62,20 @@ def on_device(bits, fmt, dev, ld=None, offset=0):
     return view
 
 
-def run(A, B, fmt, dev, cfg=None, lda=None, ldb=None, offs=(0, 0)):
+def run(A, B, fmt, dev, cfg=None, lda=None, ldb=None, offs=(0, 0), ldc=None):
+    """C = A B on the GPU after rounding A and B to the 16-bit format; with ldc, C is a view
+    with that row stride into a NaN-filled buffer, whose gaps must stay NaN."""
     Ab, Af = quantize(A, fmt)
     Bb, Bf = quantize(B, fmt)
+    M, N = A.shape[0], B.shape[1]
+    out = buf = None
+    if ldc is not None:
+        buf, out = nan_output(M, N, ldc, dev)
     C = mm.gemm16(on_device(Ab, fmt, dev, lda, offs[0]), on_device(Bb, fmt, dev, ldb, offs[1]),
-                  config=cfg)
+                  out=out, config=cfg)
     torch.cuda.synchronize()
+    if buf is not None:
+        assert outside_untouched(buf, M, N), "wrote outside C"
     return C.cpu().numpy(), Af, Bf
 
 
@@ -88,10 +96,9 @@ def test_workloads(dev, fmt, cfg, name):
     assert r, str(r)
 
 
-# Shapes the direct HBM -> LDS pipeline takes (K % 32 == 0, N % 8 == 0, aligned): one,
-# two, three and many K-steps of 32 (four stages: the prologue fills up to three) and,
-# where K % 64 == 0, of 64 (two stages), M and N that are not tile multiples (clamped
-# loads, masked stores), a single row.
+# Aligned shapes on the direct HBM -> LDS pipeline (K % 32 == 0, N % 8 == 0): K of one
+# step of 32, of whole steps of 64 and of whole steps plus a tail step, M and N that are
+# not tile multiples (clamped rows, shifted last tile column, masked stores), a single row.
 DIRECT_SHAPES = [(1, 8, 32), (37, 8, 64), (300, 264, 96), (257, 520, 128), (300, 264, 192),
                  (129, 136, 4096), (1000, 1528, 800)]
 
@@ -110,6 +117,35 @@ def test_direct_pipeline_shapes(dev, fmt, cfg, shape):
     A = wl.random_matrix(900 + M, M, K, "normal")
     B = wl.random_matrix(1000 + N, K, N, "normal")
     C, Af, Bf = run(A, B, fmt, dev, cfg)
+    C64, S64 = oracle.gemm(Af, Bf)
+    r = verify.within_tol(C, C64, S64, REL_TOL)
+    assert r, f"{shape}: {r}"
+
+
+# Shapes for the direct pipeline's general edges: K tails of 1 to 63 after whole K-steps
+# (the tail step overlaps the one before), K of exactly one step of 32 or 64, N just past a
+# tile width (the last tile column's B panel moves left), N below the tile width (a
+# multiple of 8), odd widths and leading dimensions (2-byte-aligned rows), a single row.
+GENERAL_SHAPES = [(1000, 1531, 777), (1, 65, 65), (37, 64, 64), (70, 129, 127), (130, 257, 33),
+                  (300, 200, 1000), (64, 40, 100), (129, 67, 191), (257, 520, 96), (65, 300, 4097)]
+
+
+@pytest.mark.parametrize("fmt", list(FORMATS))
+@pytest.mark.parametrize("cfg", [c for c in CONFIGS if c >= 5] + [None])
+@pytest.mark.parametrize("shape", GENERAL_SHAPES, ids=[f"{m}x{n}x{k}" for m, n, k in GENERAL_SHAPES])
+def test_direct_general_edges(dev, fmt, cfg, shape):
+    M, N, K = shape
+    A = wl.random_matrix(1100 + M, M, K, "int4")
+    B = wl.random_matrix(1200 + N, K, N, "int4")
+    # packed, then offset starts with odd leading dimensions and NaN around the views
+    for lda, ldb, offs in ((None, None, (0, 0)), (K + 1, N + 3, (1, 3))):
+        C, Af, Bf = run(A, B, fmt, dev, cfg, lda=lda, ldb=ldb, offs=offs, ldc=N + 5)
+        C64, _ = oracle.gemm(Af, Bf)
+        r = verify.exact(C, C64)
+        assert r, f"{shape} lda={lda} ldb={ldb} offs={offs}: {r}"
+    A = wl.random_matrix(1300 + M, M, K, "normal")
+    B = wl.random_matrix(1400 + N, K, N, "normal")
+    C, Af, Bf = run(A, B, fmt, dev, cfg, lda=K + 3, ldb=N + 1, offs=(3, 1))
     C64, S64 = oracle.gemm(Af, Bf)
     r = verify.within_tol(C, C64, S64, REL_TOL)
     assert r, f"{shape}: {r}"
@@ -158,8 +194,9 @@ def test_strided_unaligned(dev, fmt, cfg, lds, offs):
 @pytest.mark.parametrize("K", [96, 192])
 def test_direct_strided_views(dev, fmt, cfg, K):
     """The direct pipeline addresses its loads from the tile's corner plus a fixed offset
-    per lane: leading dimensions beyond the width (multiples of 8, as it requires) with
-    NaN around the views, K-steps of 32 (K = 96) and 64 (K = 192)."""
+    per lane: leading dimensions beyond the width (here multiples of 8, so every lane is
+    16-byte aligned) with NaN around the views; K = 96 (a whole K-step of 64 and a tail
+    step over [32, 96)) and K = 192 (three whole steps)."""
     M, N = 300, 264
     A = wl.random_matrix(53, M, K, "int4")
     B = wl.random_matrix(54, K, N, "int4")

@@ -9,10 +9,13 @@
 // bits), so C is the same sum as the fp32 GEMM of the inputs' exact values, summed
 // in fp32 in a different order.
 //
-// Same scheme as the fp32 kernel (mm_gemm.hip): one workgroup per BM x BN tile of
-// C, two LDS stages, HBM loads for the next K-step in flight during the current
-// step's MFMAs, one barrier per K-step, masked loads at the edges, XCD-aware tile
-// order. Differences:
+// Two kernels. The direct HBM -> LDS pipeline (further below; configs 5-10, the ones
+// mm_gemm_bf16 / mm_gemm_f16 choose) serves every shape with K >= 32 and N >= 64 or
+// N % 8 == 0, at any 2-byte alignment. The register-staged kernel here serves the rest
+// (and configs 0-4). It follows the fp32 kernel (mm_gemm.hip): one workgroup per
+// BM x BN tile of C, two LDS stages, HBM loads for the next K-step in flight during the
+// current step's MFMAs, one barrier per K-step, masked loads at the edges, XCD-aware
+// tile order. Differences:
 //   * v_mfma_f32_32x32x16_{bf16,f16}: lane l supplies A[l % 32][8 (l / 32) + e] and
 //     B[8 (l / 32) + e][l % 32] for e = 0..7, i.e. one 16-byte LDS read per operand;
 //     MFMA step s of a K-step covers k = 16 s .. 16 s + 15;
@@ -345,18 +348,16 @@ hipError_t launch16(const Gemm16Args &a, hipStream_t stream)
 }
 
 // ---------------------------------------------------------------------------
-// Direct HBM -> LDS pipeline (the fast path for aligned shapes).
+// Direct HBM -> LDS pipeline.
 //
 // gfx950's global_load_lds_dwordx4 moves 16 bytes per lane from memory straight into
 // LDS (lane l's bytes land at M0 + 16 l), with no staging registers. That frees the
-// registers the loop above spends on staged data, so the pipeline can run NS = 4 LDS
-// stages deep: the loads for K-step kt + 3 are issued while step kt's MFMAs run, which
-// covers three K-steps of MFMA time instead of one. BK = 32 (64-byte A rows); where
-// K % 64 == 0, BK = 64 in two stages of twice the size (the same LDS): each A row of a
-// step is then one whole 128-byte line (a 64-byte row is half a line, and the DMA's LDS
-// writes of such rows count bank-conflict cycles), with twice the MFMAs per barrier
-// (measured +2-5% on the 256 x 256 tile, +5-17% on the 128 x 128 one, +17-30% on the
-// 64 x 64 one).
+// registers the loop above spends on staged data, so the pipeline runs NS LDS stages
+// deep: the loads for K-step kt + NS - 1 are issued while step kt's MFMAs run. K-steps
+// of BK = 64 make each A row of a step one whole 128-byte line (a 64-byte row is half a
+// line, and the DMA's LDS writes of such rows count bank-conflict cycles), with twice the
+// MFMAs per barrier of BK = 32 (measured +2-5% on the 256 x 256 tile, +5-17% on the
+// 128 x 128 one, +17-30% on the 64 x 64 one).
 //   * A panel (BM rows x BK k): stored as loaded, 2 BK bytes per row; the 16-byte
 //     chunks of row r sit in slots c ^ swz_a(r), so that the MFMA operand reads of 32
 //     rows at one k fall in distinct banks (no padding; the load pattern applies the
@@ -370,11 +371,23 @@ hipError_t launch16(const Gemm16Args &a, hipStream_t stream)
 //   * One barrier per K-step, after an explicit wait for the step's loads (vmcnt
 //     counts the loads of the steps issued after it). The loads are issued from inline
 //     asm so that the compiler does not add a wait for all of them before every LDS read.
-//   * Requirements (checked on the host): K % 32 == 0 (K % 64 == 0 for BK = 64), N % 8 == 0, lda and ldb
-//     multiples of 8 elements, A and B 16-byte aligned. Rows past M and column chunks
-//     past N are clamped to in-range ones; they only feed C elements that are not
-//     stored. K needs no mask (whole K-steps).
-template <int BM_, int BN_, int WM_, int WN_, int BK_ = 32, int NS_ = 4>
+//   * Any alignment: a lane's 16 bytes are read from wherever its 8 elements start (rows
+//     of odd length put half the rows at 2-byte alignment; the device's unaligned access
+//     mode serves such loads, into LDS as into registers), so neither the leading
+//     dimensions nor the base pointers need more than the elements' 2-byte alignment.
+//   * Edges, with every 16-byte chunk inside the matrix:
+//       - rows past M are clamped to row M - 1; they only feed C rows that are not stored;
+//       - columns: with N >= BN the last tile column's B panel starts at N - BN instead of
+//         its own origin (every chunk inside B's rows); the columns left of the origin
+//         belong to the tile before and are not stored again, so each C element is
+//         written once. With N < BN (one tile column) N must be a multiple of 8 and
+//         chunks past N are clamped to the last one (they feed only unstored columns);
+//       - K % BK != 0: after the whole K-steps, one more step loads k in [K - BK, K). Its
+//         first BK - K % BK k overlap the step before: once its loads have landed, the
+//         workgroup writes zeros over those k in both panels (between two barriers), so
+//         they add 0 * 0 (also where A or B holds an infinity or a NaN).
+//     These need K >= BK and offsets from a tile's corner that fit 32 bits (direct_ok).
+template <int BM_, int BN_, int WM_, int WN_, int BK_, int NS_>
 struct Direct16 {
     static constexpr int BM = BM_, BN = BN_, BK = BK_, NS = NS_, WM = WM_, WN = WN_;
     static constexpr int WAVES = (BM / WM) * (BN / WN), NT = WAVES * 64;
@@ -390,7 +403,7 @@ struct Direct16 {
     static_assert(BK == 32 || BK == 64, "K-steps of 32 or 64");
     static_assert(A_BYTES % (1024 * WAVES) == 0 && B_BYTES % (1024 * WAVES) == 0,
                   "whole 1 KB loads per wave");
-    static_assert((NS - 2) * (A_LOADS + B_LOADS) <= 63, "vmcnt range");
+    static_assert(NS >= 2 && (NS - 2) * (A_LOADS + B_LOADS) <= 63, "vmcnt range");
     static_assert(BN >= 64 && BN % 32 == 0 && WN % 32 == 0 && WM % 32 == 0, "tile shape");
     static_assert(NS * STAGE <= 160 * 1024, "stages must fit the 160 KB LDS");
 };
@@ -445,10 +458,17 @@ __device__ __forceinline__ void wait_later(int later)
     }
 }
 
-template <class T, bool BF16>
-__global__ __launch_bounds__(T::NT) void gemm_h16_direct_kernel(Gemm16Args p)
+// KG wave groups of T::WAVES waves each share a workgroup and its tile: group g takes the
+// K-steps s with s % KG == g into a ring of its own, and at the end group 1 hands its
+// accumulators to group 0 through LDS, which adds them (in that fixed order) and stores
+// the tile. Two groups put twice the waves and twice the loads in flight on the CU that
+// holds the tile, for shapes with about one tile per CU.
+template <class T, bool BF16, int KG>
+__global__ __launch_bounds__(T::NT * KG) void gemm_h16_direct_kernel(Gemm16Args p)
 {
-    __shared__ __attribute__((aligned(1024))) char lds[T::NS * T::STAGE];
+    static_assert(KG == 1 || (KG == 2 && T::WAVES * T::FM * T::FN * 16 * 64 * 4 <= KG * T::NS * T::STAGE),
+                  "group 1's accumulators must fit the stages");
+    __shared__ __attribute__((aligned(1024))) char lds[KG * T::NS * T::STAGE];
     const int tiles_m = (p.M + T::BM - 1) / T::BM;
     const int tiles_n = (p.N + T::BN - 1) / T::BN;
     const int64_t tiles = (int64_t)tiles_m * tiles_n;
@@ -457,11 +477,21 @@ __global__ __launch_bounds__(T::NT) void gemm_h16_direct_kernel(Gemm16Args p)
     int tm, tn;
     tile_of_block16((int)bid, (int)tiles, tiles_m, tiles_n, tm, tn);
     const int m0 = tm * T::BM, n0 = tn * T::BN;
+    // origin of the B panel: n0, or N - BN for a last tile column that would cross N
+    const int nb0 = p.N >= T::BN ? min(n0, p.N - T::BN) : 0;
 
     const int lane = threadIdx.x & 63;
-    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave index, in a scalar register
+    const int wg = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave index, in a scalar register
+    const int grp = KG == 1 ? 0 : wg / T::WAVES, w = KG == 1 ? wg : wg % T::WAVES;  // K group, wave in it
     const int wm0 = (w / (T::BN / T::WN)) * T::WM, wn0 = (w % (T::BN / T::WN)) * T::WN;
-    const int nk = p.K / T::BK;
+    // K-steps: with K % BK != 0 step 0 is the tail, k in [K - BK, K); it shares its first
+    // ov k with the whole steps, which follow as steps 1 .. nk - 1 (k0 = (s - 1) BK)
+    const int nk_full = p.K / T::BK;              // whole K-steps (>= 1)
+    const int ov = (T::BK - p.K % T::BK) % T::BK;
+    const int tail = ov ? 1 : 0;
+    const int nk = nk_full + tail;
+    const int nj = (nk + KG - 1) / KG;            // ring steps of every group (the last may idle)
+    const int my_steps = KG == 1 ? nk : (nk - grp + KG - 1) / KG;  // steps of this group
 
     // this lane's byte offsets from the tile's corner at the K-step (the loads' scalar
     // base, advanced by BK per step); direct_ok keeps them below 2^32
@@ -477,14 +507,18 @@ __global__ __launch_bounds__(T::NT) void gemm_h16_direct_kernel(Gemm16Args p)
         constexpr int CPR = T::B_ROW / 16;  // 16-byte chunks per B row
         const int krow = T::B_ROWS_PER_LOAD * (T::B_LOADS * w + i) + lane / CPR;
         const int chunk = (lane % CPR) ^ swz_b16<T>(krow);
-        // N % 8 == 0: min(n0 + 8 chunk, N - 8) >= n0
-        boff[i] = (unsigned)(((int64_t)krow * p.ldb + (min(n0 + 8 * chunk, p.N - 8) - n0)) * 2);
+        int col = nb0 + 8 * chunk;               // N >= BN: inside the row
+        if (p.N < T::BN) col = min(col, p.N - 8);  // N % 8 == 0 here
+        boff[i] = (unsigned)(((int64_t)krow * p.ldb + (col - nb0)) * 2);
     }
-    const unsigned lds0 = (unsigned)(uintptr_t)(lds_char *)lds;  // LDS byte offset of the array
-    auto issue = [&](int kt) {
-        const unsigned st = lds0 + (kt % T::NS) * T::STAGE;
-        const unsigned short *abase = p.A + (int64_t)m0 * p.lda + (int64_t)kt * T::BK;
-        const unsigned short *bbase = p.B + (int64_t)kt * T::BK * p.ldb + n0;
+    // this group's ring
+    const unsigned ring0 = (unsigned)(uintptr_t)(lds_char *)lds + grp * T::NS * T::STAGE;
+    auto issue = [&](int j) {  // the group's ring step j: K-step s = j KG + grp
+        const int s = j * KG + grp;
+        const unsigned st = ring0 + (j % T::NS) * T::STAGE;
+        const int k0 = (tail && s == 0) ? p.K - T::BK : (s - tail) * T::BK;
+        const unsigned short *abase = p.A + (int64_t)m0 * p.lda + k0;
+        const unsigned short *bbase = p.B + (int64_t)k0 * p.ldb + nb0;
 #pragma unroll
         for (int i = 0; i < T::A_LOADS; ++i) load_to_lds_s(st + (T::A_LOADS * w + i) * 1024, abase, aoff[i]);
 #pragma unroll
@@ -521,16 +555,9 @@ __global__ __launch_bounds__(T::NT) void gemm_h16_direct_kernel(Gemm16Args p)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-    constexpr int LOADS = T::A_LOADS + T::B_LOADS;  // per wave per K-step
-    for (int s = 0; s < T::NS - 1 && s < nk; ++s) issue(s);
-    for (int kt = 0; kt < nk; ++kt) {
-        // step kt's loads are done when at most the later steps' loads are outstanding
-        wait_later<LOADS, T::NS - 2>(nk - 1 - kt);
-        // every wave's loads for stage kt are in LDS, and every wave is done with the
-        // stage the next issue overwrites (read in step kt - 1)
-        __syncthreads();
-        if (kt + T::NS - 1 < nk) issue(kt + T::NS - 1);
-        const lds_char *st = (const lds_char *)lds + (kt % T::NS) * T::STAGE;
+    const lds_char *ring = (const lds_char *)lds + grp * T::NS * T::STAGE;
+    auto multiply = [&](int j) {
+        const lds_char *st = ring + (j % T::NS) * T::STAGE;
 #pragma unroll
         for (int ks = 0; ks < T::KS; ++ks) {
             u32x4 a[T::FM], b[T::FN];
@@ -538,71 +565,126 @@ __global__ __launch_bounds__(T::NT) void gemm_h16_direct_kernel(Gemm16Args p)
             for (int i = 0; i < T::FM; ++i)
                 a[i] = *(const __attribute__((address_space(3))) u32x4 *)(st + a_off[ks][i]);
 #pragma unroll
-            for (int j = 0; j < T::FN; ++j) {
+            for (int jj = 0; jj < T::FN; ++jj) {
                 const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (__attribute__((address_space(3))) v4i16 *)(st + b_off[ks][0][j]));
+                    (__attribute__((address_space(3))) v4i16 *)(st + b_off[ks][0][jj]));
                 const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (__attribute__((address_space(3))) v4i16 *)(st + b_off[ks][1][j]));
+                    (__attribute__((address_space(3))) v4i16 *)(st + b_off[ks][1][jj]));
                 const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
-                b[j] = u32x4{l2[0], l2[1], h2[0], h2[1]};
+                b[jj] = u32x4{l2[0], l2[1], h2[0], h2[1]};
             }
 #pragma unroll
             for (int i = 0; i < T::FM; ++i)
 #pragma unroll
-                for (int j = 0; j < T::FN; ++j) acc[i][j] = mfma16<BF16>(a[i], b[j], acc[i][j]);
+                for (int jj = 0; jj < T::FN; ++jj) acc[i][jj] = mfma16<BF16>(a[i], b[jj], acc[i][jj]);
         }
+    };
+
+    constexpr int LOADS = T::A_LOADS + T::B_LOADS;  // per wave per K-step
+    for (int j = 0; j < T::NS - 1 && j < my_steps; ++j) issue(j);
+    // ring step 0, peeled: step j's loads are done when at most the later steps' loads are
+    // outstanding; after the barrier every wave's loads for stage j are in LDS, and every
+    // wave is done with the stage the next issue overwrites (read in step j - 1)
+    wait_later<LOADS, T::NS - 2>(my_steps - 1);
+    __syncthreads();
+    if (T::NS - 1 < my_steps) issue(T::NS - 1);
+    if (tail) {
+        // K-step 0 (group 0's first) is the tail: zeros over the ov k it shares with the
+        // whole steps, in both panels; its loads have landed (the wait and barrier above),
+        // and nothing reads the stage before the barrier below
+        if (grp == 0) {
+            lds_char *st = (lds_char *)lds;
+            for (int e = threadIdx.x; e < T::BM * ov; e += T::NT) {
+                const int r = e / ov, k = e - r * ov;
+                *(__attribute__((address_space(3))) unsigned short *)(
+                    st + r * T::A_ROW + 16 * ((k >> 3) ^ swz_a16<T>(r)) + 2 * (k & 7)) = 0;
+            }
+            for (int e = threadIdx.x; e < ov * (T::B_ROW / 16); e += T::NT)
+                *(__attribute__((address_space(3))) u32x4 *)(st + T::A_BYTES + 16 * e) = u32x4{0u, 0u, 0u, 0u};
+        }
+        __syncthreads();
+    }
+    if (my_steps > 0) multiply(0);
+    for (int j = 1; j < nj; ++j) {
+        wait_later<LOADS, T::NS - 2>(my_steps - 1 - j);
+        __syncthreads();
+        if (j + T::NS - 1 < my_steps) issue(j + T::NS - 1);
+        if (KG == 1 || j < my_steps) multiply(j);
     }
 
+    if constexpr (KG == 2) {
+        // group 1's accumulators to LDS (lane-minor: conflict-free), group 0 adds them
+        __syncthreads();  // every wave is done with the stages
+        typedef __attribute__((address_space(3))) float lds_f32;
+        lds_f32 *x = (lds_f32 *)lds + w * (T::FM * T::FN * 16 * 64) + lane;
+        if (grp == 1) {
+#pragma unroll
+            for (int i = 0; i < T::FM; ++i)
+#pragma unroll
+                for (int jj = 0; jj < T::FN; ++jj)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) x[((i * T::FN + jj) * 16 + r) * 64] = acc[i][jj][r];
+        }
+        __syncthreads();
+        if (grp == 1) return;
+#pragma unroll
+        for (int i = 0; i < T::FM; ++i)
+#pragma unroll
+            for (int jj = 0; jj < T::FN; ++jj)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[i][jj][r] += x[((i * T::FN + jj) * 16 + r) * 64];
+    }
+
+    // accumulator layout as for the fp32 32x32 blocks; local column c is column nb0 + c of
+    // C, stored from n0 on (columns left of n0 belong to the tile column before)
     const int col_l = lane & 31, row_l = 4 * (lane >> 5);
 #pragma unroll
     for (int i = 0; i < T::FM; ++i)
 #pragma unroll
-        for (int j = 0; j < T::FN; ++j)
+        for (int jj = 0; jj < T::FN; ++jj)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int gm = m0 + wm0 + i * 32 + 8 * (r >> 2) + row_l + (r & 3);
-                const int gn = n0 + wn0 + j * 32 + col_l;
-                if (gm < p.M && gn < p.N) p.C[(int64_t)gm * p.ldc + gn] = acc[i][j][r];
+                const int gn = nb0 + wn0 + jj * 32 + col_l;
+                if (gm < p.M && gn < p.N && gn >= n0) p.C[(int64_t)gm * p.ldc + gn] = acc[i][jj][r];
             }
 }
 
-// The direct pipeline's requirements (see above).
-bool direct_ok(const Gemm16Args &a)
+// The direct pipeline's requirements for K-steps of bk (see above).
+bool direct_ok(const Gemm16Args &a, int bm, int bn, int bk)
 {
-    // the per-lane byte offsets from a tile's corner (below 256 rows of A, 64 rows of B
-    // and 256 columns) must fit 32 bits
+    // the per-lane byte offsets from a tile's corner (below bm rows of A, bk rows of B and
+    // bn columns) must fit 32 bits
     constexpr int64_t kOffMax = int64_t(1) << 32;
-    return a.K % 32 == 0 && a.N >= 8 && a.N % 8 == 0 && a.lda % 8 == 0 && a.ldb % 8 == 0 &&
-           (uintptr_t)a.A % 16 == 0 && (uintptr_t)a.B % 16 == 0 && 2 * (255 * a.lda + 64) < kOffMax &&
-           2 * (63 * a.ldb + 256) < kOffMax;
+    return a.K >= bk && a.N >= 8 && (a.N >= bn || a.N % 8 == 0) &&
+           2 * ((bm - 1) * a.lda + bk) < kOffMax && 2 * ((int64_t)(bk - 1) * a.ldb + bn) < kOffMax;
 }
 
-template <class T, bool BF16>
+template <class T, bool BF16, int KG>
 hipError_t launch16_direct(const Gemm16Args &a, hipStream_t stream)
 {
     const int64_t tiles = (int64_t)((a.M + T::BM - 1) / T::BM) * ((a.N + T::BN - 1) / T::BN);
-    if (a.K % T::BK) return hipErrorInvalidValue;
+    if (!direct_ok(a, T::BM, T::BN, T::BK)) return hipErrorInvalidValue;
     if (tiles > 0x7fffffff) return hipErrorInvalidConfiguration;
     unsigned gx, gy;
     if (!grid_for(tiles, gx, gy)) return hipErrorInvalidConfiguration;
     Gemm16Args arg = a;
     void *args[] = {&arg};
-    return hipLaunchKernel(reinterpret_cast<const void *>(&gemm_h16_direct_kernel<T, BF16>),
-                           dim3(gx, gy), dim3(T::NT), args, 0, stream);
+    return hipLaunchKernel(reinterpret_cast<const void *>(&gemm_h16_direct_kernel<T, BF16, KG>),
+                           dim3(gx, gy), dim3(T::NT * KG), args, 0, stream);
 }
 
-using D16L = Direct16<256, 256, 128, 64>;
-using D16M = Direct16<128, 128, 64, 64>;
-using D16S = Direct16<64, 64, 32, 32>;
-// K-steps of 64 in half the stages (the same LDS), for K % 64 == 0
-using D16L64 = Direct16<256, 256, 128, 64, 64, 2>;
-using D16M64 = Direct16<128, 128, 64, 64, 64, 2>;
-using D16S64 = Direct16<64, 64, 32, 32, 64, 2>;
-
-template <class T, class T64, bool BF16>
-hipError_t launch16_direct_k(const Gemm16Args &a, hipStream_t stream)
+// A direct tile with K-steps of 64 (T64) where K >= 64, else of 32 (T32), in KG wave
+// groups; shapes the pipeline cannot take (K < 32, N < BN with N % 8 != 0, offsets beyond
+// 32 bits) run the register-staged tile `staged`.
+template <class T32, class T64, class TS, int KG>
+hipError_t launch16_direct_k(bool bf16, const Gemm16Args &a, hipStream_t stream)
 {
-    return a.K % 64 == 0 ? launch16_direct<T64, BF16>(a, stream) : launch16_direct<T, BF16>(a, stream);
+    if (direct_ok(a, T64::BM, T64::BN, 64))
+        return bf16 ? launch16_direct<T64, true, KG>(a, stream) : launch16_direct<T64, false, KG>(a, stream);
+    if (direct_ok(a, T32::BM, T32::BN, 32))
+        return bf16 ? launch16_direct<T32, true, KG>(a, stream) : launch16_direct<T32, false, KG>(a, stream);
+    return bf16 ? launch16<TS, true>(a, stream) : launch16<TS, false>(a, stream);
 }
 
 using T16L = Tile16<256, 256, 128, 64>;
@@ -611,31 +693,84 @@ using T16S = Tile16<64, 64, 32, 32>;
 using T16Mp2 = Tile16<128, 128, 64, 64, 2>;
 using T16Sp2 = Tile16<64, 64, 32, 32, 2>;
 
+// direct tiles: <BM, BN, WM, WN, BK, stages>
+using D16L = Direct16<256, 256, 128, 64, 32, 4>;
+using D16L64 = Direct16<256, 256, 128, 64, 64, 2>;
+using D16M = Direct16<128, 128, 64, 64, 32, 4>;
+using D16M64 = Direct16<128, 128, 64, 64, 64, 2>;
+using D16S = Direct16<64, 64, 32, 32, 32, 4>;
+using D16S64 = Direct16<64, 64, 32, 32, 64, 2>;
+// deeper rings for the smaller tiles
+using D16M32s8 = Direct16<128, 128, 64, 64, 32, 8>;
+using D16M64s4 = Direct16<128, 128, 64, 64, 64, 4>;
+using D16S32s8 = Direct16<64, 64, 32, 32, 32, 8>;
+using D16S64s4 = Direct16<64, 64, 32, 32, 64, 4>;
+
+struct Config16 {
+    const char *name;
+    hipError_t (*launch)(bool, const Gemm16Args &, hipStream_t);
+};
+
+template <class T>
+hipError_t staged16(bool bf16, const Gemm16Args &a, hipStream_t stream)
+{
+    return bf16 ? launch16<T, true>(a, stream) : launch16<T, false>(a, stream);
+}
+
+template <class T32, class T64, class TS, int KG = 1>
+hipError_t direct16(bool bf16, const Gemm16Args &a, hipStream_t stream)
+{
+    return launch16_direct_k<T32, T64, TS, KG>(bf16, a, stream);
+}
+
+const Config16 kConfigs16[] = {
+    {"256x256x64 w128x64 pf1 (8 waves)", &staged16<T16L>},
+    {"128x128x64 w64x64 pf1 (4 waves)", &staged16<T16M>},
+    {"64x64x64 w32x32 pf1 (4 waves)", &staged16<T16S>},
+    {"128x128x64 w64x64 pf2 (4 waves)", &staged16<T16Mp2>},
+    {"64x64x64 w32x32 pf2 (4 waves)", &staged16<T16Sp2>},
+    {"256x256x64 w128x64 direct-to-LDS 2 stages (8 waves; K < 64: K-steps of 32, 4 stages)",
+     &direct16<D16L, D16L64, T16L>},
+    {"128x128x64 w64x64 direct-to-LDS 2 stages (4 waves; K < 64: K-steps of 32, 4 stages)",
+     &direct16<D16M, D16M64, T16Mp2>},
+    {"64x64x64 w32x32 direct-to-LDS 2 stages (4 waves; K < 64: K-steps of 32, 4 stages)",
+     &direct16<D16S, D16S64, T16Sp2>},
+    {"128x128x64 w64x64 direct-to-LDS 4 stages (4 waves; K < 64: K-steps of 32, 8 stages)",
+     &direct16<D16M32s8, D16M64s4, T16Mp2>},
+    {"64x64x64 w32x32 direct-to-LDS 4 stages (4 waves; K < 64: K-steps of 32, 8 stages)",
+     &direct16<D16S32s8, D16S64s4, T16Sp2>},
+    {"128x128x64 w64x64 direct-to-LDS 2 stages, K over 2 wave groups (8 waves; K < 64: K-steps of 32, 4 stages)",
+     &direct16<D16M, D16M64, T16Mp2, 2>},
+};
+constexpr int kNumConfigs16 = sizeof(kConfigs16) / sizeof(kConfigs16[0]);
+
 }  // namespace
 
-int gemm16_num_configs() { return 8; }
+int gemm16_num_configs() { return kNumConfigs16; }
 
 const char *gemm16_config_name(int cfg)
 {
-    static const char *names[] = {"256x256x64 w128x64 pf1 (8 waves)", "128x128x64 w64x64 pf1 (4 waves)",
-                                  "64x64x64 w32x32 pf1 (4 waves)", "128x128x64 w64x64 pf2 (4 waves)",
-                                  "64x64x64 w32x32 pf2 (4 waves)",
-                                  "256x256x32 w128x64 direct-to-LDS 4 stages (8 waves; K % 64 == 0: K-steps of 64, 2 stages)",
-                                  "128x128x32 w64x64 direct-to-LDS 4 stages (4 waves; K % 64 == 0: K-steps of 64, 2 stages)",
-                                  "64x64x32 w32x32 direct-to-LDS 4 stages (4 waves; K % 64 == 0: K-steps of 64, 2 stages)"};
-    return (cfg >= 0 && cfg < 8) ? names[cfg] : nullptr;
+    return (cfg >= 0 && cfg < kNumConfigs16) ? kConfigs16[cfg].name : nullptr;
 }
 
 int gemm16_select_config(int64_t M, int64_t N, int64_t K)
 {
     (void)K;
-    // 5, 6 and 7 are the direct pipelines; on shapes they cannot take they run the
-    // register-staged kernels of their size (configs 0, 3 and 4). Smaller tiles where the
-    // big ones would leave CUs idle (1024^3 bf16: 243 TFLOP/s on the 64 x 64 direct tile
-    // against 144 staged).
-    if (((M + 255) / 256) * ((N + 255) / 256) >= 200) return 5;
-    if (((M + 127) / 128) * ((N + 127) / 128) >= 200) return 6;
-    return 7;
+    // The direct pipelines (5 .. 10); on shapes they cannot take they run the register-
+    // staged tile of their size. From the timed sweep of every config (bf16 and fp16,
+    // 128^3 .. 8192^3, the projection and ragged shapes): the 256 x 256 tile from 144 tiles
+    // on (3072^3: 788 TFLOP/s against 739 on 128 x 128); with fewer, the 128 x 128 tile in
+    // two wave groups from 200 tiles of 128^2 on (2048^3: 725 against 609 in one group,
+    // 4096 x 1024 x 4096: 847 against 708); below that the 64 x 64 tile, four stages deep
+    // where at most two workgroups per CU are needed (1024^3: 316; 1000 x 1531 x 777: 208
+    // against 191 with two stages), else two stages, which fit three workgroups per CU
+    // (1536^3, 576 tiles: 458 against 412).
+    const int64_t t256 = ((M + 255) / 256) * ((N + 255) / 256);
+    const int64_t t128 = ((M + 127) / 128) * ((N + 127) / 128);
+    const int64_t t64 = ((M + 63) / 64) * ((N + 63) / 64);
+    if (t256 >= 144) return 5;
+    if (t128 >= 200) return 10;
+    return t64 > 512 ? 7 : 9;
 }
 
 hipError_t gemm16_launch(int cfg, bool bf16, const void *A, int64_t lda, const void *B, int64_t ldb,
@@ -651,24 +786,8 @@ hipError_t gemm16_launch(int cfg, bool bf16, const void *A, int64_t lda, const v
     a.M = M;
     a.N = N;
     a.K = K;
-    switch (cfg) {
-    case 0: return bf16 ? launch16<T16L, true>(a, stream) : launch16<T16L, false>(a, stream);
-    case 1: return bf16 ? launch16<T16M, true>(a, stream) : launch16<T16M, false>(a, stream);
-    case 2: return bf16 ? launch16<T16S, true>(a, stream) : launch16<T16S, false>(a, stream);
-    case 3: return bf16 ? launch16<T16Mp2, true>(a, stream) : launch16<T16Mp2, false>(a, stream);
-    case 4: return bf16 ? launch16<T16Sp2, true>(a, stream) : launch16<T16Sp2, false>(a, stream);
-    // the direct pipelines; shapes they do not take run the same tile size staged
-    // through registers
-    case 5:
-        if (!direct_ok(a)) return gemm16_launch(0, bf16, A, lda, B, ldb, C, ldc, M, N, K, stream);
-        return bf16 ? launch16_direct_k<D16L, D16L64, true>(a, stream) : launch16_direct_k<D16L, D16L64, false>(a, stream);
-    case 6:
-        if (!direct_ok(a)) return gemm16_launch(3, bf16, A, lda, B, ldb, C, ldc, M, N, K, stream);
-        return bf16 ? launch16_direct_k<D16M, D16M64, true>(a, stream) : launch16_direct_k<D16M, D16M64, false>(a, stream);
-    default:
-        if (!direct_ok(a)) return gemm16_launch(4, bf16, A, lda, B, ldb, C, ldc, M, N, K, stream);
-        return bf16 ? launch16_direct_k<D16S, D16S64, true>(a, stream) : launch16_direct_k<D16S, D16S64, false>(a, stream);
-    }
+    if (cfg < 0 || cfg >= kNumConfigs16) return hipErrorInvalidValue;
+    return kConfigs16[cfg].launch(bf16, a, stream);
 }
 
 }  // namespace mm
