@@ -276,7 +276,7 @@ __global__ __launch_bounds__(T::NT) void conv_direct_kernel(GemmArgs p, Im2colOp
         direct_multiply<T>((const lds_char *)lds + (kt % T::NS) * T::STAGE, a_off, b_off, acc);
         if (kt + T::NS - 1 < nk) issue(kt + T::NS - 1);
     }
-    direct_store<T>(p, m0, n0, wm0, wn0, lane, acc, [&](int gn) { return o.c_column(p, gn); });
+    direct_store<T>(p, m0, n0, n0, wm0, wn0, lane, acc, [&](int gn) { return o.c_column(p, gn); });
 }
 
 template <class T>

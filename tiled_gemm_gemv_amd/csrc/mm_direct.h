@@ -164,11 +164,12 @@ __device__ __forceinline__ void direct_multiply(const lds_char *st, const int (&
 }
 
 // Accumulator layout of v_mfma_f32_32x32x2_f32: lane l, register r holds row
-// 8 (r / 4) + 4 (l / 32) + r % 4, column l % 32 of the 32 x 32 block. Element (gm, gn)
-// of the product goes to C + gm * ldc + col_off(gn), for gm < M and gn < N.
+// 8 (r / 4) + 4 (l / 32) + r % 4, column l % 32 of the 32 x 32 block. The tile's columns
+// start at nb0; element (gm, gn) of the product goes to C + gm * ldc + col_off(gn), for
+// gm < M, gn < N and gn >= n_first (columns left of n_first belong to another tile).
 template <class T, class ColOff>
-__device__ __forceinline__ void direct_store(const GemmArgs &p, int m0, int n0, int wm0, int wn0, int lane,
-                                             const f32x16 (&acc)[T::FM][T::FN], ColOff col_off)
+__device__ __forceinline__ void direct_store(const GemmArgs &p, int m0, int nb0, int n_first, int wm0, int wn0,
+                                             int lane, const f32x16 (&acc)[T::FM][T::FN], ColOff col_off)
 {
     const int col_l = lane & 31, row_l = 4 * (lane >> 5);
 #pragma unroll
@@ -178,8 +179,8 @@ __device__ __forceinline__ void direct_store(const GemmArgs &p, int m0, int n0, 
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int gm = m0 + wm0 + i * 32 + 8 * (r >> 2) + row_l + (r & 3);
-                const int gn = n0 + wn0 + jj * 32 + col_l;
-                if (gm < p.M && gn < p.N) p.C[(int64_t)gm * p.ldc + col_off(gn)] = acc[i][jj][r];
+                const int gn = nb0 + wn0 + jj * 32 + col_l;
+                if (gm < p.M && gn < p.N && gn >= n_first) p.C[(int64_t)gm * p.ldc + col_off(gn)] = acc[i][jj][r];
             }
 }
 
@@ -187,8 +188,8 @@ __device__ __forceinline__ void direct_store(const GemmArgs &p, int m0, int n0, 
 // for two K halves of one product summed into a zeroed C, where the result does not
 // depend on which half arrives first (0 + x is exact and x + y == y + x).
 template <class T>
-__device__ __forceinline__ void direct_store_add(const GemmArgs &p, int m0, int n0, int wm0, int wn0, int lane,
-                                                 const f32x16 (&acc)[T::FM][T::FN])
+__device__ __forceinline__ void direct_store_add(const GemmArgs &p, int m0, int nb0, int n_first, int wm0, int wn0,
+                                                 int lane, const f32x16 (&acc)[T::FM][T::FN])
 {
     const int col_l = lane & 31, row_l = 4 * (lane >> 5);
 #pragma unroll
@@ -198,8 +199,8 @@ __device__ __forceinline__ void direct_store_add(const GemmArgs &p, int m0, int 
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int gm = m0 + wm0 + i * 32 + 8 * (r >> 2) + row_l + (r & 3);
-                const int gn = n0 + wn0 + jj * 32 + col_l;
-                if (gm < p.M && gn < p.N) atomicAdd(p.C + (int64_t)gm * p.ldc + gn, acc[i][jj][r]);
+                const int gn = nb0 + wn0 + jj * 32 + col_l;
+                if (gm < p.M && gn < p.N && gn >= n_first) atomicAdd(p.C + (int64_t)gm * p.ldc + gn, acc[i][jj][r]);
             }
 }
 

@@ -16,7 +16,7 @@ hipError_t launch_tile(const GemmArgs &a, hipStream_t stream)
 // lanes; on other shapes the register-staged kernel of that tile size runs instead.
 hipError_t direct_or_staged_256(const GemmArgs &a, hipStream_t stream)
 {
-    return direct_f32_wide_ok(a) ? gemm_direct_launch(DirectTile::T256, a, stream)
+    return direct_f32_wide_ok(a, 256) ? gemm_direct_launch(DirectTile::T256, a, stream)
                                  : launch_tile<T256x256k32>(a, stream);
 }
 
@@ -239,8 +239,9 @@ hipError_t gemm_split_launch(const GemmArgs &a, float *ws, hipStream_t stream)
 // the workspace path, 4096 x 64 x 4096 lost, 58 -> 50).
 bool gemm_split2_ok(int64_t M, int64_t N, int64_t K)
 {
-    // halves on the lean build; N < 64 stays on the narrow kernels
-    if (K < 2048 || K % 32 != 0 || N < 64 || N % 4 != 0) return false;
+    // N < 64 stays on the narrow kernels; N % 4 != 0 runs the halves on the general build
+    // (4-byte B lanes in the last tile column)
+    if (K < 2048 || K % 32 != 0 || N < 64) return false;
     const int64_t tiles = (M + 63) / 64 * ((N + 63) / 64);
     // halves of 1024-1040 k on 129-256 tiles measured 1-2% slower (4096 x 256 x 2048,
     // 2000 x 300 x 2080); on 128 tiles still faster (1000 x 500 x 2048: 51 -> 72)

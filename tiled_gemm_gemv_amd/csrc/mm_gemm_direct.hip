@@ -16,14 +16,17 @@
 //     element(s) the permutations put there, and 4- and 16-byte lanes build the same
 //     LDS image. Full K-steps load A with 16-byte lanes whatever its alignment (gfx950
 //     serves 16-byte loads from any 4-byte-aligned address, also into LDS; a full step's
-//     chunks never cross a row end). B takes 16-byte lanes too, except in the last tile
-//     column when N % 4 != 0, whose chunks would cross the row end: 4-byte lanes there.
+//     chunks never cross a row end). B takes 16-byte lanes too: with N >= BN the last
+//     tile column's B panel starts at N - BN, so that no chunk crosses the row end (its
+//     columns left of its own origin belong to the tile before and are not stored again:
+//     each C element is written once). Only with N < BN and N % 4 != 0 does B take 4-byte
+//     lanes.
 //   * Edges: rows past M and columns past N are clamped to in-range data that only feeds
 //     C elements that are not stored. A partial last K-step (K % 16 != 0) loads both
 //     panels with 4-byte lanes at k clamped to K - 1, then the workgroup writes zeros
 //     over the k >= K entries of both panels between two barriers.
-//   * Addressing. Lean builds (K % 16 == 0, N % 4 == 0, leading dimensions that keep the
-//     offsets below 2^32) take the load's scalar-base form: the tile's corner at the
+//   * Addressing. Lean builds (K % 16 == 0, N % 4 == 0 or N >= BN, leading dimensions
+//     that keep the offsets below 2^32) take the load's scalar-base form: the tile's corner at the
 //     K-step in scalar registers plus a byte offset per lane fixed for the whole K loop,
 //     so a load needs no vector instruction. General builds keep a 64-bit pointer per
 //     lane.
@@ -54,6 +57,9 @@ __global__ __launch_bounds__(T::NT) void gemm_f32_direct_kernel(GemmArgs p)
     int tm, tn;
     tile_of_block((int)bid, (int)tiles, tiles_m, tiles_n, 8, tm, tn);
     const int m0 = tm * T::BM, n0 = tn * T::BN;
+    // origin of the B panel: n0, or N - BN for a last tile column that would cross N (its
+    // columns left of n0 belong to the tile before and are not stored)
+    const int nb0 = p.N >= T::BN ? min(n0, p.N - T::BN) : n0;
     // problem of a strided batch: grid layer blockIdx.z
     p.A += blockIdx.z * p.sa;
     p.B += blockIdx.z * p.sb;
@@ -66,8 +72,9 @@ __global__ __launch_bounds__(T::NT) void gemm_f32_direct_kernel(GemmArgs p)
 
     // The 16-byte lanes of full K-steps are addressed from the tile's corner at the K-step
     // (a scalar base) plus a fixed byte offset per lane; direct_f32_offsets_fit keeps those
-    // offsets below 2^32. (B's are used only by tiles whose chunks all take 16-byte lanes,
-    // for which min(col, N - 4) >= n0.)
+    // offsets below 2^32. (B's are used only by tiles whose chunks all take 16-byte lanes:
+    // with N >= BN every chunk lies inside B's rows, else N % 4 == 0 and chunks past N are
+    // clamped to the last one, min(col, N - 4) >= nb0.)
     unsigned aoff[T::A16], boff[T::B16];
     if constexpr (SADDR) {
 #pragma unroll
@@ -80,8 +87,8 @@ __global__ __launch_bounds__(T::NT) void gemm_f32_direct_kernel(GemmArgs p)
         for (int i = 0; i < T::B16; ++i) {
             const int o = (T::B16 * w + i) * 1024 + 16 * lane;
             const int krow = o / T::B_ROW, chunk = (o % T::B_ROW) / 16;
-            const int col = n0 + 4 * (chunk ^ swz_b<T>(krow));  // N % 4 == 0: min(col, N - 4) >= n0
-            boff[i] = (unsigned)(((int64_t)krow * p.ldb + (min(col, p.N - 4) - n0)) * 4);
+            const int col = nb0 + 4 * (chunk ^ swz_b<T>(krow));
+            boff[i] = (unsigned)(((int64_t)krow * p.ldb + (min(col, p.N - 4) - nb0)) * 4);
         }
     }
 
@@ -97,13 +104,13 @@ __global__ __launch_bounds__(T::NT) void gemm_f32_direct_kernel(GemmArgs p)
         asrc[i] = p.A + (int64_t)min(m0 + row, p.M - 1) * p.lda + 4 * (chunk ^ swz_a<T>(row));
     }
     // B chunks stay inside their row when N % 4 == 0 (clamped to the last chunk) or when
-    // the whole tile lies left of the last partial chunk
-    const bool wide_b = !T::GEN || (p.N % 4 == 0) || (n0 + T::BN <= p.N - p.N % 4);
+    // the panel starts at least BN columns before N
+    const bool wide_b = !T::GEN || (p.N % 4 == 0) || (p.N >= T::BN);
 #pragma unroll
     for (int i = 0; i < T::B16; ++i) {
         const int o = (T::B16 * w + i) * 1024 + 16 * lane;
         const int krow = o / T::B_ROW, chunk = (o % T::B_ROW) / 16;
-        const int col = n0 + 4 * (chunk ^ swz_b<T>(krow));
+        const int col = nb0 + 4 * (chunk ^ swz_b<T>(krow));
         bsrc[i] = p.B + (int64_t)krow * p.ldb + max(min(col, p.N - 4), 0);
     }
     // 4-byte lanes: source of load i at K-step k0, k clamped to K - 1 (partial step)
@@ -116,7 +123,7 @@ __global__ __launch_bounds__(T::NT) void gemm_f32_direct_kernel(GemmArgs p)
     auto b4_src = [&](int i, int k0) {
         const int o = (T::B4 * w + i) * 256 + 4 * lane;
         const int krow = o / T::B_ROW, slot = (o % T::B_ROW) / 4;
-        const int col = n0 + 4 * ((slot >> 2) ^ swz_b<T>(krow)) + (slot & 3);
+        const int col = nb0 + 4 * ((slot >> 2) ^ swz_b<T>(krow)) + (slot & 3);
         return p.B + (int64_t)min(k0 + krow, p.K - 1) * p.ldb + min(col, p.N - 1);
     };
     const unsigned lds0 = (unsigned)(uintptr_t)(lds_char *)lds;  // LDS byte offset of the array
@@ -154,7 +161,7 @@ __global__ __launch_bounds__(T::NT) void gemm_f32_direct_kernel(GemmArgs p)
                 for (int i = 0; i < T::A16; ++i) load_to_lds<16>(st + (T::A16 * w + i) * 1024, asrc[i] + k0);
             }
             if constexpr (WIDE && SADDR) {
-                const float *bbase = p.B + (int64_t)k0 * p.ldb + n0;
+                const float *bbase = p.B + (int64_t)k0 * p.ldb + nb0;
 #pragma unroll
                 for (int i = 0; i < T::B16; ++i)
                     load_to_lds_s16(st + T::A_BYTES + (T::B16 * w + i) * 1024, bbase, boff[i]);
@@ -217,8 +224,8 @@ __global__ __launch_bounds__(T::NT) void gemm_f32_direct_kernel(GemmArgs p)
     if (!T::GEN || wide_b) k_loop(std::true_type{});
     else k_loop(std::false_type{});
 
-    if constexpr (ADD) direct_store_add<T>(p, m0, n0, wm0, wn0, lane, acc);
-    else direct_store<T>(p, m0, n0, wm0, wn0, lane, acc, [](int gn) { return gn; });
+    if constexpr (ADD) direct_store_add<T>(p, m0, nb0, n0, wm0, wn0, lane, acc);
+    else direct_store<T>(p, m0, nb0, n0, wm0, wn0, lane, acc, [](int gn) { return gn; });
 }
 
 template <class T, bool SB = true, bool ADD = false>
@@ -244,9 +251,9 @@ static bool direct_f32_offsets_fit(const GemmArgs &a)
     return 4 * (255 * a.lda + 32) < kOffMax && 4 * (31 * a.ldb + 256) < kOffMax;
 }
 
-bool direct_f32_wide_ok(const GemmArgs &a)
+bool direct_f32_wide_ok(const GemmArgs &a, int bn)
 {
-    return a.K % 16 == 0 && a.N >= 4 && a.N % 4 == 0 && direct_f32_offsets_fit(a);
+    return a.K % 16 == 0 && a.N >= 4 && (a.N % 4 == 0 || a.N >= bn) && direct_f32_offsets_fit(a);
 }
 
 namespace {
@@ -259,9 +266,9 @@ namespace {
 template <int BM, int BN, int WM, int WN, int NS, bool ADD = false>
 hipError_t launch_lean_or_general(const GemmArgs &a, hipStream_t stream)
 {
-    if (direct_f32_wide_ok(a) && a.K % 32 == 0)
+    if (direct_f32_wide_ok(a, BN) && a.K % 32 == 0)
         return launch_direct<DirectF32<BM, BN, WM, WN, NS / 2, false, 32>, true, ADD>(a, stream);
-    if (direct_f32_wide_ok(a)) return launch_direct<DirectF32<BM, BN, WM, WN, NS, false>, true, ADD>(a, stream);
+    if (direct_f32_wide_ok(a, BN)) return launch_direct<DirectF32<BM, BN, WM, WN, NS, false>, true, ADD>(a, stream);
     return direct_f32_offsets_fit(a) ? launch_direct<DirectF32<BM, BN, WM, WN, NS, true>, true, ADD>(a, stream)
                                      : launch_direct<DirectF32<BM, BN, WM, WN, NS, true>, false, ADD>(a, stream);
 }
@@ -273,7 +280,7 @@ hipError_t gemm_direct_launch(DirectTile t, const GemmArgs &a, hipStream_t strea
     switch (t) {
     case DirectTile::T256:
         // K-steps of 32 (two 64 KB stages) where K allows, else of 16 (four 32 KB stages)
-        if (!direct_f32_wide_ok(a)) return hipErrorInvalidValue;
+        if (!direct_f32_wide_ok(a, 256)) return hipErrorInvalidValue;
         if (a.K % 32 == 0) return launch_direct<DirectF32<256, 256, 128, 64, 2, false, 32>>(a, stream);
         return launch_direct<DirectF32<256, 256, 128, 64, 4, false>>(a, stream);
     case DirectTile::T128:
