@@ -759,12 +759,31 @@ def sweep(kind, torch, mm, dev):
                 del A, B, C
     else:
         VN = 4096
+        # The per-launch floor: kernels with next to no work, launched back to back (host
+        # rate) and replayed from a HIP graph (the GPU's own dispatch-to-completion time).
+        one = torch.empty(1, device=dev)
+        xa = torch.rand(64, device=dev)
+        ya = torch.empty(1, device=dev)
+
+        def fill(i, st):
+            one.zero_()
+
+        def tiny_gemv(i, st):
+            mm.mm_gemv_f32(1, 64, xa, xa, ya, st)
+        floor_rows = []
+        for name, fn in (("torch fill of 1 float", fill), ("mm_gemv_f32 1 x 64", tiny_gemv)):
+            floor_rows.append((name, burst_time_ms(torch, fn, 500), graph_time_ms(torch, fn, 500)))
+        floor_graph = min(r[2] for r in floor_rows)
+        print("# per-launch floor (kernels with next to no work, 500 launches):")
+        for name, tb, tg in floor_rows:
+            print(f"#   {name:24s} back-to-back {tb * 1e3:6.2f} us   replayed from a HIP graph "
+                  f"{tg * 1e3:6.2f} us")
         print("# fp32 GEMV y = A x, N = 4096: time per launch vs M (back-to-back launches "
-              "between two events)")
+              "between two events; graph: the same launches replayed from a HIP graph)")
         print("#   cold: the launches rotate over matrices totalling >= 512 MiB (more than the "
               "256 MB Infinity Cache); warm: one matrix, launched repeatedly")
         print(f"{'M':>7s} {'MiB':>7s} {'cold_us':>9s} {'cold_GB/s':>10s} {'warm_us':>9s} "
-              f"{'warm_GB/s':>10s}")
+              f"{'warm_GB/s':>10s} {'graph_cold_us':>14s}")
         rows = []
         for VM in (256, 512, 1024, 2048, 4096, 8192, 16384, 32768):
             sets = max(2, min(16, (512 << 20) // (VM * VN * 4)))
@@ -782,9 +801,10 @@ def sweep(kind, torch, mm, dev):
             by = rl.gemv_algorithmic_bytes(VM, VN)
             tc = burst_time_ms(torch, cold, reps)
             tw = burst_time_ms(torch, warm, reps)
+            tg = graph_time_ms(torch, cold, reps)
             rows.append((VM, by, tc))
             print(f"{VM:7d} {VM * VN * 4 / 2**20:7.0f} {tc * 1e3:9.2f} {by / tc / 1e6:10.0f} "
-                  f"{tw * 1e3:9.2f} {by / tw / 1e6:10.0f}", flush=True)
+                  f"{tw * 1e3:9.2f} {by / tw / 1e6:10.0f} {tg * 1e3:14.2f}", flush=True)
             del As, xs, ys
         # least-squares line t = t0 + bytes / rate over the cold points with M >= 2048
         pts = [(b, t) for (m, b, t) in rows if m >= 2048]
@@ -796,6 +816,14 @@ def sweep(kind, torch, mm, dev):
         rate = 1e3 / slope                      # bytes per second
         print(f"# cold fit over M >= 2048: fixed {t0 * 1e3:.2f} us per launch + streaming at "
               f"{rate / 1e9:.0f} GB/s ({100 * rate / rl.MI355X_HBM_PEAK:.1f}% of 8 TB/s)")
+        by = rl.gemv_algorithmic_bytes(4096, VN)
+        best = by / (floor_graph * 1e-3 + by / rl.MI355X_HBM_PEAK)
+        print(f"# single-launch ceiling for the 4096 x 4096 GEMV: even streaming at the full 8 TB/s, "
+              f"one launch takes at least the graph-replayed floor {floor_graph * 1e3:.2f} us + "
+              f"{by / rl.MI355X_HBM_PEAK * 1e6:.2f} us, i.e. at most {best / 1e9:.0f} GB/s = "
+              f"{100 * best / rl.MI355X_HBM_PEAK:.1f}% of 8 TB/s; at the fitted streaming rate, "
+              f"{t0 * 1e3 + by / rate * 1e6:.2f} us = {100 * by / (t0 * 1e-3 + by / rate) / rl.MI355X_HBM_PEAK:.1f}%; "
+              f"80% needs {by / (0.8 * rl.MI355X_HBM_PEAK) * 1e6:.2f} us")
         # What another implementation's single cold launch over the same bytes reaches: the
         # framework's row-sum reduction reads a 4096 x 4096 matrix once and writes 4096
         # floats, the GEMV's traffic without x (not part of the path, a reference point).
