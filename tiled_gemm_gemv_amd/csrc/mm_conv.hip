@@ -167,7 +167,10 @@ __global__ __launch_bounds__(T::NT) void conv_direct_kernel(GemmArgs p, Im2colOp
     int tm, tn;
     tile_of_block((int)bid, (int)tiles, tiles_m, tiles_n, 8, tm, tn);
     const int m0 = tm * T::BM, n0 = tn * T::BN;
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    // the wave index in a scalar register: the rows a wave gathers, their (c, r, s) and
+    // offsets, and the branches that step them are then scalar work
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int wm0 = (w / (T::BN / T::WN)) * T::WM, wn0 = (w % (T::BN / T::WN)) * T::WN;
     const int nk = (p.K + T::BK - 1) / T::BK;
     const float *zeros = kZeros + lane;
