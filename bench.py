@@ -20,10 +20,11 @@ CPU oracle (64+ sampled GEMM rows in full, every GEMV output) and the oracle's
 own time on a bounded sample of the same work is reported as `cpu_baseline`.
 
 Profiling helpers (same script, for rocprofv3 runs): --only gemm | gemv | copy | h16 |
-conv runs just that kernel `--steps` times with no oracle; `copy` is a plain
-device-to-device copy of known size used to calibrate HBM counters; `h16` is the
-bf16-input GEMM at the projection shape; `conv` the 3x3 convolution layer
-(N=32, C=K=128, 28x28).
+conv | split | gemm1024 | ragged runs just that kernel `--steps` times with no oracle;
+`copy` is a plain device-to-device copy of known size used to calibrate HBM counters;
+`h16` is the bf16-input GEMM at the projection shape; `conv` the 3x3 convolution layer
+(N=32, C=K=128, 28x28); `split` the FC layer on a batch of 128 through both K splits;
+`gemm1024` and `ragged` the fp32 GEMM at 1024^3 and 1000 x 1531 x 777.
 
 Sweeps (tables, not the benchmark line): --sweep conv times every convolution tile
 configuration on the layer workloads; --sweep gemm times every GEMM tile
@@ -222,7 +223,8 @@ def main():
     ap.add_argument("--gemv-reps", type=int, default=400)
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="target length of the oracle's timed sample")
-    ap.add_argument("--only", choices=["gemm", "gemv", "copy", "h16", "conv", "split"], default=None,
+    ap.add_argument("--only", choices=["gemm", "gemv", "copy", "h16", "conv", "split", "gemm1024", "ragged"],
+                    default=None,
                     help="profiling helper: launch only this kernel --steps times")
     ap.add_argument("--clock-seconds", type=float, default=None,
                     help="length of the clock phase (default 2.5 s after the timed steps; "
@@ -298,6 +300,20 @@ def main():
             mm.mm_gemm_f32_ws(SM, SN, SK, A, SK, B, SN, C, SN, ws, ws.numel(), stream)
         torch.cuda.synchronize()
         log(f"split: {args.steps} mm_gemm_f32 and {args.steps} mm_gemm_f32_ws calls at {SM}x{SN}x{SK}")
+        return
+
+    if args.only in ("gemm1024", "ragged"):
+        # the report-only GEMM workloads, in the configuration mm_gemm_f32 chooses
+        w = wl.WORKLOADS["gemm1024" if args.only == "gemm1024" else "gemm_ragged"]
+        Ah, Bh = wl.gemm_inputs(w)
+        A = torch.from_numpy(Ah).to(dev)
+        B = torch.from_numpy(Bh).to(dev)
+        C = torch.empty((w.M, w.N), dtype=torch.float32, device=dev)
+        for _ in range(args.steps):
+            mm.mm_gemm_f32(w.M, w.N, w.K, A, w.K, B, w.N, C, w.N, stream)
+        torch.cuda.synchronize()
+        log(f"{args.only}: {args.steps} launches of {w.describe()}, config "
+            f"{mm.mm_gemm_f32_config_name(mm.mm_gemm_f32_select(w.M, w.N, w.K))}")
         return
 
     if args.only == "conv":
