@@ -55,6 +55,10 @@ struct Im2colOperands {
     int Q, PQ, HW, RS, CHW;
     int sK, rK, cK;  // one K-step (BK rows) of the im2col matrix: s += sK, r += rK, c += cK (with carries)
     int64_t KPQ;
+    // the direct gather's tap-mask path (R S <= 31, a run of x below 2^31 bytes): 1 if taken,
+    // and the run's size in bytes (the bound of its buffer loads)
+    int tap_masks;
+    unsigned run_bytes;
 
     // Output column (n, p, q): input row h0 and column w0 under the filter's first
     // tap, and base = offset of x[n][0][h0][w0] (negative when in the padding).
@@ -151,7 +155,14 @@ struct Im2colOperands {
 // K-step and stepped across the wave's 4 consecutive rows. An element that is zero
 // (padding, k >= K, column >= N) is read from kZeros, so a partial last K-step needs
 // no clearing. A's partial step takes 4-byte lanes with the same rule.
-template <class T>
+// MASK: each lane also keeps, per column, a bit per filter tap (r S + s < 31) that is set
+// where the tap falls in the padding (bit 31 always set). A B element is then read by a
+// buffer load of x (the run's size as the bound) at byte offset (column base + row offset)
+// * 4, or at 2^31 for a padded tap or a row past K: that offset is beyond the run (runs are
+// kept below 2^31 bytes), so the load returns 0. Three vector instructions per element
+// (shift-add, bit extract, bit select) instead of the bounds tests and a 64-bit pointer
+// select.
+template <class T, bool MASK>
 __global__ __launch_bounds__(T::NT) void conv_direct_kernel(GemmArgs p, Im2colOperands o)
 {
     static_assert(T::B_ROW <= 1024 && (T::B4 * 256) % T::B_ROW == 0, "a wave's B loads cover whole rows");
@@ -195,6 +206,24 @@ __global__ __launch_bounds__(T::NT) void conv_direct_kernel(GemmArgs p, Im2colOp
         cols[h] = o.columns_of(p, col);
     }
     static_assert((T::BK / 2) % ROWS == 0, "a wave's rows lie in one half of the K-step: they share swz_b");
+    // the tap-mask path: per column, bit r S + s set where that tap is in the padding (or the
+    // column is past N), and the column's base offset in bytes
+    unsigned pad_taps[PER_ROW], base4[PER_ROW];
+    __amdgpu_buffer_rsrc_t xrsrc;
+    if constexpr (MASK) {
+        xrsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(p.B), (short)0, (int)o.run_bytes, 0x00020000);
+#pragma unroll
+        for (int h = 0; h < PER_ROW; ++h) {
+            unsigned m = 0x80000000u;
+            for (int r = 0, t = 0; r < o.R; ++r) {
+                const bool hin = (unsigned)(cols[h].h0 + r * o.dh) < (unsigned)o.H;
+                for (int ss = 0; ss < o.S; ++ss, ++t)
+                    if (!hin || (unsigned)(cols[h].w0 + ss * o.dw) >= (unsigned)o.W) m |= 1u << t;
+            }
+            pad_taps[h] = m;
+            base4[h] = (unsigned)cols[h].base * 4u;
+        }
+    }
 
     const unsigned lds0 = (unsigned)(uintptr_t)(lds_char *)lds;
     // (c, r, s) of row krow0 of the next K-step to issue (one division, here)
@@ -230,16 +259,29 @@ __global__ __launch_bounds__(T::NT) void conv_direct_kernel(GemmArgs p, Im2colOp
         const int cr = fr >= o.R;
         fr -= cr ? o.R : 0;
         fc += o.cK + cr;
+        int tap = r * o.S + s;  // the row's filter tap (scalar)
 #pragma unroll
         for (int rr = 0; rr < ROWS; ++rr) {
 #pragma unroll
             for (int h = 0; h < PER_ROW; ++h) {
-                const int hh = cols[h].h0 + dy, ww = cols[h].w0 + dx;
-                const bool ok = k < p.K && (unsigned)hh < (unsigned)o.H && (unsigned)ww < (unsigned)o.W;
-                const float *src = ok ? reinterpret_cast<const float *>(x + (unsigned)(cols[h].base + rowoff) * 4u)
-                                      : zeros;
-                load_to_lds<4>(st + T::A_BYTES + (krow0 + rr) * T::B_ROW + 256 * h, src);
+                const unsigned dst = st + T::A_BYTES + (krow0 + rr) * T::B_ROW + 256 * h;
+                if constexpr (MASK) {
+                    // a padded tap or a row past K (tap 31) reads at 2^31, past the run
+                    const int bit = k < p.K ? tap : 31;
+                    const unsigned pad = (unsigned)__builtin_amdgcn_sbfe((int)pad_taps[h], bit, 1);
+                    const unsigned v = base4[h] + (unsigned)rowoff * 4u;
+                    const unsigned off = (pad & 0x80000000u) | (~pad & v);
+                    asm volatile("s_nop 0\n\tbuffer_load_dword %0, %1, 0 offen lds"
+                                 :: "v"(off), "s"(xrsrc), "{m0}"(dst) : "memory");
+                } else {
+                    const int hh = cols[h].h0 + dy, ww = cols[h].w0 + dx;
+                    const bool ok = k < p.K && (unsigned)hh < (unsigned)o.H && (unsigned)ww < (unsigned)o.W;
+                    const float *src = ok ? reinterpret_cast<const float *>(x + (unsigned)(cols[h].base + rowoff) * 4u)
+                                          : zeros;
+                    load_to_lds<4>(dst, src);
+                }
             }
+            ++tap;
             ++k;
             dx += o.dw;
             rowoff += o.dw;
@@ -251,6 +293,7 @@ __global__ __launch_bounds__(T::NT) void conv_direct_kernel(GemmArgs p, Im2colOp
                 if (++r == o.R) {
                     r = 0;
                     dy = 0;
+                    tap = 0;
                     rowoff += o.HW - o.R * o.dh * o.W;
                 }
             }
@@ -292,8 +335,9 @@ hipError_t launch_conv_direct(const GemmArgs &a, const Im2colOperands &o, hipStr
     GemmArgs ga = a;
     Im2colOperands oa = o;
     void *args[] = {&ga, &oa};
-    return hipLaunchKernel(reinterpret_cast<const void *>(&conv_direct_kernel<T>), dim3(gx, gy), dim3(T::NT),
-                           args, 0, stream);
+    const void *fn = o.tap_masks ? reinterpret_cast<const void *>(&conv_direct_kernel<T, true>)
+                                 : reinterpret_cast<const void *>(&conv_direct_kernel<T, false>);
+    return hipLaunchKernel(fn, dim3(gx, gy), dim3(T::NT), args, 0, stream);
 }
 
 struct ConvConfig {
@@ -305,6 +349,8 @@ struct ConvConfig {
     int wg_per_cu;      // workgroups one CU holds (registers and LDS)
     double tflops;      // rate of the tile on the gather, for the choice below
     int bk;             // K-step depth
+    bool direct = false;  // the direct-to-LDS gather (conv_direct_kernel)
+    double fill_waves = 8;  // waves per CU at which the tile reaches its rate
 };
 
 template <class T>
@@ -323,17 +369,22 @@ const ConvConfig kConvConfigs[] = {
     {"64x64x64 w32x32 pf2 ks1 (4 waves)", &launch_im2col<T64x64k64p2>, 3, 64, 64, 4, 2, 90, 64},
     {"64x64x64 w32x32 pf2 ks2 (8 waves)", &launch_im2col<T64x64k64p2s2>, 4, 64, 64, 8, 2, 86, 64},
     {"128x64x64 w64x32 pf1 ks2 (8 waves)", &launch_im2col<T128x64k64s2>, 5, 128, 64, 8, 1, 80, 64},
-    // K-steps of 16 in 4 stages: K-steps of 32 in 2 stages (the GEMM's choice where K % 32
-    // == 0) measured +2-4% on the 3 x 3 layers but -3% on the 7 x 7 input layer (C R S =
-    // 147), which is the one these tiles are chosen for
-    {"64x64x16 w32x32 direct-to-LDS gather 4 stages (4 waves)", &launch_conv_direct<DirectF32<64, 64, 32, 32, 4, false>>,
-     13, 64, 64, 4, 5, 85, 16},
+    // The direct gather (timed on the tap-mask path): the 64 x 64 tile in K-steps of 32 and
+    // 2 stages (5 workgroups per CU) beat K-steps of 16 in 4 stages by 7% on the dilated
+    // 3 x 3 layer and 2% on the 3 x 3 one, within 1% elsewhere. The 128 x 128 tile: K-steps
+    // of 32 in 2 stages are 6% faster where a CU holds one workgroup (the 3 x 3 layer at 128
+    // filters: 196 tiles), 16 in 4 stages 4% faster where it holds two (256 filters).
+    {"64x64x32 w32x32 direct-to-LDS gather 2 stages (4 waves)",
+     &launch_conv_direct<DirectF32<64, 64, 32, 32, 2, false, 32>>, 13, 64, 64, 4, 5, 95, 32, true, 4},
     {"128x128x16 w64x64 direct-to-LDS gather 4 stages (4 waves)",
-     &launch_conv_direct<DirectF32<128, 128, 64, 64, 4, false>>, 11, 128, 128, 4, 2, 115, 16},
+     &launch_conv_direct<DirectF32<128, 128, 64, 64, 4, false>>, 11, 128, 128, 4, 2, 115, 16, true, 6},
+    {"128x128x32 w64x64 direct-to-LDS gather 2 stages (4 waves)",
+     &launch_conv_direct<DirectF32<128, 128, 64, 64, 2, false, 32>>, 11, 128, 128, 4, 2, 112, 32, true, 4},
 };
 constexpr int kNumConvConfigs = sizeof(kConvConfigs) / sizeof(kConvConfigs[0]);
 constexpr int64_t kMaxI32 = 0x7fffffff;
-constexpr int64_t kMaxRun = (int64_t(1) << 30) - 1;  // elements of x per launch
+constexpr int64_t kMaxRun = (int64_t(1) << 30) - 1;      // elements of x per launch
+constexpr int64_t kMaxMaskRun = (int64_t(1) << 29) - 1;  // ... with the direct gather's tap masks
 
 }  // namespace
 
@@ -355,7 +406,8 @@ int conv_select_config(int64_t M, int64_t N, int64_t K)
     for (int c = 0; c < kNumConvConfigs; ++c) {
         const ConvConfig &k = kConvConfigs[c];
         const int64_t tiles = ((M + k.bm - 1) / k.bm) * ((N + k.bn - 1) / k.bn);
-        const double t = tile_time(tiles, k.bm, k.bn, k.waves, k.wg_per_cu, k.tflops) * k_steps_factor(K, k.bk);
+        const double t = tile_time(tiles, k.bm, k.bn, k.waves, k.wg_per_cu, k.tflops, k.fill_waves) *
+                         k_steps_factor(K, k.bk);
         if (c == 0 || t < best_t) {
             best = c;
             best_t = t;
@@ -448,8 +500,11 @@ hipError_t conv_launch(int cfg, const ConvArgs &a, hipStream_t stream)
     o.rK = (int)((bk / a.S) % a.R);
     o.cK = (int)(bk / (a.R * a.S));
     o.KPQ = KPQ;
-    // images per launch: x offsets below 2^30, product columns below 2^31
-    int64_t per = kMaxRun / CHW;
+    // images per launch: x offsets below 2^30, product columns below 2^31; the direct
+    // gather's tap masks need a filter of at most 31 taps and runs below 2^31 bytes
+    const bool masks = kConvConfigs[cfg].direct && a.R * a.S <= 31 && CHW <= kMaxMaskRun;
+    o.tap_masks = masks ? 1 : 0;
+    int64_t per = (masks ? kMaxMaskRun : kMaxRun) / CHW;
     if (kMaxI32 / PQ < per) per = kMaxI32 / PQ;
     for (int64_t n0 = 0; n0 < a.N; n0 += per) {
         const int64_t nb = (a.N - n0 < per) ? a.N - n0 : per;
@@ -463,6 +518,7 @@ hipError_t conv_launch(int cfg, const ConvArgs &a, hipStream_t stream)
         g.M = (int)a.K;
         g.N = (int)(nb * PQ);
         g.K = (int)(a.C * a.R * a.S);
+        o.run_bytes = (unsigned)(nb * CHW * 4);
         const hipError_t e = kConvConfigs[cfg].launch(g, o, stream);
         if (e != hipSuccess) return e;
     }
