@@ -313,14 +313,19 @@ __global__ __launch_bounds__(T::NT) void conv_direct_kernel(GemmArgs p, Im2colOp
     // loads per wave per K-step (a partial step issues more: the count is then conservative)
     constexpr int L = T::A16 + T::B4;
     static_assert((T::NS - 2) * L <= 63, "vmcnt range");
+    // The step NS - 1 ahead goes into the stage read in the previous step, free once every
+    // wave is past the barrier. With two waves per SIMD it is issued before this step's
+    // MFMAs, which then cover its latency while the other wave fills the matrix core (3 x 3
+    // layers +2-6%); with one, the MFMAs go first and the gather's address work runs
+    // while they execute (the 64 x 64 tile on the 3 x 3 layer: 70.3 against 68.3).
+    constexpr bool kIssueFirst = T::WAVES >= 8;
     for (int st = 0; st < T::NS - 1 && st < nk; ++st) issue(st);
     for (int kt = 0; kt < nk; ++kt) {
         wait_steps<L, T::NS - 2>(nk - 1 - kt);
         __syncthreads();
-        // the MFMAs first: the gather's address work for the step NS - 1 ahead then runs
-        // while they execute
+        if (kIssueFirst && kt + T::NS - 1 < nk) issue(kt + T::NS - 1);
         direct_multiply<T>((const lds_char *)lds + (kt % T::NS) * T::STAGE, a_off, b_off, acc);
-        if (kt + T::NS - 1 < nk) issue(kt + T::NS - 1);
+        if (!kIssueFirst && kt + T::NS - 1 < nk) issue(kt + T::NS - 1);
     }
     direct_store<T>(p, m0, n0, n0, wm0, wn0, lane, acc, [&](int gn) { return o.c_column(p, gn); });
 }
@@ -369,17 +374,21 @@ const ConvConfig kConvConfigs[] = {
     {"64x64x64 w32x32 pf2 ks1 (4 waves)", &launch_im2col<T64x64k64p2>, 3, 64, 64, 4, 2, 90, 64},
     {"64x64x64 w32x32 pf2 ks2 (8 waves)", &launch_im2col<T64x64k64p2s2>, 4, 64, 64, 8, 2, 86, 64},
     {"128x64x64 w64x32 pf1 ks2 (8 waves)", &launch_im2col<T128x64k64s2>, 5, 128, 64, 8, 1, 80, 64},
-    // The direct gather (timed on the tap-mask path): the 64 x 64 tile in K-steps of 32 and
-    // 2 stages (5 workgroups per CU) beat K-steps of 16 in 4 stages by 7% on the dilated
-    // 3 x 3 layer and 2% on the 3 x 3 one, within 1% elsewhere. The 128 x 128 tile: K-steps
-    // of 32 in 2 stages are 6% faster where a CU holds one workgroup (the 3 x 3 layer at 128
-    // filters: 196 tiles), 16 in 4 stages 4% faster where it holds two (256 filters).
+    // The direct gather (timed on the tap-mask path, TFLOP/s). 64 x 64: K-steps of 32 in 2
+    // stages (5 workgroups per CU) beat 16 in 4 stages (dilated 3 x 3 layer 70.0 against
+    // 65.4, 3 x 3 70.2 against 68.7). 128 x 128 and 64 x 128 on 8 waves (wave tiles of
+    // 64 x 32 and 32 x 32, two waves per SIMD) beat 4 waves: 3 x 3 layer 79.4 against 73.1,
+    // 3 x 3 at 256 filters 85.4 against 83.0, dilated 3 x 3 (64 filters: 256 tiles of
+    // 64 x 128) 74.0. The 128 x 128 tiles: K-steps of 32 in 2 stages where a CU holds one
+    // workgroup (196 tiles), 16 in 4 stages (fill_waves 16) where it holds two.
     {"64x64x32 w32x32 direct-to-LDS gather 2 stages (4 waves)",
      &launch_conv_direct<DirectF32<64, 64, 32, 32, 2, false, 32>>, 13, 64, 64, 4, 5, 95, 32, true, 4},
-    {"128x128x16 w64x64 direct-to-LDS gather 4 stages (4 waves)",
-     &launch_conv_direct<DirectF32<128, 128, 64, 64, 4, false>>, 11, 128, 128, 4, 2, 115, 16, true, 6},
-    {"128x128x32 w64x64 direct-to-LDS gather 2 stages (4 waves)",
-     &launch_conv_direct<DirectF32<128, 128, 64, 64, 2, false, 32>>, 11, 128, 128, 4, 2, 112, 32, true, 4},
+    {"128x128x16 w64x32 direct-to-LDS gather 4 stages (8 waves)",
+     &launch_conv_direct<DirectF32<128, 128, 64, 32, 4, false>>, 11, 128, 128, 8, 2, 122, 16, true, 16},
+    {"128x128x32 w64x32 direct-to-LDS gather 2 stages (8 waves)",
+     &launch_conv_direct<DirectF32<128, 128, 64, 32, 2, false, 32>>, 11, 128, 128, 8, 2, 120, 32, true, 8},
+    {"64x128x32 w32x32 direct-to-LDS gather 2 stages (8 waves)",
+     &launch_conv_direct<DirectF32<64, 128, 32, 32, 2, false, 32>>, 13, 64, 128, 8, 3, 105, 32, true, 8},
 };
 constexpr int kNumConvConfigs = sizeof(kConvConfigs) / sizeof(kConvConfigs[0]);
 constexpr int64_t kMaxI32 = 0x7fffffff;
