@@ -59,6 +59,8 @@ struct Im2colOperands {
     // and the run's size in bytes (the bound of its buffer loads)
     int tap_masks;
     unsigned run_bytes;
+    // the tap-mask path's row table in LDS (K rounded up to whole K-steps, 8 bytes a row)
+    int row_table;
 
     // Output column (n, p, q): input row h0 and column w0 under the filter's first
     // tap, and base = offset of x[n][0][h0][w0] (negative when in the padding).
@@ -162,9 +164,10 @@ struct Im2colOperands {
 // kept below 2^31 bytes), so the load returns 0. Three vector instructions per element
 // (shift-add, bit extract, bit select) instead of the bounds tests and a 64-bit pointer
 // select.
-template <class T, bool MASK>
+template <class T, bool MASK, bool TABLE>
 __global__ __launch_bounds__(T::NT) void conv_direct_kernel(GemmArgs p, Im2colOperands o)
 {
+    static_assert(MASK || !TABLE, "the row table feeds the tap-mask path");
     static_assert(T::B_ROW <= 1024 && (T::B4 * 256) % T::B_ROW == 0, "a wave's B loads cover whole rows");
     constexpr int ROWS = T::B4 * 256 / T::B_ROW;      // k rows of a K-step one wave loads
     constexpr int PER_ROW = T::B_ROW / 256;           // loads per row
@@ -186,6 +189,21 @@ __global__ __launch_bounds__(T::NT) void conv_direct_kernel(GemmArgs p, Im2colOp
     const int nk = (p.K + T::BK - 1) / T::BK;
     const float *zeros = kZeros + lane;
     const char *x = reinterpret_cast<const char *>(p.B);
+    // TABLE: per im2col row k, its offset in x from the column's base and its filter tap
+    // (31 past K: the tap masks' always-set bit), built once per workgroup
+    extern __shared__ int2 ktab[];
+    if constexpr (TABLE) {
+        for (int e = threadIdx.x; e < nk * T::BK; e += T::NT) {
+            int2 t = {0, 31};
+            if (e < p.K) {
+                const int c = e / o.RS, rs = e - c * o.RS, r = rs / o.S, s = rs - r * o.S;
+                t.x = c * o.HW + r * o.dh * o.W + s * o.dw;
+                t.y = rs;
+            }
+            ktab[e] = t;
+        }
+        __syncthreads();
+    }
 
     // A: 16-byte lanes on full K-steps (sources at k0 = 0)
     const float *asrc[T::A16];
@@ -244,6 +262,22 @@ __global__ __launch_bounds__(T::NT) void conv_direct_kernel(GemmArgs p, Im2colOp
                 const float *src = k < p.K ? p.A + (int64_t)min(m0 + row, p.M - 1) * p.lda + k : zeros;
                 load_to_lds<4>(st + (T::A4 * w + i) * 256, src);
             }
+        }
+        if constexpr (TABLE) {
+#pragma unroll
+            for (int rr = 0; rr < ROWS; ++rr) {
+                const int2 t = ktab[k0 + krow0 + rr];
+#pragma unroll
+                for (int h = 0; h < PER_ROW; ++h) {
+                    const unsigned dst = st + T::A_BYTES + (krow0 + rr) * T::B_ROW + 256 * h;
+                    const unsigned pad = (unsigned)__builtin_amdgcn_sbfe((int)pad_taps[h], t.y, 1);
+                    const unsigned v = base4[h] + (unsigned)t.x * 4u;
+                    const unsigned off = (pad & 0x80000000u) | (~pad & v);
+                    asm volatile("s_nop 0\n\tbuffer_load_dword %0, %1, 0 offen lds"
+                                 :: "v"(off), "s"(xrsrc), "{m0}"(dst) : "memory");
+                }
+            }
+            return;
         }
         // (c, r, s) of the wave's first row: carried over from the previous issue (the
         // steps are issued in order), then stepped across the wave's rows
@@ -340,9 +374,11 @@ hipError_t launch_conv_direct(const GemmArgs &a, const Im2colOperands &o, hipStr
     GemmArgs ga = a;
     Im2colOperands oa = o;
     void *args[] = {&ga, &oa};
-    const void *fn = o.tap_masks ? reinterpret_cast<const void *>(&conv_direct_kernel<T, true>)
-                                 : reinterpret_cast<const void *>(&conv_direct_kernel<T, false>);
-    return hipLaunchKernel(fn, dim3(gx, gy), dim3(T::NT), args, 0, stream);
+    const void *fn = !o.tap_masks  ? reinterpret_cast<const void *>(&conv_direct_kernel<T, false, false>)
+                     : o.row_table ? reinterpret_cast<const void *>(&conv_direct_kernel<T, true, true>)
+                                   : reinterpret_cast<const void *>(&conv_direct_kernel<T, true, false>);
+    const size_t table = o.row_table ? (size_t)((a.K + T::BK - 1) / T::BK) * T::BK * 8 : 0;
+    return hipLaunchKernel(fn, dim3(gx, gy), dim3(T::NT), args, table, stream);
 }
 
 struct ConvConfig {
@@ -356,6 +392,7 @@ struct ConvConfig {
     int bk;             // K-step depth
     bool direct = false;  // the direct-to-LDS gather (conv_direct_kernel)
     double fill_waves = 8;  // waves per CU at which the tile reaches its rate
+    bool row_table = false; // the tap-mask gather reads its rows' offsets from an LDS table
 };
 
 template <class T>
@@ -384,16 +421,17 @@ const ConvConfig kConvConfigs[] = {
     {"64x64x32 w32x32 direct-to-LDS gather 2 stages (4 waves)",
      &launch_conv_direct<DirectF32<64, 64, 32, 32, 2, false, 32>>, 13, 64, 64, 4, 5, 95, 32, true, 4},
     {"128x128x16 w64x32 direct-to-LDS gather 4 stages (8 waves)",
-     &launch_conv_direct<DirectF32<128, 128, 64, 32, 4, false>>, 11, 128, 128, 8, 2, 122, 16, true, 16},
+     &launch_conv_direct<DirectF32<128, 128, 64, 32, 4, false>>, 11, 128, 128, 8, 2, 122, 16, true, 16, true},
     {"128x128x32 w64x32 direct-to-LDS gather 2 stages (8 waves)",
-     &launch_conv_direct<DirectF32<128, 128, 64, 32, 2, false, 32>>, 11, 128, 128, 8, 2, 120, 32, true, 8},
+     &launch_conv_direct<DirectF32<128, 128, 64, 32, 2, false, 32>>, 11, 128, 128, 8, 2, 120, 32, true, 8, true},
     {"64x128x32 w32x32 direct-to-LDS gather 2 stages (8 waves)",
-     &launch_conv_direct<DirectF32<64, 128, 32, 32, 2, false, 32>>, 13, 64, 128, 8, 3, 105, 32, true, 8},
+     &launch_conv_direct<DirectF32<64, 128, 32, 32, 2, false, 32>>, 13, 64, 128, 8, 3, 105, 32, true, 8, true},
 };
 constexpr int kNumConvConfigs = sizeof(kConvConfigs) / sizeof(kConvConfigs[0]);
 constexpr int64_t kMaxI32 = 0x7fffffff;
 constexpr int64_t kMaxRun = (int64_t(1) << 30) - 1;      // elements of x per launch
 constexpr int64_t kMaxMaskRun = (int64_t(1) << 29) - 1;  // ... with the direct gather's tap masks
+constexpr int64_t kMaxRowTable = 16 * 1024;                // bytes of LDS for the row table
 
 }  // namespace
 
@@ -513,6 +551,7 @@ hipError_t conv_launch(int cfg, const ConvArgs &a, hipStream_t stream)
     // gather's tap masks need a filter of at most 31 taps and runs below 2^31 bytes
     const bool masks = kConvConfigs[cfg].direct && a.R * a.S <= 31 && CHW <= kMaxMaskRun;
     o.tap_masks = masks ? 1 : 0;
+    o.row_table = masks && kConvConfigs[cfg].row_table && (a.C * a.R * a.S + bk - 1) / bk * bk * 8 <= kMaxRowTable;
     int64_t per = (masks ? kMaxMaskRun : kMaxRun) / CHW;
     if (kMaxI32 / PQ < per) per = kMaxI32 / PQ;
     for (int64_t n0 = 0; n0 < a.N; n0 += per) {
