@@ -20,11 +20,12 @@ CPU oracle (64+ sampled GEMM rows in full, every GEMV output) and the oracle's
 own time on a bounded sample of the same work is reported as `cpu_baseline`.
 
 Profiling helpers (same script, for rocprofv3 runs): --only gemm | gemv | copy | h16 |
-conv | split | gemm1024 | ragged runs just that kernel `--steps` times with no oracle;
+conv | split | gemm1024 | ragged | gemvt runs just that kernel `--steps` times with no oracle;
 `copy` is a plain device-to-device copy of known size used to calibrate HBM counters;
 `h16` is the bf16-input GEMM at the projection shape; `conv` the 3x3 convolution layer
 (N=32, C=K=128, 28x28); `split` the FC layer on a batch of 128 through both K splits;
-`gemm1024` and `ragged` the fp32 GEMM at 1024^3 and 1000 x 1531 x 777.
+`gemm1024` and `ragged` the fp32 GEMM at 1024^3 and 1000 x 1531 x 777; `gemvt` the
+transposed GEMV with a workspace (row blocks, then the sum) on the GEMV workload's matrices.
 
 Sweeps (tables, not the benchmark line): --sweep conv times every convolution tile
 configuration on the layer workloads; --sweep gemm times every GEMM tile
@@ -223,7 +224,8 @@ def main():
     ap.add_argument("--gemv-reps", type=int, default=400)
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="target length of the oracle's timed sample")
-    ap.add_argument("--only", choices=["gemm", "gemv", "copy", "h16", "conv", "split", "gemm1024", "ragged"],
+    ap.add_argument("--only", choices=["gemm", "gemv", "copy", "h16", "conv", "split", "gemm1024", "ragged",
+                                           "gemvt"],
                     default=None,
                     help="profiling helper: launch only this kernel --steps times")
     ap.add_argument("--clock-seconds", type=float, default=None,
@@ -356,6 +358,17 @@ def main():
             gemv(i % GEMV_SETS)
         torch.cuda.synchronize()
         log(f"gemv: {args.steps} launches")
+        return
+    if args.only == "gemvt":
+        # y = A^T x over the same rotating matrices (x has VM entries, y VN)
+        nbytes = mm.mm_gemv_t_f32_workspace_bytes(VM, VN)
+        ws = torch.empty(max(nbytes, 4), dtype=torch.uint8, device=dev)
+        xt = torch.randn(VM, device=dev)
+        yt = torch.empty(VN, device=dev)
+        for i in range(args.steps):
+            mm.mm_gemv_t_f32_ws(VM, VN, Avs[i % GEMV_SETS], xt, yt, ws, nbytes, stream)
+        torch.cuda.synchronize()
+        log(f"gemvt: {args.steps} launches of {VM} x {VN}, workspace {nbytes} bytes")
         return
 
     clock = ClockProbe(torch, dev)
