@@ -240,11 +240,16 @@ def test_conv_config_table(lib):
     assert n >= 1
     names = [mm.mm_conv2d_f32_config_name(i) for i in range(n)]
     assert all(names) and len(set(names)) == n
-    gemm_names = [mm.mm_gemm_f32_config_name(i) for i in range(mm.mm_gemm_f32_num_configs())]
-    # tile shapes of the GEMM (BMxBN and the wave tile; the K-step may differ)
-    def shape(nm):
-        return nm.split()[0].rsplit("x", 1)[0], nm.split()[1]
-    assert all(any(shape(name) == shape(g) for g in gemm_names) for name in names)
+    # each name states the tile (BM x BN x BK), the wave tile and the waves: the wave tiles
+    # divide the tile, and the waves are its wave grid (twice that where K is split over two
+    # wave groups, "ks2")
+    for name in names:
+        m = re.match(r"(\d+)x(\d+)x(\d+) w(\d+)x(\d+) .*\((\d+) waves\)", name)
+        assert m, name
+        bm, bn, bk, wm, wn, waves = map(int, m.groups())
+        assert bm % wm == 0 and bn % wn == 0 and bk % 16 == 0, name
+        grid = (bm // wm) * (bn // wn)
+        assert waves == (2 * grid if " ks2 " in name else grid), name
     assert mm.mm_conv2d_f32_config_name(n) is None
     for geo in [(1, 1, 1, 1, 1, 1, 1, 1, 1, 0, 0, 1, 1), (32, 3, 224, 224, 64, 7, 7, 2, 2, 3, 3, 1, 1),
                 (32, 128, 28, 28, 128, 3, 3, 1, 1, 1, 1, 1, 1), (32, 256, 56, 56, 64, 1, 1, 1, 1, 0, 0, 1, 1),
