@@ -1,5 +1,5 @@
-// mm_conv.hip -- fp32 2-D convolution as an implicit GEMM on the tiled matrix-core
-// kernel of mm_gemm_tile.h.
+// mm_conv.hip -- fp32 2-D convolution as an implicit GEMM on the matrix-core tiles:
+// the register-staged tiles of mm_gemm_tile.h and the direct-to-LDS tiles of mm_direct.h.
 //
 // The core of a convolutional layer can be recast as a matrix product, and im2col
 // is the classic way to do so ("Matrix Operations", docs.vulkan.org ML-inference
@@ -13,10 +13,12 @@
 // w exactly as stored, row k, column (c R + r) S + s -- with the CRS x NPQ im2col
 // matrix, whose row (c, r, s) and column (n, p, q) hold that x element.
 //
-// The im2col matrix is never written to memory. The tiled kernel stages it K-step
-// by K-step like any B operand, but its loader (Im2colOperands) computes every
-// element's address in x, or a zero for the padding, as it goes; the C store
-// scatters product column (n, p, q) to y[n][.][p][q]. The images are laid side by
+// The im2col matrix is never written to memory. The tiles stage it K-step by K-step
+// like any B operand, but its loader computes every element's address in x, or a zero
+// for the padding, as it goes: through registers on the register-staged tiles
+// (Im2colOperands), by 4-byte LDS DMA lanes straight into the B panel on the direct
+// ones (conv_direct_kernel); the C store scatters product column (n, p, q) to
+// y[n][.][p][q]. The images are laid side by
 // side along the product's columns (j = n P Q + p Q + q), so a batch of small
 // feature maps still makes one wide product that fills the chip. Beyond reading w
 // and x and writing y once, HBM traffic is only the x panels the L2 does not keep
@@ -32,8 +34,9 @@ namespace {
 
 constexpr int kFar = -(1 << 30);  // an input row that is outside any image
 
-// Read by the LDS DMA for every element of the product that is zero: a tap in the
-// padding, a row past K (partial K-step) or a column past N.
+// Read by the direct gather's LDS DMA, where it runs without tap masks, for every
+// element of the product that is zero: a tap in the padding, a row past K (partial
+// K-step) or a column past N.
 __device__ float kZeros[64];
 
 // B = the im2col matrix of a run of images of x (p.B points at the first), C = those
@@ -154,7 +157,7 @@ struct Im2colOperands {
 // A lane of a B load lands at a fixed column of one k row of the panel, so it keeps that
 // column's state (h0, w0, image offset) for the whole K loop; the row's (c, r, s) and
 // offset are the same in every lane (scalar registers), found by one division per
-// K-step and stepped across the wave's 4 consecutive rows. An element that is zero
+// workgroup and stepped across the wave's ROWS consecutive rows. An element that is zero
 // (padding, k >= K, column >= N) is read from kZeros, so a partial last K-step needs
 // no clearing. A's partial step takes 4-byte lanes with the same rule.
 // MASK: each lane also keeps, per column, a bit per filter tap (r S + s < 31) that is set
@@ -164,6 +167,9 @@ struct Im2colOperands {
 // kept below 2^31 bytes), so the load returns 0. Three vector instructions per element
 // (shift-add, bit extract, bit select) instead of the bounds tests and a 64-bit pointer
 // select.
+// TABLE (with MASK): the row offset and tap of every k come from a table the workgroup
+// writes into LDS before its first load, one wave-uniform LDS read per row instead of the
+// scalar stepping.
 template <class T, bool MASK, bool TABLE>
 __global__ __launch_bounds__(T::NT) void conv_direct_kernel(GemmArgs p, Im2colOperands o)
 {
