@@ -38,6 +38,7 @@ kernels much shorter than ~5 us are bounded by the host's launch rate instead).
 import argparse
 import hashlib
 import json
+import statistics
 import os
 import platform
 import sys
@@ -571,6 +572,11 @@ def burst_time_ms(torch, launch, reps):
     return e0.elapsed_time(e1) / reps
 
 
+def median_graph_ms(torch, launch, reps, runs=3):
+    """Median over `runs` graph-replayed timings (graph_time_ms) of the same launches."""
+    return statistics.median(graph_time_ms(torch, launch, reps) for _ in range(runs))
+
+
 def graph_time_ms(torch, launch, reps):
     """Average time per launch over `reps` launches captured in one HIP graph and replayed
     between two events: the kernels' own time on the GPU, without the host's launch rate
@@ -677,8 +683,8 @@ def sweep(kind, torch, mm, dev):
                    (1024, 512, 8192, "K in two halves"), (2048, 512, 8192, "K in two halves")]
         shapes += [(4096, n, 4096, f"FC layer 4096x4096, batch of {n}") for n in (1, 2, 4, 8, 16, 32, 64)]
         nc = mm.mm_gemm_f32_num_configs()
-        print("# fp32 GEMM, TFLOP/s per tile configuration (back-to-back launches between two "
-              "events, inputs N(0,1))")
+        print("# fp32 GEMM, TFLOP/s per tile configuration (launches captured in a HIP graph and "
+              "replayed between two events, median of 3 replays; inputs N(0,1))")
         for c in range(nc):
             print(f"#   cfg {c}: {mm.mm_gemm_f32_config_name(c)}")
         print("#   * = the configuration mm_gemm_f32 selects for the shape; default = mm_gemm_f32 itself "
@@ -696,12 +702,12 @@ def sweep(kind, torch, mm, dev):
             for c in range(nc):
                 def launch(i, st, c=c):
                     mm.mm_gemm_f32_config(c, M, N, K, A, K, B, N, C, N, st)
-                ms = burst_time_ms(torch, launch, reps)
+                ms = median_graph_ms(torch, launch, reps)
                 cells.append(f"{flop / ms / 1e9:7.1f}" + ("*" if c == sel else " "))
 
             def default(i, st):
                 mm.mm_gemm_f32(M, N, K, A, K, B, N, C, N, st)
-            cells.append(f"{flop / burst_time_ms(torch, default, reps) / 1e9:8.1f}")
+            cells.append(f"{flop / median_graph_ms(torch, default, reps) / 1e9:8.1f}")
             print(f"{M:6d} {N:6d} {K:6d}  " + " ".join(cells) + f"  {name}", flush=True)
             del A, B, C
         print("# strided batched GEMM (one mm_gemm_f32_batched launch) vs the same problems as "
@@ -721,8 +727,8 @@ def sweep(kind, torch, mm, dev):
             def separate(i, st):
                 for b in range(batch):
                     mm.mm_gemm_f32(M, N, K, A[b], K, B[b], N, C[b], N, st)
-            tb = burst_time_ms(torch, batched, reps)
-            ts = burst_time_ms(torch, separate, max(1, reps // 4))
+            tb = median_graph_ms(torch, batched, reps)
+            ts = median_graph_ms(torch, separate, max(1, reps // 4))
             print(f"{batch:6d} {M:6d} {N:6d} {K:6d} {flop / tb / 1e9:9.1f} {flop / ts / 1e9:9.1f}",
                   flush=True)
             del A, B, C
@@ -747,8 +753,8 @@ def sweep(kind, torch, mm, dev):
 
             def split(i, st):
                 mm.mm_gemm_f32_ws(M, N, K, A, K, B, N, C, N, ws, wsb, st)
-            tp = burst_time_ms(torch, plain, reps)
-            tw = burst_time_ms(torch, split, reps)
+            tp = median_graph_ms(torch, plain, reps)
+            tw = median_graph_ms(torch, split, reps)
             print(f"{M:6d} {N:6d} {K:6d} {chunks:7d} {flop / tp / 1e9:9.1f} {flop / tw / 1e9:9.1f}",
                   flush=True)
             del A, B, C, ws
