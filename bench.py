@@ -625,8 +625,8 @@ def launch_conv(mm, cw, x, f, y, stream, cfg=None):
 def sweep_conv(torch, mm, dev):
     nc = mm.mm_conv2d_f32_num_configs()
     peak = rl.MI355X_FP32_MFMA_PEAK
-    print("# fp32 convolution (implicit GEMM), TFLOP/s per tile configuration (back-to-back "
-          "launches between two events)")
+    print("# fp32 convolution (implicit GEMM), TFLOP/s per tile configuration (launches captured "
+          "in a HIP graph and replayed between two events, median of 3 replays)")
     for c in range(nc):
         print(f"#   cfg {c}: {mm.mm_conv2d_f32_config_name(c)}")
     print("#   default = mm_conv2d_f32's own choice (* marks it among the configs; 1x1 layers on "
@@ -649,12 +649,12 @@ def sweep_conv(torch, mm, dev):
         for c in range(nc):
             def launch(i, st, c=c):
                 launch_conv(mm, cw, x, f, y, st, c)
-            tf = flop / burst_time_ms(torch, launch, reps) / 1e9
+            tf = flop / median_graph_ms(torch, launch, reps) / 1e9
             cells.append(f"{tf:6.1f}" + ("*" if c == sel else " "))
 
         def launch_default(i, st):
             launch_conv(mm, cw, x, f, y, st)
-        td = flop / burst_time_ms(torch, launch_default, reps) / 1e9
+        td = flop / median_graph_ms(torch, launch_default, reps) / 1e9
         del x, y
         GM, GN, GK = cw.K, cw.N * P * Q, cw.C * cw.R * cw.S
         Bd = torch.randn(GK, GN, device=dev)
@@ -662,7 +662,7 @@ def sweep_conv(torch, mm, dev):
 
         def launch_dense(i, st):
             mm.mm_gemm_f32(GM, GN, GK, f, GK, Bd, GN, Cd, GN, st)
-        tdense = flop / burst_time_ms(torch, launch_dense, reps) / 1e9
+        tdense = flop / median_graph_ms(torch, launch_dense, reps) / 1e9
         print(f"{cw.name:>12s} {GM:7d} {GN:8d} {GK:7d} "
               f"{flop / 1e9:7.2f}  " + " ".join(cells) +
               f" {td:8.1f} {tdense:7.1f} {bound / 1e12:7.1f} {100 * td * 1e12 / bound:6.1f}",
