@@ -311,8 +311,9 @@ int64_t mm_conv2d_out_dim(int64_t in, int64_t filter, int64_t stride, int64_t pa
                           int64_t dil);
 
 /*
- * Tile configurations of the convolution (tile shapes of the GEMM, with an im2col
- * gather in place of the B loads), as for the GEMM:
+ * Tile configurations of the convolution (matrix-core tiles with an im2col gather in
+ * place of the B loads: the GEMM's register-staged tiles, and tiles whose gather moves
+ * x straight into the LDS), as for the GEMM:
  *   mm_conv2d_f32_num_configs, mm_conv2d_f32_config_name(cfg): count and names;
  *   mm_conv2d_f32_select: the config mm_conv2d_f32 uses for the geometry (same
  *     arguments without the pointers and stream), or -1 if it is invalid;
