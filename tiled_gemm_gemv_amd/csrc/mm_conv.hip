@@ -432,6 +432,12 @@ const ConvConfig kConvConfigs[] = {
      &launch_conv_direct<DirectF32<128, 128, 64, 32, 2, false, 32>>, 11, 128, 128, 8, 2, 120, 32, true, 8, true},
     {"64x128x32 w32x32 direct-to-LDS gather 2 stages (8 waves)",
      &launch_conv_direct<DirectF32<64, 128, 32, 32, 2, false, 32>>, 13, 64, 128, 8, 3, 105, 32, true, 8, true},
+    // K-steps of 64 (96 KB of LDS: one workgroup per CU) for layers of about one 64 x 128 tile
+    // per CU: twice the MFMAs per barrier and per gather issue. Dilated 3 x 3 layer (256
+    // tiles) 82.0 against 78.9; the 128 x 128 tile gains nothing from them (82.1 against
+    // 83.1 on the 3 x 3 layer).
+    {"64x128x64 w32x32 direct-to-LDS gather 2 stages (8 waves)",
+     &launch_conv_direct<DirectF32<64, 128, 32, 32, 2, false, 64>>, 13, 64, 128, 8, 1, 110, 64, true, 8, true},
 };
 constexpr int kNumConvConfigs = sizeof(kConvConfigs) / sizeof(kConvConfigs[0]);
 constexpr int64_t kMaxI32 = 0x7fffffff;

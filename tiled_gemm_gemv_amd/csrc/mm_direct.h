@@ -3,7 +3,7 @@
 // mm_conv.hip): tile parameters, the LDS layout's permutations, the DMA and wait
 // primitives, and the MFMA step on one stage.
 //
-// LDS layout of a stage (BK = 16 or 32 k per K-step):
+// LDS layout of a stage (BK = 16, 32 or 64 k per K-step; 64 in the convolution only):
 //   * A panel: BM rows of 4 BK bytes. The 16-byte chunk c of row r sits in slot
 //     c ^ swz_a(r), so that a wave's reads of 32 rows at one k hit distinct banks; each
 //     lane reads 4 consecutive k of its row with one 16-byte read.
@@ -48,16 +48,18 @@ struct DirectF32 {
     static_assert(B_ROW >= 256 && B_ROW <= 1024, "B rows of 64 to 256 floats");
     static_assert(NS * STAGE <= 160 * 1024, "stages must fit the 160 KB LDS");
     static_assert((NS - 2) * LOADS_NARROW_B <= 63, "vmcnt range");
-    static_assert(BK == 16 || (BK == 32 && !GEN), "BK of 32 only for the lean build");
+    static_assert(BK == 16 || ((BK == 32 || BK == 64) && !GEN), "BK of 32 or 64 only for the lean build");
 };
 
 // Rows of 64 bytes: two rows per 128 bytes of banks. Rows of 128 bytes: the 8 chunk slots
-// of any 8 (or, on 64 banks, 16) consecutive rows read at one k are distinct.
+// of any 8 (or, on 64 banks, 16) consecutive rows read at one k are distinct. Rows of 256
+// bytes (every bank): the 16 slots of any 16 consecutive rows are distinct.
 template <class T>
 __device__ __forceinline__ int swz_a(int row)
 {
     if constexpr (T::BK == 16) return ((row >> 1) ^ (row >> 3)) & 3;
-    else return ((row >> 1) & 7) ^ ((row & 1) << 2);
+    else if constexpr (T::BK == 32) return ((row >> 1) & 7) ^ ((row & 1) << 2);
+    else return row & 15;  // rows of 256 bytes: any 16 consecutive rows, 16 distinct slots
 }
 template <class T>
 __device__ __forceinline__ int swz_b(int krow) { return ((krow / (T::BK / 2)) & 1) * 8; }
