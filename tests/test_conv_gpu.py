@@ -56,6 +56,10 @@ GEOMETRIES = [
     ("7x7 stride 2 pad 3 (input-layer form)", 2, 3, 30, 30, 16, 7, 7, (2, 2), (3, 3), (1, 1)),
     ("stride larger than the filter", 2, 3, 20, 20, 5, 2, 2, (3, 3), (0, 0), (1, 1)),
     ("one output position per image", 5, 7, 3, 3, 6, 3, 3, (1, 1), (0, 0), (1, 1)),
+    # tap masks of two words: 63 taps (the most they hold; bit 63 marks rows past K), and 64
+    # taps, gathered without masks
+    ("7x9 filter, 63 taps, padded", 1, 2, 12, 12, 5, 7, 9, (1, 1), (3, 4), (1, 1)),
+    ("8x8 filter, 64 taps, padded", 1, 2, 11, 11, 3, 8, 8, (1, 1), (2, 2), (1, 1)),
     # C R S = 2160: more rows than the direct gather's LDS row table takes (2048), so the
     # tap masks run with their rows stepped in scalar registers
     ("3x3, C R S = 2160 (tap masks without the row table)", 1, 240, 6, 6, 12, 3, 3, (1, 1), (1, 1),

@@ -58,8 +58,9 @@ struct Im2colOperands {
     int Q, PQ, HW, RS, CHW;
     int sK, rK, cK;  // one K-step (BK rows) of the im2col matrix: s += sK, r += rK, c += cK (with carries)
     int64_t KPQ;
-    // the direct gather's tap-mask path (R S <= 31, a run of x below 2^31 bytes): 1 if taken,
-    // and the run's size in bytes (the bound of its buffer loads)
+    // the direct gather's tap-mask path (a run of x below 2^31 bytes): 0 if not taken, else
+    // the mask words per column (1: R S <= 31, 2: R S <= 63), and the run's size in bytes
+    // (the bound of its buffer loads)
     int tap_masks;
     unsigned run_bytes;
     // the tap-mask path's row table in LDS (K rounded up to whole K-steps, 8 bytes a row)
@@ -160,20 +161,23 @@ struct Im2colOperands {
 // workgroup and stepped across the wave's ROWS consecutive rows. An element that is zero
 // (padding, k >= K, column >= N) is read from kZeros, so a partial last K-step needs
 // no clearing. A's partial step takes 4-byte lanes with the same rule.
-// MASK: each lane also keeps, per column, a bit per filter tap (r S + s < 31) that is set
-// where the tap falls in the padding (bit 31 always set). A B element is then read by a
+// MASK (1 or 2 words): each lane also keeps, per column, a bit per filter tap r S + s that
+// is set where the tap falls in the padding; the last bit of the last word (31 or 63, above
+// every tap) is always set and stands for the rows past K. A B element is then read by a
 // buffer load of x (the run's size as the bound) at byte offset (column base + row offset)
 // * 4, or at 2^31 for a padded tap or a row past K: that offset is beyond the run (runs are
 // kept below 2^31 bytes), so the load returns 0. Three vector instructions per element
-// (shift-add, bit extract, bit select) instead of the bounds tests and a 64-bit pointer
-// select.
+// (shift-add, bit extract, bit select; one more, the word select, with two words) instead
+// of the bounds tests and a 64-bit pointer select.
 // TABLE (with MASK): the row offset and tap of every k come from a table the workgroup
 // writes into LDS before its first load, one wave-uniform LDS read per row instead of the
 // scalar stepping.
-template <class T, bool MASK, bool TABLE>
+template <class T, int MASK, bool TABLE>
 __global__ __launch_bounds__(T::NT) void conv_direct_kernel(GemmArgs p, Im2colOperands o)
 {
-    static_assert(MASK || !TABLE, "the row table feeds the tap-mask path");
+    static_assert(MASK > 0 || !TABLE, "the row table feeds the tap-mask path");
+    static_assert(MASK >= 0 && MASK <= 2, "one or two mask words");
+    constexpr int kPastK = MASK == 2 ? 63 : 31;  // the mask bit of a row past K
     static_assert(T::B_ROW <= 1024 && (T::B4 * 256) % T::B_ROW == 0, "a wave's B loads cover whole rows");
     constexpr int ROWS = T::B4 * 256 / T::B_ROW;      // k rows of a K-step one wave loads
     constexpr int PER_ROW = T::B_ROW / 256;           // loads per row
@@ -196,11 +200,11 @@ __global__ __launch_bounds__(T::NT) void conv_direct_kernel(GemmArgs p, Im2colOp
     const float *zeros = kZeros + lane;
     const char *x = reinterpret_cast<const char *>(p.B);
     // TABLE: per im2col row k, its offset in x from the column's base and its filter tap
-    // (31 past K: the tap masks' always-set bit), built once per workgroup
+    // (kPastK past K: the tap masks' always-set bit), built once per workgroup
     extern __shared__ int2 ktab[];
     if constexpr (TABLE) {
         for (int e = threadIdx.x; e < nk * T::BK; e += T::NT) {
-            int2 t = {0, 31};
+            int2 t = {0, kPastK};
             if (e < p.K) {
                 const int c = e / o.RS, rs = e - c * o.RS, r = rs / o.S, s = rs - r * o.S;
                 t.x = c * o.HW + r * o.dh * o.W + s * o.dw;
@@ -232,22 +236,35 @@ __global__ __launch_bounds__(T::NT) void conv_direct_kernel(GemmArgs p, Im2colOp
     static_assert((T::BK / 2) % ROWS == 0, "a wave's rows lie in one half of the K-step: they share swz_b");
     // the tap-mask path: per column, bit r S + s set where that tap is in the padding (or the
     // column is past N), and the column's base offset in bytes
-    unsigned pad_taps[PER_ROW], base4[PER_ROW];
+    unsigned pad_lo[PER_ROW], pad_hi[PER_ROW], base4[PER_ROW];
     __amdgpu_buffer_rsrc_t xrsrc;
-    if constexpr (MASK) {
+    if constexpr (MASK > 0) {
         xrsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(p.B), (short)0, (int)o.run_bytes, 0x00020000);
+        // tap (r, s) is in the padding when its filter row r or its filter column s is:
+        // the mask is the S bits of the padded columns, or all S bits for a padded row,
+        // at r S for each r (R + S steps rather than R S)
+        const uint64_t full_row = (uint64_t(1) << o.S) - 1;  // S <= 63
 #pragma unroll
         for (int h = 0; h < PER_ROW; ++h) {
-            unsigned m = 0x80000000u;
-            for (int r = 0, t = 0; r < o.R; ++r) {
+            uint64_t col_pad = 0;
+            for (int ss = 0; ss < o.S; ++ss)
+                if ((unsigned)(cols[h].w0 + ss * o.dw) >= (unsigned)o.W) col_pad |= uint64_t(1) << ss;
+            uint64_t m = uint64_t(1) << kPastK;
+            for (int r = 0; r < o.R; ++r) {
                 const bool hin = (unsigned)(cols[h].h0 + r * o.dh) < (unsigned)o.H;
-                for (int ss = 0; ss < o.S; ++ss, ++t)
-                    if (!hin || (unsigned)(cols[h].w0 + ss * o.dw) >= (unsigned)o.W) m |= 1u << t;
+                m |= (hin ? col_pad : full_row) << (r * o.S);
             }
-            pad_taps[h] = m;
+            pad_lo[h] = (unsigned)m;
+            pad_hi[h] = (unsigned)(m >> 32);
             base4[h] = (unsigned)cols[h].base * 4u;
         }
     }
+    // all ones where tap `bit` of column h is in the padding (or the row is past K), else 0
+    auto pad_of = [&](int h, int bit) -> unsigned {
+        unsigned word = pad_lo[h];
+        if constexpr (MASK == 2) word = bit < 32 ? pad_lo[h] : pad_hi[h];
+        return (unsigned)__builtin_amdgcn_sbfe((int)word, bit & 31, 1);
+    };
 
     const unsigned lds0 = (unsigned)(uintptr_t)(lds_char *)lds;
     // (c, r, s) of row krow0 of the next K-step to issue (one division, here)
@@ -276,7 +293,7 @@ __global__ __launch_bounds__(T::NT) void conv_direct_kernel(GemmArgs p, Im2colOp
 #pragma unroll
                 for (int h = 0; h < PER_ROW; ++h) {
                     const unsigned dst = st + T::A_BYTES + (krow0 + rr) * T::B_ROW + 256 * h;
-                    const unsigned pad = (unsigned)__builtin_amdgcn_sbfe((int)pad_taps[h], t.y, 1);
+                    const unsigned pad = pad_of(h, t.y);
                     const unsigned v = base4[h] + (unsigned)t.x * 4u;
                     const unsigned off = (pad & 0x80000000u) | (~pad & v);
                     asm volatile("s_nop 0\n\tbuffer_load_dword %0, %1, 0 offen lds"
@@ -305,10 +322,10 @@ __global__ __launch_bounds__(T::NT) void conv_direct_kernel(GemmArgs p, Im2colOp
 #pragma unroll
             for (int h = 0; h < PER_ROW; ++h) {
                 const unsigned dst = st + T::A_BYTES + (krow0 + rr) * T::B_ROW + 256 * h;
-                if constexpr (MASK) {
-                    // a padded tap or a row past K (tap 31) reads at 2^31, past the run
-                    const int bit = k < p.K ? tap : 31;
-                    const unsigned pad = (unsigned)__builtin_amdgcn_sbfe((int)pad_taps[h], bit, 1);
+                if constexpr (MASK > 0) {
+                    // a padded tap or a row past K (bit kPastK) reads at 2^31, past the run
+                    const int bit = k < p.K ? tap : kPastK;
+                    const unsigned pad = pad_of(h, bit);
                     const unsigned v = base4[h] + (unsigned)rowoff * 4u;
                     const unsigned off = (pad & 0x80000000u) | (~pad & v);
                     asm volatile("s_nop 0\n\tbuffer_load_dword %0, %1, 0 offen lds"
@@ -380,9 +397,12 @@ hipError_t launch_conv_direct(const GemmArgs &a, const Im2colOperands &o, hipStr
     GemmArgs ga = a;
     Im2colOperands oa = o;
     void *args[] = {&ga, &oa};
-    const void *fn = !o.tap_masks  ? reinterpret_cast<const void *>(&conv_direct_kernel<T, false, false>)
-                     : o.row_table ? reinterpret_cast<const void *>(&conv_direct_kernel<T, true, true>)
-                                   : reinterpret_cast<const void *>(&conv_direct_kernel<T, true, false>);
+    const void *fn = o.tap_masks == 0 ? reinterpret_cast<const void *>(&conv_direct_kernel<T, 0, false>)
+                     : o.tap_masks == 1
+                         ? (o.row_table ? reinterpret_cast<const void *>(&conv_direct_kernel<T, 1, true>)
+                                        : reinterpret_cast<const void *>(&conv_direct_kernel<T, 1, false>))
+                         : (o.row_table ? reinterpret_cast<const void *>(&conv_direct_kernel<T, 2, true>)
+                                        : reinterpret_cast<const void *>(&conv_direct_kernel<T, 2, false>));
     const size_t table = o.row_table ? (size_t)((a.K + T::BK - 1) / T::BK) * T::BK * 8 : 0;
     return hipLaunchKernel(fn, dim3(gx, gy), dim3(T::NT), args, table, stream);
 }
@@ -560,9 +580,9 @@ hipError_t conv_launch(int cfg, const ConvArgs &a, hipStream_t stream)
     o.cK = (int)(bk / (a.R * a.S));
     o.KPQ = KPQ;
     // images per launch: x offsets below 2^30, product columns below 2^31; the direct
-    // gather's tap masks need a filter of at most 31 taps and runs below 2^31 bytes
-    const bool masks = kConvConfigs[cfg].direct && a.R * a.S <= 31 && CHW <= kMaxMaskRun;
-    o.tap_masks = masks ? 1 : 0;
+    // gather's tap masks need a filter of at most 63 taps and runs below 2^31 bytes
+    const bool masks = kConvConfigs[cfg].direct && a.R * a.S <= 63 && CHW <= kMaxMaskRun;
+    o.tap_masks = masks ? (a.R * a.S <= 31 ? 1 : 2) : 0;
     o.row_table = masks && kConvConfigs[cfg].row_table && (a.C * a.R * a.S + bk - 1) / bk * bk * 8 <= kMaxRowTable;
     int64_t per = (masks ? kMaxMaskRun : kMaxRun) / CHW;
     if (kMaxI32 / PQ < per) per = kMaxI32 / PQ;
