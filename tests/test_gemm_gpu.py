@@ -433,7 +433,7 @@ def run_default(A, B, dev, a_offset=0):
 @pytest.mark.parametrize("M,N,K", SPLIT2_SHAPES)
 @pytest.mark.parametrize("a_offset", [0, 1])
 def test_two_k_halves(dev, M, N, K, a_offset):
-    assert mm.mm_gemm_f32_select(M, N, K) == 13  # the halves' tile: 64 x 64 direct
+    assert mm.mm_gemm_f32_select(M, N, K) == 14  # the halves' tile: 64 x 64 direct, two wave groups
     A = wl.random_matrix(1700 + M, M, K, "int4")
     B = wl.random_matrix(1800 + N, K, N, "int4")
     assert_exact(run_default(A, B, dev, a_offset), A, B)

@@ -176,6 +176,7 @@ template <class T, int MASK, bool TABLE>
 __global__ __launch_bounds__(T::NT) void conv_direct_kernel(GemmArgs p, Im2colOperands o)
 {
     static_assert(MASK > 0 || !TABLE, "the row table feeds the tap-mask path");
+    static_assert(T::KS == 1, "one wave group per K-step");
     static_assert(MASK >= 0 && MASK <= 2, "one or two mask words");
     constexpr int kPastK = MASK == 2 ? 63 : 31;  // the mask bit of a row past K
     static_assert(T::B_ROW <= 1024 && (T::B4 * 256) % T::B_ROW == 0, "a wave's B loads cover whole rows");
@@ -357,7 +358,7 @@ __global__ __launch_bounds__(T::NT) void conv_direct_kernel(GemmArgs p, Im2colOp
         }
     };
 
-    int a_off[T::QN][T::FM], b_off[T::QN][4][T::FN];
+    int a_off[T::QW][T::FM], b_off[T::QW][4][T::FN];
     direct_operand_offsets<T>(lane, wm0, wn0, a_off, b_off);
     f32x16 acc[T::FM][T::FN];
 #pragma unroll

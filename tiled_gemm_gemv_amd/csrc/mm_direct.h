@@ -29,13 +29,17 @@ typedef __attribute__((address_space(3))) float lds_float;
 
 // GEN: every shape (4-byte lanes where needed); otherwise K % 16 == 0 and N % 4 == 0 only
 // (direct_f32_wide_ok), which keeps the narrow-lane code out of the kernel.
-template <int BM_, int BN_, int WM_, int WN_, int NS_, bool GEN_, int BK_ = 16>
+// KS: wave groups that split each K-step's k groups (KS = 2: 8 waves on a 4-wave tile grid;
+// group g multiplies groups g QN / 2 .. of every step, and the two sums meet in LDS).
+template <int BM_, int BN_, int WM_, int WN_, int NS_, bool GEN_, int BK_ = 16, int KS_ = 1>
 struct DirectF32 {
-    static constexpr int BM = BM_, BN = BN_, BK = BK_, NS = NS_, WM = WM_, WN = WN_;
+    static constexpr int BM = BM_, BN = BN_, BK = BK_, NS = NS_, WM = WM_, WN = WN_, KS = KS_;
     static constexpr int QN = BK / 8;      // groups of 4 k per wave half and K-step
+    static constexpr int QW = QN / KS;     // ... that one wave multiplies
     static constexpr int A_ROW = BK * 4;   // bytes per A row
     static constexpr bool GEN = GEN_;
-    static constexpr int WAVES = (BM / WM) * (BN / WN), NT = WAVES * 64;
+    static constexpr int GRID = (BM / WM) * (BN / WN);  // waves of the tile's wave grid
+    static constexpr int WAVES = GRID * KS, NT = WAVES * 64;
     static constexpr int FM = WM / 32, FN = WN / 32;
     static constexpr int A_BYTES = BM * BK * 4, B_BYTES = BK * BN * 4;
     static constexpr int STAGE = A_BYTES + B_BYTES;
@@ -49,6 +53,7 @@ struct DirectF32 {
     static_assert(NS * STAGE <= 160 * 1024, "stages must fit the 160 KB LDS");
     static_assert((NS - 2) * LOADS_NARROW_B <= 63, "vmcnt range");
     static_assert(BK == 16 || ((BK == 32 || BK == 64) && !GEN), "BK of 32 or 64 only for the lean build");
+    static_assert(KS == 1 || (KS == 2 && !GEN && QN % 2 == 0), "K-step groups split in two only in the lean build");
 };
 
 // Rows of 64 bytes: two rows per 128 bytes of banks. Rows of 128 bytes: the 8 chunk slots
@@ -115,17 +120,19 @@ __device__ __forceinline__ void wait_steps(int steps)
 }
 
 // This lane's operand addresses inside a stage (bytes): A per group q and block i; B per
-// group q, step j and block jj (k = 8 (lane / 32) + 4 q + j, column wn0 + 32 jj + lane % 32).
+// group q, step j and block jj (k = (BK / 2) (lane / 32) + 4 q + j, column wn0 + 32 jj +
+// lane % 32), for this wave's QW groups q = q0 + qq.
 template <class T>
-__device__ __forceinline__ void direct_operand_offsets(int lane, int wm0, int wn0, int (&a_off)[T::QN][T::FM],
-                                                       int (&b_off)[T::QN][4][T::FN])
+__device__ __forceinline__ void direct_operand_offsets(int lane, int wm0, int wn0, int (&a_off)[T::QW][T::FM],
+                                                       int (&b_off)[T::QW][4][T::FN], int q0 = 0)
 {
 #pragma unroll
-    for (int q = 0; q < T::QN; ++q) {
+    for (int qq = 0; qq < T::QW; ++qq) {
+        const int q = q0 + qq;
 #pragma unroll
         for (int i = 0; i < T::FM; ++i) {
             const int row = wm0 + 32 * i + (lane & 31);
-            a_off[q][i] = row * T::A_ROW + 16 * ((q + T::QN * (lane >> 5)) ^ swz_a<T>(row));
+            a_off[qq][i] = row * T::A_ROW + 16 * ((q + T::QN * (lane >> 5)) ^ swz_a<T>(row));
         }
 #pragma unroll
         for (int j = 0; j < 4; ++j)
@@ -133,19 +140,19 @@ __device__ __forceinline__ void direct_operand_offsets(int lane, int wm0, int wn
             for (int jj = 0; jj < T::FN; ++jj) {
                 const int krow = (T::BK / 2) * (lane >> 5) + 4 * q + j;
                 const int col = wn0 + 32 * jj + (lane & 31);
-                b_off[q][j][jj] = T::A_BYTES + krow * T::B_ROW + 16 * ((col >> 2) ^ swz_b<T>(krow)) +
-                                  4 * (col & 3);
+                b_off[qq][j][jj] = T::A_BYTES + krow * T::B_ROW + 16 * ((col >> 2) ^ swz_b<T>(krow)) +
+                                   4 * (col & 3);
             }
     }
 }
 
-// The MFMAs of one K-step on stage st: BK / 8 groups of 4 k per lane half.
+// The MFMAs of one K-step on stage st: this wave's QW groups of 4 k per lane half.
 template <class T>
-__device__ __forceinline__ void direct_multiply(const lds_char *st, const int (&a_off)[T::QN][T::FM],
-                                                const int (&b_off)[T::QN][4][T::FN], f32x16 (&acc)[T::FM][T::FN])
+__device__ __forceinline__ void direct_multiply(const lds_char *st, const int (&a_off)[T::QW][T::FM],
+                                                const int (&b_off)[T::QW][4][T::FN], f32x16 (&acc)[T::FM][T::FN])
 {
 #pragma unroll
-    for (int q = 0; q < T::QN; ++q) {
+    for (int q = 0; q < T::QW; ++q) {
         f32x4 a[T::FM];
         float b[4][T::FN];
 #pragma unroll

@@ -53,6 +53,8 @@ const ConfigEntry kConfigs[] = {
     {"128x128x16 w64x64 direct-to-LDS 4 stages (4 waves; K % 32 == 0: K-steps of 32, 2 stages)", &direct<DirectTile::T128>, 128, 128, 4, 2, 148, 16, 5},
     {"64x64x16 w32x32 direct-to-LDS 8 stages (4 waves; K % 32 == 0: K-steps of 32, 4 stages)", &direct<DirectTile::T64S8>, 64, 64, 4, 2, 136, 16, 5.5},
     {"64x64x16 w32x32 direct-to-LDS 4 stages (4 waves; K % 32 == 0: K-steps of 32, 2 stages)", &direct<DirectTile::T64S4>, 64, 64, 4, 5, 140, 16, 5.5},
+    {"64x64x32 w32x32 direct-to-LDS 4 stages, K-step over 2 wave groups (8 waves; K % 32 != 0: config 13's kernel)",
+     &direct<DirectTile::T64K2>, 64, 64, 8, 2, 140, 16, 5.5},
 };
 constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
 
@@ -84,8 +86,10 @@ int gemm_select_config(int64_t M, int64_t N, int64_t K, int64_t batch)
     // alignment is not known here). The 256 and 128 direct tiles fill 3 stages of a big
     // tile before their first MFMA; below K = 2048 that costs more than the deeper
     // pipeline saves (measured: K = 512 and 1024 slower by 10% and 3%, K = 4096 faster
-    // by 5%).
-    static const int kTileConfigs[] = {0, 1, 2, 3, 4, 5, 10, 11, 12, 13};
+    // by 5%). 14 takes the place of 13: the same tile on 8 waves (each K-step's k split
+    // over two wave groups) where K % 32 == 0, 13's own kernel elsewhere; measured at least
+    // as fast on every swept shape (1024^3 90 -> 100 TFLOP/s, 1024 x 4096 x 4096 123 -> 134).
+    static const int kTileConfigs[] = {0, 1, 2, 3, 4, 5, 10, 11, 12, 14};
     int best = 0;
     double best_t = 0;
     for (int c : kTileConfigs) {
@@ -130,7 +134,7 @@ hipError_t gemm_launch(int cfg, const GemmArgs &a, hipStream_t stream)
 // eats the gain and such shapes are not split.
 namespace {
 
-constexpr int kSplitCfg = 13;  // 64 x 64 direct tile, 4 stages
+constexpr int kSplitCfg = 14;  // 64 x 64 direct tile, 4 stages, K-steps over two wave groups
 
 int64_t round4(int64_t n) { return (n + 3) & ~int64_t(3); }
 

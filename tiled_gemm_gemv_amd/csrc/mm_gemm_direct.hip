@@ -67,7 +67,9 @@ __global__ __launch_bounds__(T::NT) void gemm_f32_direct_kernel(GemmArgs p)
 
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave index, in a scalar register
-    const int wm0 = (w / (T::BN / T::WN)) * T::WM, wn0 = (w % (T::BN / T::WN)) * T::WN;
+    // the wave's place in the tile's wave grid, and its group of each K-step's k (KS = 2)
+    const int wg = w % T::GRID, kg = w / T::GRID;
+    const int wm0 = (wg / (T::BN / T::WN)) * T::WM, wn0 = (wg % (T::BN / T::WN)) * T::WN;
     const int nk = (p.K + T::BK - 1) / T::BK;
 
     // The 16-byte lanes of full K-steps are addressed from the tile's corner at the K-step
@@ -129,8 +131,8 @@ __global__ __launch_bounds__(T::NT) void gemm_f32_direct_kernel(GemmArgs p)
     const unsigned lds0 = (unsigned)(uintptr_t)(lds_char *)lds;  // LDS byte offset of the array
     const int nk_full = p.K / T::BK;  // full K-steps; a partial one follows if K % 16 != 0
 
-    int a_off[T::QN][T::FM], b_off[T::QN][4][T::FN];
-    direct_operand_offsets<T>(lane, wm0, wn0, a_off, b_off);
+    int a_off[T::QW][T::FM], b_off[T::QW][4][T::FN];
+    direct_operand_offsets<T>(lane, wm0, wn0, a_off, b_off, kg * T::QW);
 
     f32x16 acc[T::FM][T::FN];
 #pragma unroll
@@ -224,6 +226,29 @@ __global__ __launch_bounds__(T::NT) void gemm_f32_direct_kernel(GemmArgs p)
     if (!T::GEN || wide_b) k_loop(std::true_type{});
     else k_loop(std::false_type{});
 
+    if constexpr (T::KS == 2) {
+        // group 1's sums to LDS (lane-minor: conflict-free), group 0 adds them to its own
+        __syncthreads();  // every wave is done with the stages
+        lds_float *x = (lds_float *)lds + wg * (T::FM * T::FN * 16 * 64) + lane;
+        static_assert(T::GRID * T::FM * T::FN * 16 * 64 * 4 <= T::NS * T::STAGE, "the sums fit the ring");
+        if (kg == 1) {
+#pragma unroll
+            for (int i = 0; i < T::FM; ++i)
+#pragma unroll
+                for (int jj = 0; jj < T::FN; ++jj)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) x[((i * T::FN + jj) * 16 + r) * 64] = acc[i][jj][r];
+        }
+        __syncthreads();
+        if (kg == 1) return;  // no barrier follows
+#pragma unroll
+        for (int i = 0; i < T::FM; ++i)
+#pragma unroll
+            for (int jj = 0; jj < T::FN; ++jj)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[i][jj][r] += x[((i * T::FN + jj) * 16 + r) * 64];
+    }
+
     if constexpr (ADD) direct_store_add<T>(p, m0, nb0, n0, wm0, wn0, lane, acc);
     else direct_store<T>(p, m0, nb0, n0, wm0, wn0, lane, acc, [](int gn) { return gn; });
 }
@@ -289,12 +314,20 @@ hipError_t gemm_direct_launch(DirectTile t, const GemmArgs &a, hipStream_t strea
         return launch_lean_or_general<64, 64, 32, 32, 8>(a, stream);
     case DirectTile::T64S4:
         return launch_lean_or_general<64, 64, 32, 32, 4>(a, stream);
+    case DirectTile::T64K2:
+        // each K-step's k split over two groups of 4 waves (two waves per SIMD where a CU
+        // holds one tile); other shapes run the T64S4 kernel
+        if (direct_f32_wide_ok(a, 64) && a.K % 32 == 0)
+            return launch_direct<DirectF32<64, 64, 32, 32, 4, false, 32, 2>>(a, stream);
+        return launch_lean_or_general<64, 64, 32, 32, 4>(a, stream);
     }
     return hipErrorInvalidValue;
 }
 
 hipError_t gemm_direct64_add_launch(const GemmArgs &a, hipStream_t stream)
 {
+    if (direct_f32_wide_ok(a, 64) && a.K % 32 == 0)
+        return launch_direct<DirectF32<64, 64, 32, 32, 4, false, 32, 2>, true, true>(a, stream);
     return launch_lean_or_general<64, 64, 32, 32, 4, true>(a, stream);
 }
 

@@ -119,11 +119,12 @@ hipError_t gemm_skinny_launch(const GemmArgs &a, hipStream_t stream);
 // (hipErrorInvalidValue otherwise). T64S8 / T64S4: 64 x 64 tiles with 8 / 4 LDS stages.
 // direct_f32_wide_ok(a, bn): every B load of a tile bn wide can take 16-byte lanes
 // (K % 16 == 0, and N % 4 == 0 or N >= bn) and the lane offsets fit 32 bits.
-enum class DirectTile { T256, T128, T64S8, T64S4 };
+enum class DirectTile { T256, T128, T64S8, T64S4, T64K2 };
 bool direct_f32_wide_ok(const GemmArgs &a, int bn);
 hipError_t gemm_direct_launch(DirectTile t, const GemmArgs &a, hipStream_t stream);
-// The 64 x 64 direct tile (4 stages) with an epilogue that adds each tile into C
-// atomically; a.batch problems may share C (sc = 0).
+// The 64 x 64 direct tile (4 stages; K-steps over two wave groups where K % 32 == 0, as
+// config 14) with an epilogue that adds each tile into C atomically; a.batch problems may
+// share C (sc = 0).
 hipError_t gemm_direct64_add_launch(const GemmArgs &a, hipStream_t stream);
 
 // GEMM for C with few columns (mm_gemm_cols.hip): one wave per row, B staged in LDS;
