@@ -68,7 +68,7 @@ __global__ __launch_bounds__(T::NT) void gemm_f32_direct_kernel(GemmArgs p)
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave index, in a scalar register
     // the wave's place in the tile's wave grid, and its group of each K-step's k (KS = 2)
-    const int wg = w % T::GRID, kg = w / T::GRID;
+    const int wg = T::KS == 1 ? w : w % T::GRID, kg = T::KS == 1 ? 0 : w / T::GRID;
     const int wm0 = (wg / (T::BN / T::WN)) * T::WM, wn0 = (wg % (T::BN / T::WN)) * T::WN;
     const int nk = (p.K + T::BK - 1) / T::BK;
 
