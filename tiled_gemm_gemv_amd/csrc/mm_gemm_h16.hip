@@ -558,12 +558,11 @@ __global__ __launch_bounds__(T::NT * KG) void gemm_h16_direct_kernel(Gemm16Args 
     const lds_char *ring = (const lds_char *)lds + grp * T::NS * T::STAGE;
     auto multiply = [&](int j) {
         const lds_char *st = ring + (j % T::NS) * T::STAGE;
-#pragma unroll
-        for (int ks = 0; ks < T::KS; ++ks) {
-            u32x4 a[T::FM], b[T::FN];
+        u32x4 a[2][T::FM], b[2][T::FN];
+        auto operands = [&](int ks, int buf) {
 #pragma unroll
             for (int i = 0; i < T::FM; ++i)
-                a[i] = *(const __attribute__((address_space(3))) u32x4 *)(st + a_off[ks][i]);
+                a[buf][i] = *(const __attribute__((address_space(3))) u32x4 *)(st + a_off[ks][i]);
 #pragma unroll
             for (int jj = 0; jj < T::FN; ++jj) {
                 const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
@@ -571,12 +570,23 @@ __global__ __launch_bounds__(T::NT * KG) void gemm_h16_direct_kernel(Gemm16Args 
                 const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                     (__attribute__((address_space(3))) v4i16 *)(st + b_off[ks][1][jj]));
                 const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
-                b[jj] = u32x4{l2[0], l2[1], h2[0], h2[1]};
+                b[buf][jj] = u32x4{l2[0], l2[1], h2[0], h2[1]};
             }
+        };
+        // software-pipelined: the LDS reads of MFMA step ks + 1 go out before the MFMAs of
+        // step ks (a second register set), so their latency hides behind those MFMAs
+        // (+1-3.5% on the large shapes; the sums are those of the plain loop, in its order)
+        operands(0, 0);
+#pragma unroll
+        for (int ks = 0; ks < T::KS; ++ks) {
+            if (ks + 1 < T::KS) operands(ks + 1, (ks + 1) & 1);
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int i = 0; i < T::FM; ++i)
 #pragma unroll
-                for (int jj = 0; jj < T::FN; ++jj) acc[i][jj] = mfma16<BF16>(a[i], b[jj], acc[i][jj]);
+                for (int jj = 0; jj < T::FN; ++jj)
+                    acc[i][jj] = mfma16<BF16>(a[ks & 1][i], b[ks & 1][jj], acc[i][jj]);
+            __builtin_amdgcn_sched_barrier(0);
         }
     };
 
