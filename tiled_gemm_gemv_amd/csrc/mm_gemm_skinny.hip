@@ -46,9 +46,17 @@ __device__ __forceinline__ f32x4 load4s(const float *p, int valid)
 
 // NB: 16-column blocks of C handled (1..4); W: waves splitting K; U: chunks per wave
 // per round (all of a round's loads are issued before its MFMAs).
-template <int NB, int W, int U, bool VEC_A>
+// VEC_B (NB = 4, B's rows 16-byte aligned), on tiles whose 64 columns all lie in C:
+// the blocks' columns are interleaved, column c of block nb being column n0 + NB c + nb of
+// C, so the NB values a lane feeds the NB blocks at one MFMA step are NB consecutive floats
+// of one row of B: one 16-byte load instead of four 4-byte loads, which cost the same
+// address cycles each (4096 x 64 x 4096: 51 -> 58-60 TFLOP/s; with NB = 2 and 8-byte loads
+// 4096 x 32 x 4096 lost 8-28%). Other tiles keep the blocks side by side (column
+// n0 + 16 nb + c) and load B by the float.
+template <int NB, int W, int U, bool VEC_A, bool VEC_B>
 __global__ __launch_bounds__(W * 64) void gemm_skinny_kernel(GemmArgs p)
 {
+    static_assert(!VEC_B || NB == 4, "vector B loads of 4 floats");
     __shared__ f32x4 partial[(W > 1 ? W - 1 : 1) * NB * 64];
     // workgroup -> (row block, column block): row blocks vary fastest
     const int64_t tiles_m = (p.M + kSkinnyRows - 1) / kSkinnyRows;
@@ -72,6 +80,10 @@ __global__ __launch_bounds__(W * 64) void gemm_skinny_kernel(GemmArgs p)
     for (int nb = 0; nb < NB; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     const int nchunks = (p.K + kChunk - 1) / kChunk;
+    // every lane's NB columns inside C (wave-uniform): interleaved blocks, vector loads of B
+    const bool full_cols = VEC_B && n0 + NB * 16 <= p.N;
+    // this lane's column in block nb: col0 + nb * cstep
+    const int col0 = full_cols ? n0 + NB * c16 : n0 + c16, cstep = full_cols ? 1 : 16;
     for (int c0 = w * U; c0 < nchunks; c0 += W * U) {
         f32x4 a[U];
         float b[U][4][NB];
@@ -80,13 +92,26 @@ __global__ __launch_bounds__(W * 64) void gemm_skinny_kernel(GemmArgs p)
             const int k = (c0 + u) * kChunk + 4 * g;   // this lane's first k of the chunk
             const int valid_a = row_ok ? p.K - k : 0;  // <= 0 past the end of K
             a[u] = load4s<VEC_A>(arow + k, valid_a);
+            if (full_cols) {
 #pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                const int kk = k + s;
+                for (int s = 0; s < 4; ++s) {
+                    const int kk = k + s;
+                    // rows past K read row K - 1 and are replaced by zeros
+                    const float *src = p.B + (int64_t)min(kk, p.K - 1) * p.ldb + col0;
+                    typedef float fv __attribute__((ext_vector_type(NB)));
+                    const fv v = *reinterpret_cast<const fv *>(src);
 #pragma unroll
-                for (int nb = 0; nb < NB; ++nb) {
-                    const int col = n0 + nb * 16 + c16;
-                    b[u][s][nb] = (kk < p.K && col < p.N) ? p.B[(int64_t)kk * p.ldb + col] : 0.f;
+                    for (int nb = 0; nb < NB; ++nb) b[u][s][nb] = kk < p.K ? v[nb] : 0.f;
+                }
+            } else {
+#pragma unroll
+                for (int s = 0; s < 4; ++s) {
+                    const int kk = k + s;
+#pragma unroll
+                    for (int nb = 0; nb < NB; ++nb) {
+                        const int col = col0 + nb * cstep;
+                        b[u][s][nb] = (kk < p.K && col < p.N) ? p.B[(int64_t)kk * p.ldb + col] : 0.f;
+                    }
                 }
             }
         }
@@ -116,13 +141,13 @@ __global__ __launch_bounds__(W * 64) void gemm_skinny_kernel(GemmArgs p)
     }
 
     // Accumulator layout of v_mfma_f32_16x16x4_f32: lane l, register r holds row
-    // 4 * (l / 16) + r, column l % 16 of the 16 x 16 block.
+    // 4 * (l / 16) + r, column l % 16 of the 16 x 16 block (column col0 + nb cstep of C).
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int i = m0 + 4 * g + r;
-            const int j = n0 + nb * 16 + c16;
+            const int j = col0 + nb * cstep;
             if (i < p.M && j < p.N) p.C[(int64_t)i * p.ldc + j] = acc[nb][r];
         }
 }
@@ -133,8 +158,14 @@ hipError_t launch_nb(const GemmArgs &a, bool vec, hipStream_t stream)
     const int64_t tiles = ((a.M + kSkinnyRows - 1) / kSkinnyRows) * ((a.N + kSkinnyCols - 1) / kSkinnyCols);
     unsigned gx, gy;
     if (!grid_for(tiles, gx, gy)) return hipErrorInvalidConfiguration;
-    const void *fn = vec ? reinterpret_cast<const void *>(&gemm_skinny_kernel<NB, W, U, true>)
-                         : reinterpret_cast<const void *>(&gemm_skinny_kernel<NB, W, U, false>);
+    // B's rows (and the batch's B matrices) aligned for loads of 4 floats
+    constexpr bool kVecNb = NB == 4;
+    const bool vec_b = kVecNb && a.ldb % NB == 0 && a.sb % NB == 0 && (uintptr_t)a.B % (4 * NB) == 0;
+    const void *fn;
+    if (vec_b) fn = vec ? reinterpret_cast<const void *>(&gemm_skinny_kernel<NB, W, U, true, kVecNb>)
+                        : reinterpret_cast<const void *>(&gemm_skinny_kernel<NB, W, U, false, kVecNb>);
+    else fn = vec ? reinterpret_cast<const void *>(&gemm_skinny_kernel<NB, W, U, true, false>)
+                  : reinterpret_cast<const void *>(&gemm_skinny_kernel<NB, W, U, false, false>);
     GemmArgs arg = a;
     void *args[] = {&arg};
     return hipLaunchKernel(fn, dim3(gx, gy, (unsigned)a.batch), dim3(W * 64), args, 0, stream);
