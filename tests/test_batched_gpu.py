@@ -74,6 +74,18 @@ def test_narrow_batches(dev):
     check_batch(C.cpu().numpy(), A, B, True)
 
 
+@pytest.mark.parametrize("N,K", [(24, 512), (60, 384), (8, 256)])
+def test_narrow_lds_batches(dev, N, K):
+    """Narrow shapes that the kernel moving A into LDS in whole row segments takes (N % 4
+    == 0, K a multiple of its round): the batch index is the third grid dimension."""
+    batch, M = 4, 333
+    A = np.stack([wl.random_matrix(110 + b, M, K, "int4") for b in range(batch)])
+    B = np.stack([wl.random_matrix(115 + b, K, N, "int4") for b in range(batch)])
+    C = mm.gemm_batched(to_device(A, dev), to_device(B, dev))
+    torch.cuda.synchronize()
+    check_batch(C.cpu().numpy(), A, B, True)
+
+
 def test_large_batches_sampled_rows(dev):
     """16 problems of 1024^3: enough tiles for the 256 x 256 direct-to-LDS tile (batch on
     the third grid dimension); 8 sampled rows of every problem checked exactly."""

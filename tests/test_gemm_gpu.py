@@ -312,6 +312,32 @@ def test_fc_layer_small_batch(dev, N):
     assert_tol(gpu_gemm(A, X, dev), A, X)
 
 
+# The narrow kernel that moves A into LDS in whole row segments (config 15): one, two and
+# four column blocks (rounds of 256 k, 256 k and 128 k), ragged M (rows clamped), N below
+# the tile's width (B's chunks past N clamped), a single round; then shapes it does not
+# take (N % 4 != 0, K not a multiple of its round), which run config 8's kernel.
+NARROW_SHAPES = [(16, 4, 256), (37, 16, 512), (100, 12, 768), (33, 20, 256), (130, 32, 1024),
+                 (50, 36, 128), (255, 64, 384), (300, 60, 640), (20, 18, 256), (20, 16, 200),
+                 (70, 44, 96)]
+
+
+@pytest.mark.parametrize("M,N,K", NARROW_SHAPES)
+@pytest.mark.parametrize("offsets", [(0, 0), (1, 2)])
+def test_narrow_lds_kernel(dev, M, N, K, offsets):
+    """Config 15 on strided views with NaN in every gap and starts that are only 4-byte
+    aligned: exact on integers, within tolerance on random inputs, nothing written outside C."""
+    for dist, check in (("int4", assert_exact), ("u11", assert_tol)):
+        A = wl.random_matrix(61 + M, M, K, dist)
+        B = wl.random_matrix(62 + N, K, N, dist)
+        _, Av = strided_on_device(A, K + 3, dev, offset=offsets[0])
+        _, Bv = strided_on_device(B, N + 5, dev, offset=offsets[1])
+        Cbuf, Cv = nan_output(M, N, N + 7, dev)
+        mm.gemm(Av, Bv, out=Cv, config=15)
+        torch.cuda.synchronize()
+        check(Cv.cpu().numpy(), A, B)
+        assert outside_untouched(Cbuf, M, N)
+
+
 def test_small_batch_columns_equal_gemv(dev):
     """Each column of A X equals the GEMV A x_j, exactly on integers."""
     A = wl.random_matrix(95, 1000, 777, "int4")

@@ -15,7 +15,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libmm.so")
 SOURCES = ["mm_api.hip", "mm_gemm.hip", "mm_gemm_direct.hip", "mm_gemm_skinny.hip", "mm_gemm_cols.hip",
-           "mm_gemm_h16.hip",
+           "mm_gemm_h16.hip", "mm_gemm_narrow.hip",
            "mm_conv.hip",
            "mm_gemv.hip", "mm_gemv_t.hip", "mm_static_ws.hip"]
 ARCH = "gfx950"

@@ -55,6 +55,8 @@ const ConfigEntry kConfigs[] = {
     {"64x64x16 w32x32 direct-to-LDS 4 stages (4 waves; K % 32 == 0: K-steps of 32, 2 stages)", &direct<DirectTile::T64S4>, 64, 64, 4, 5, 140, 16, 5.5},
     {"64x64x32 w32x32 direct-to-LDS 4 stages, K-step over 2 wave groups (8 waves; K % 32 != 0: config 13's kernel)",
      &direct<DirectTile::T64K2>, 64, 64, 8, 2, 140, 16, 5.5},
+    {"narrow 16x64 (16x16x4 MFMA), A and B moved into LDS in whole row segments (N % 4 == 0, K a multiple of 256 or 128; else config 8's kernel)",
+     &gemm_narrow_launch, 16, 64, 16, 1, 0, 16},
 };
 constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
 
@@ -80,7 +82,9 @@ const char *gemm_config_name(int cfg)
 int gemm_select_config(int64_t M, int64_t N, int64_t K, int64_t batch)
 {
     if (N <= 4) return 9;   // a GEMV with a few vectors (mm_gemm_cols.hip)
-    if (N <= 64) return 8;  // a few columns: stream A once (mm_gemm_skinny.hip)
+    // a few columns: stream A once, moved into LDS in whole row segments where the shape
+    // allows (mm_gemm_narrow.hip), else in 16-row pieces (mm_gemm_skinny.hip)
+    if (N <= 64) return 15;
     if (batch * tiles_for(4, M, N) < 128) return 6;  // few 64 x 64 tiles: 16-row tiles fill more CUs
     // the macro-tile configs (10 runs 0's kernel on shapes its 16-byte DMA does not take;
     // alignment is not known here). The 256 and 128 direct tiles fill 3 stages of a big

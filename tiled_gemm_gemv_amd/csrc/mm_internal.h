@@ -113,6 +113,11 @@ hipError_t gemm_split2_launch(const GemmArgs &a, hipStream_t stream);
 // any shape.
 template <int W, int L>
 hipError_t gemm_skinny_launch(const GemmArgs &a, hipStream_t stream);
+// Narrow C with A moved into LDS in whole row segments (mm_gemm_narrow.hip): true where it
+// takes the shape (N <= 64, N % 4 == 0, K a multiple of its round), and the launch (other
+// shapes run config 8's 16-row kernel).
+bool gemm_narrow_ok(const GemmArgs &a);
+hipError_t gemm_narrow_launch(const GemmArgs &a, hipStream_t stream);
 
 // fp32 GEMM with panels loaded straight into LDS (mm_gemm_direct.hip); any shape and
 // alignment, except T256, which takes only shapes direct_f32_wide_ok(a, 256) accepts
