@@ -20,12 +20,14 @@ CPU oracle (64+ sampled GEMM rows in full, every GEMV output) and the oracle's
 own time on a bounded sample of the same work is reported as `cpu_baseline`.
 
 Profiling helpers (same script, for rocprofv3 runs): --only gemm | gemv | copy | h16 |
-conv | split | gemm1024 | ragged | gemvt runs just that kernel `--steps` times with no oracle;
+conv | split | gemm1024 | ragged | gemvt | narrow runs just that kernel `--steps` times with no oracle;
 `copy` is a plain device-to-device copy of known size used to calibrate HBM counters;
 `h16` is the bf16-input GEMM at the projection shape; `conv` the 3x3 convolution layer
 (N=32, C=K=128, 28x28); `split` the FC layer on a batch of 128 through both K splits;
 `gemm1024` and `ragged` the fp32 GEMM at 1024^3 and 1000 x 1531 x 777; `gemvt` the
-transposed GEMV with a workspace (row blocks, then the sum) on the GEMV workload's matrices.
+transposed GEMV with a workspace (row blocks, then the sum) on the GEMV workload's matrices;
+`narrow` the FC layer on a batch of 64 (4096 x 64 x 4096) through mm_gemm_f32, A rotating
+over 8 matrices.
 
 Sweeps (tables, not the benchmark line): --sweep conv times every convolution tile
 configuration on the layer workloads; --sweep gemm times every GEMM tile
@@ -226,7 +228,7 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="target length of the oracle's timed sample")
     ap.add_argument("--only", choices=["gemm", "gemv", "copy", "h16", "conv", "split", "gemm1024", "ragged",
-                                           "gemvt"],
+                                           "gemvt", "narrow"],
                     default=None,
                     help="profiling helper: launch only this kernel --steps times")
     ap.add_argument("--clock-seconds", type=float, default=None,
@@ -303,6 +305,20 @@ def main():
             mm.mm_gemm_f32_ws(SM, SN, SK, A, SK, B, SN, C, SN, ws, ws.numel(), stream)
         torch.cuda.synchronize()
         log(f"split: {args.steps} mm_gemm_f32 and {args.steps} mm_gemm_f32_ws calls at {SM}x{SN}x{SK}")
+        return
+
+    if args.only == "narrow":
+        # the fully-connected layer on a batch of 64 (4096 x 64 x 4096) through mm_gemm_f32
+        # (narrow C), A rotating over 8 matrices so that every call reads its A from HBM
+        SM, SN, SK = 4096, 64, 4096
+        As = [torch.randn(SM, SK, device=dev) for _ in range(GEMV_SETS)]
+        B = torch.randn(SK, SN, device=dev) / 64.0
+        C = torch.empty((SM, SN), dtype=torch.float32, device=dev)
+        for i in range(args.steps):
+            mm.mm_gemm_f32(SM, SN, SK, As[i % GEMV_SETS], SK, B, SN, C, SN, stream)
+        torch.cuda.synchronize()
+        log(f"narrow: {args.steps} mm_gemm_f32 calls at {SM}x{SN}x{SK}, config "
+            f"{mm.mm_gemm_f32_config_name(mm.mm_gemm_f32_select(SM, SN, SK))}")
         return
 
     if args.only in ("gemm1024", "ragged"):
