@@ -704,9 +704,10 @@ def sweep(kind, torch, mm, dev):
         for c in range(nc):
             print(f"#   cfg {c}: {mm.mm_gemm_f32_config_name(c)}")
         print("#   * = the configuration mm_gemm_f32 selects for the shape; default = mm_gemm_f32 itself "
-              "(differs from the starred column where it runs K as two halves)")
+              "(differs from the starred column where it runs K as two halves); cold (FC layer rows "
+              "only) = mm_gemm_f32 with A rotating over 8 copies, so that each call reads A from HBM")
         print(f"{'M':>6s} {'N':>6s} {'K':>6s}  " + " ".join(f"{'cfg' + str(c):>8s}" for c in range(nc))
-              + f" {'default':>8s}  workload")
+              + f" {'default':>8s} {'cold':>8s}  workload")
         for M, N, K, name in shapes:
             A = torch.randn(M, K, device=dev)
             B = torch.randn(K, N, device=dev)
@@ -724,6 +725,17 @@ def sweep(kind, torch, mm, dev):
             def default(i, st):
                 mm.mm_gemm_f32(M, N, K, A, K, B, N, C, N, st)
             cells.append(f"{flop / median_graph_ms(torch, default, reps) / 1e9:8.1f}")
+            if N <= 64 and M * K * 4 >= 32 << 20:
+                # the FC layer with A read from HBM: calls rotate over 8 copies of A (more
+                # than the 256 MB Infinity Cache)
+                As = [A] + [torch.randn(M, K, device=dev) for _ in range(GEMV_SETS - 1)]
+
+                def cold(i, st):
+                    mm.mm_gemm_f32(M, N, K, As[i % GEMV_SETS], K, B, N, C, N, st)
+                cells.append(f"{flop / median_graph_ms(torch, cold, 64) / 1e9:8.1f}")
+                del As
+            else:
+                cells.append(f"{'':8s}")
             print(f"{M:6d} {N:6d} {K:6d}  " + " ".join(cells) + f"  {name}", flush=True)
             del A, B, C
         print("# strided batched GEMM (one mm_gemm_f32_batched launch) vs the same problems as "
