@@ -20,14 +20,14 @@ CPU oracle (64+ sampled GEMM rows in full, every GEMV output) and the oracle's
 own time on a bounded sample of the same work is reported as `cpu_baseline`.
 
 Profiling helpers (same script, for rocprofv3 runs): --only gemm | gemv | copy | h16 |
-conv | split | gemm1024 | ragged | gemvt | narrow runs just that kernel `--steps` times with no oracle;
+conv | split | gemm1024 | ragged | gemvt | narrow | h16_1024 runs just that kernel `--steps` times with no oracle;
 `copy` is a plain device-to-device copy of known size used to calibrate HBM counters;
 `h16` is the bf16-input GEMM at the projection shape; `conv` the 3x3 convolution layer
 (N=32, C=K=128, 28x28); `split` the FC layer on a batch of 128 through both K splits;
 `gemm1024` and `ragged` the fp32 GEMM at 1024^3 and 1000 x 1531 x 777; `gemvt` the
 transposed GEMV with a workspace (row blocks, then the sum) on the GEMV workload's matrices;
 `narrow` the FC layer on a batch of 64 (4096 x 64 x 4096) through mm_gemm_f32, A rotating
-over 8 matrices.
+over 8 matrices; `h16_1024` the bf16-input GEMM at 1024^3.
 
 Sweeps (tables, not the benchmark line): --sweep conv times every convolution tile
 configuration on the layer workloads; --sweep gemm times every GEMM tile
@@ -228,7 +228,7 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="target length of the oracle's timed sample")
     ap.add_argument("--only", choices=["gemm", "gemv", "copy", "h16", "conv", "split", "gemm1024", "ragged",
-                                           "gemvt", "narrow"],
+                                           "gemvt", "narrow", "h16_1024"],
                     default=None,
                     help="profiling helper: launch only this kernel --steps times")
     ap.add_argument("--clock-seconds", type=float, default=None,
@@ -289,6 +289,20 @@ def main():
             c = clock.summary(None, rl.MI355X_16BIT_MFMA_PEAK / 1e12)  # no rate timed here
             clock.close()
             log(f"h16 clock: {json.dumps(c)}")
+        return
+
+    if args.only == "h16_1024":
+        # bf16 inputs at 1024^3 (A ~ U[-1, 1), B ~ U[-1, 1)), in the configuration
+        # mm_gemm_bf16 chooses
+        S = 1024
+        A16 = (torch.rand(S, S, device=dev) * 2 - 1).to(torch.bfloat16)
+        B16 = (torch.rand(S, S, device=dev) * 2 - 1).to(torch.bfloat16)
+        C = torch.empty((S, S), dtype=torch.float32, device=dev)
+        for _ in range(args.steps):
+            mm.mm_gemm_bf16(S, S, S, A16, S, B16, S, C, S, stream)
+        torch.cuda.synchronize()
+        log(f"h16_1024: {args.steps} bf16 launches at {S}^3, config "
+            f"{mm.mm_gemm_h16_config_name(mm.mm_gemm_h16_select(S, S, S))}")
         return
 
     if args.only == "split":
