@@ -565,7 +565,7 @@ __global__ __launch_bounds__(T::NT * KG) void gemm_h16_direct_kernel(Gemm16Args 
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
     const lds_char *ring = (const lds_char *)lds + grp * T::NS * T::STAGE;
-    auto multiply = [&](int j) {
+    auto multiply = [&](int j, auto &&between) {
         const lds_char *st = ring + (j % T::NS) * T::STAGE;
         u32x4 a[2][T::FM], b[2][T::FN];
         auto operands = [&](int ks, int buf) {
@@ -586,6 +586,7 @@ __global__ __launch_bounds__(T::NT * KG) void gemm_h16_direct_kernel(Gemm16Args 
         // step ks (a second register set), so their latency hides behind those MFMAs
         // (+1-3.5% on the large shapes; the sums are those of the plain loop, in its order)
         operands(0, 0);
+        between();
 #pragma unroll
         for (int ks = 0; ks < T::KS; ++ks) {
             if (ks + 1 < T::KS) operands(ks + 1, (ks + 1) & 1);
@@ -623,12 +624,25 @@ __global__ __launch_bounds__(T::NT * KG) void gemm_h16_direct_kernel(Gemm16Args 
         }
         __syncthreads();
     }
-    if (my_steps > 0) multiply(0);
+    if (my_steps > 0) multiply(0, [] {});
     for (int j = 1; j < nj; ++j) {
         wait_later<LOADS, T::NS - 2>(my_steps - 1 - j);
         __syncthreads();
-        if (j + T::NS - 1 < my_steps) issue(j + T::NS - 1);
-        if (KG == 1 || j < my_steps) multiply(j);
+        auto next = [&] {
+            if (j + T::NS - 1 < my_steps) issue(j + T::NS - 1);
+        };
+        if constexpr (KG == 1) {
+            // the first MFMA step's operand reads go out before the next step's DMA loads, so
+            // that their latency passes while those loads issue: after the barrier every wave
+            // of a SIMD would otherwise issue its loads and then wait on its first reads with
+            // the matrix core idle (same bits; measured +2-8% on the 256 x 256 tile at the
+            // large shapes, +5% on the 64 x 64 tile at 1024^3; with two wave groups, whose
+            // barrier is shared by twice the waves, 4-13% slower, so they keep the old order)
+            multiply(j, next);
+        } else {
+            next();
+            if (j < my_steps) multiply(j, [] {});
+        }
     }
 
     if constexpr (KG == 2) {
