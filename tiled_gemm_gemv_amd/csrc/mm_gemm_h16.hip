@@ -371,6 +371,8 @@ hipError_t launch16(const Gemm16Args &a, hipStream_t stream)
 //   * One barrier per K-step, after an explicit wait for the step's loads (vmcnt
 //     counts the loads of the steps issued after it). The loads are issued from inline
 //     asm so that the compiler does not add a wait for all of them before every LDS read.
+//     With one wave group, the step's first operand reads go out right after the barrier
+//     and the next step's loads after them.
 //   * Any alignment: a lane's 16 bytes are read from wherever its 8 elements start (rows
 //     of odd length put half the rows at 2-byte alignment; the device's unaligned access
 //     mode serves such loads, into LDS as into registers), so neither the leading
@@ -382,9 +384,9 @@ hipError_t launch16(const Gemm16Args &a, hipStream_t stream)
 //         belong to the tile before and are not stored again, so each C element is
 //         written once. With N < BN (one tile column) N must be a multiple of 8 and
 //         chunks past N are clamped to the last one (they feed only unstored columns);
-//       - K % BK != 0: after the whole K-steps, one more step loads k in [K - BK, K). Its
-//         first BK - K % BK k overlap the step before: once its loads have landed, the
-//         workgroup writes zeros over those k in both panels (between two barriers), so
+//       - K % BK != 0: one more step, run first, loads k in [K - BK, K). Its first
+//         BK - K % BK k overlap the whole steps that follow: once its loads have landed,
+//         the workgroup writes zeros over those k in both panels (between two barriers), so
 //         they add 0 * 0 (also where A or B holds an infinity or a NaN).
 //     These need K >= BK and offsets from a tile's corner that fit 32 bits (direct_ok).
 template <int BM_, int BN_, int WM_, int WN_, int BK_, int NS_>
