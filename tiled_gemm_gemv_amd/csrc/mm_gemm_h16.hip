@@ -739,6 +739,13 @@ using D16L = Direct16<256, 256, 128, 64, 32, 4>;
 using D16L64 = Direct16<256, 256, 64, 64, 64, 2>;
 using D16M = Direct16<128, 128, 64, 64, 32, 4>;
 using D16M64 = Direct16<128, 128, 64, 64, 64, 2>;
+// 8 waves of 64 x 32 in one group, four stages: two waves per SIMD without splitting the
+// K-steps (the two-group tile, config 10, shares each barrier between groups that cannot
+// read early). Against config 10, same process: 2048^3 730 against 708 TFLOP/s,
+// 4096 x 1024 x 4096 851 against 852 (fp16 831 against 802), 1000 x 4000 x 3000 716 against
+// 660; against the 64 x 64 tile at 1536^3 481 against 466. With 2 stages 659 at 2048^3.
+using D16M64w8 = Direct16<128, 128, 64, 32, 64, 4>;
+using D16M32w8 = Direct16<128, 128, 64, 32, 32, 8>;
 using D16S = Direct16<64, 64, 32, 32, 32, 4>;
 using D16S64 = Direct16<64, 64, 32, 32, 64, 2>;
 // deeper rings for the smaller tiles
@@ -782,6 +789,8 @@ const Config16 kConfigs16[] = {
      &direct16<D16S32s8, D16S64s4, T16Sp2>},
     {"128x128x64 w64x64 direct-to-LDS 2 stages, K over 2 wave groups (8 waves; K < 64: K-steps of 32, 4 stages)",
      &direct16<D16M, D16M64, T16Mp2, 2>},
+    {"128x128x64 w64x32 direct-to-LDS 4 stages (8 waves; K < 64: K-steps of 32, 8 stages)",
+     &direct16<D16M32w8, D16M64w8, T16Mp2>},
 };
 constexpr int kNumConfigs16 = sizeof(kConfigs16) / sizeof(kConfigs16[0]);
 
@@ -797,20 +806,19 @@ const char *gemm16_config_name(int cfg)
 int gemm16_select_config(int64_t M, int64_t N, int64_t K)
 {
     (void)K;
-    // The direct pipelines (5 .. 10); on shapes they cannot take they run the register-
+    // The direct pipelines (5 .. 11); on shapes they cannot take they run the register-
     // staged tile of their size. From the timed sweep of every config (bf16 and fp16,
     // 128^3 .. 8192^3, the projection and ragged shapes): the 256 x 256 tile from 144 tiles
-    // on (3072^3: 788 TFLOP/s against 739 on 128 x 128); with fewer, the 128 x 128 tile in
-    // two wave groups from 200 tiles of 128^2 on (2048^3: 725 against 609 in one group,
-    // 4096 x 1024 x 4096: 847 against 708); below that the 64 x 64 tile, four stages deep
-    // where at most two workgroups per CU are needed (1024^3: 316; 1000 x 1531 x 777: 208
-    // against 191 with two stages), else two stages, which fit three workgroups per CU
-    // (1536^3, 576 tiles: 458 against 412).
+    // on (3072^3: 788 TFLOP/s against 718 on 128 x 128); with fewer, the 128 x 128 tile on 8
+    // waves of 64 x 32 from 144 tiles of 128^2 on (2048^3: 730; 4096 x 1024 x 4096: 851;
+    // 1536^3: 481 against 466 on 64 x 64); below that the 64 x 64 tile, four stages deep
+    // where at most two workgroups per CU are needed (1024^3: 334; 1000 x 1531 x 777: 208
+    // against 193 with two stages), else two stages, which fit three workgroups per CU.
     const int64_t t256 = ((M + 255) / 256) * ((N + 255) / 256);
     const int64_t t128 = ((M + 127) / 128) * ((N + 127) / 128);
     const int64_t t64 = ((M + 63) / 64) * ((N + 63) / 64);
     if (t256 >= 144) return 5;
-    if (t128 >= 200) return 10;
+    if (t128 >= 144) return 11;
     return t64 > 512 ? 7 : 9;
 }
 
