@@ -90,10 +90,11 @@ int gemm_select_config(int64_t M, int64_t N, int64_t K, int64_t batch)
     // alignment is not known here). The 256 and 128 direct tiles fill 3 stages of a big
     // tile before their first MFMA; below K = 2048 that costs more than the deeper
     // pipeline saves (measured: K = 512 and 1024 slower by 10% and 3%, K = 4096 faster
-    // by 5%). 14 takes the place of 13: the same tile on 8 waves (each K-step's k split
-    // over two wave groups) where K % 32 == 0, 13's own kernel elsewhere; measured at least
-    // as fast on every swept shape (1024^3 90 -> 100 TFLOP/s, 1024 x 4096 x 4096 123 -> 134).
-    static const int kTileConfigs[] = {0, 1, 2, 3, 4, 5, 10, 11, 12, 14};
+    // by 5%). 14 is 13's tile on 8 waves (each K-step's k split over two wave groups) where
+    // K % 32 == 0: the model rates it above 13 where a CU holds one tile (1024^3: 99 against
+    // 97 TFLOP/s), and the two tie where it holds several, which 13 (listed first) takes
+    // (1536^3: 100 against 92, 3072^3: 138 against 133, 8192 x 1792 x 4096: 141 against 136).
+    static const int kTileConfigs[] = {0, 1, 2, 3, 4, 5, 10, 11, 12, 13, 14};
     int best = 0;
     double best_t = 0;
     for (int c : kTileConfigs) {
