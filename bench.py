@@ -20,10 +20,10 @@ CPU oracle (64+ sampled GEMM rows in full, every GEMV output) and the oracle's
 own time on a bounded sample of the same work is reported as `cpu_baseline`.
 
 Profiling helpers (same script, for rocprofv3 runs): --only gemm | gemv | copy | h16 |
-conv | split | gemm1024 | ragged | gemvt | narrow | h16_1024 runs just that kernel `--steps` times with no oracle;
+conv | conv7x7 | split | gemm1024 | ragged | gemvt | narrow | h16_1024 runs just that kernel `--steps` times with no oracle;
 `copy` is a plain device-to-device copy of known size used to calibrate HBM counters;
 `h16` is the bf16-input GEMM at the projection shape; `conv` the 3x3 convolution layer
-(N=32, C=K=128, 28x28); `split` the FC layer on a batch of 128 through both K splits;
+(N=32, C=K=128, 28x28), `conv7x7` the 7x7 stride-2 first layer (N=32, C=3, 224x224, K=64); `split` the FC layer on a batch of 128 through both K splits;
 `gemm1024` and `ragged` the fp32 GEMM at 1024^3 and 1000 x 1531 x 777; `gemvt` the
 transposed GEMV with a workspace (row blocks, then the sum) on the GEMV workload's matrices;
 `narrow` the FC layer on a batch of 64 (4096 x 64 x 4096) through mm_gemm_f32, A rotating
@@ -228,7 +228,7 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="target length of the oracle's timed sample")
     ap.add_argument("--only", choices=["gemm", "gemv", "copy", "h16", "conv", "split", "gemm1024", "ragged",
-                                           "gemvt", "narrow", "h16_1024"],
+                                           "gemvt", "narrow", "h16_1024", "conv7x7"],
                     default=None,
                     help="profiling helper: launch only this kernel --steps times")
     ap.add_argument("--clock-seconds", type=float, default=None,
@@ -349,9 +349,10 @@ def main():
             f"{mm.mm_gemm_f32_config_name(mm.mm_gemm_f32_select(w.M, w.N, w.K))}")
         return
 
-    if args.only == "conv":
-        # the 3x3 middle layer, in the configuration mm_conv2d_f32 chooses
-        cw = wl.CONV_WORKLOADS["conv3x3"]
+    if args.only in ("conv", "conv7x7"):
+        # the 3x3 middle layer (or the 7x7 stride-2 first layer), in the configuration
+        # mm_conv2d_f32 chooses
+        cw = wl.CONV_WORKLOADS["conv3x3" if args.only == "conv" else "conv7x7_s2"]
         x, f, y = conv_tensors(torch, cw, dev)
         for _ in range(args.steps):
             launch_conv(mm, cw, x, f, y, stream)

@@ -181,6 +181,18 @@ __device__ __forceinline__ void direct_store(const GemmArgs &p, int m0, int nb0,
                                              int lane, const f32x16 (&acc)[T::FM][T::FN], ColOff col_off)
 {
     const int col_l = lane & 31, row_l = 4 * (lane >> 5);
+    // a lane's column in each 32-column block, and its offset in C, once per block: inside
+    // the guarded stores the compiler would evaluate col_off per element (for the
+    // convolution's NKPQ scatter a division each: 16 per block, which on a filter of
+    // 147 taps outweighed the tile's MFMAs)
+    int64_t coff[T::FN];
+    bool cok[T::FN];
+#pragma unroll
+    for (int jj = 0; jj < T::FN; ++jj) {
+        const int gn = nb0 + wn0 + jj * 32 + col_l;
+        cok[jj] = gn < p.N && gn >= n_first;
+        coff[jj] = cok[jj] ? col_off(gn) : 0;
+    }
 #pragma unroll
     for (int i = 0; i < T::FM; ++i)
 #pragma unroll
@@ -188,8 +200,7 @@ __device__ __forceinline__ void direct_store(const GemmArgs &p, int m0, int nb0,
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int gm = m0 + wm0 + i * 32 + 8 * (r >> 2) + row_l + (r & 3);
-                const int gn = nb0 + wn0 + jj * 32 + col_l;
-                if (gm < p.M && gn < p.N && gn >= n_first) p.C[(int64_t)gm * p.ldc + col_off(gn)] = acc[i][jj][r];
+                if (gm < p.M && cok[jj]) p.C[(int64_t)gm * p.ldc + coff[jj]] = acc[i][jj][r];
             }
 }
 
