@@ -150,7 +150,7 @@ __global__ __launch_bounds__(T::NT) void gemm_narrow_kernel(GemmArgs p)
     }
     __syncthreads();
     if (w > 0) return;  // no barrier follows
-#pragma unroll 1
+#pragma unroll  // all reads first, then the adds in wave order
     for (int v = 1; v < T::W; ++v)
 #pragma unroll
         for (int nb = 0; nb < T::NB; ++nb) acc[nb] += part[((v - 1) * T::NB + nb) * 64 + lane];
