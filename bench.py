@@ -917,7 +917,7 @@ def sweep(kind, torch, mm, dev):
               f"{tr * 1e3:.2f} us, {rb / tr / 1e6:.0f} GB/s ({100 * rb / (tr * 1e-3) / rl.MI355X_HBM_PEAK:.1f}% of 8 TB/s)",
               flush=True)
         del As, ys
-        print("# transposed GEMV y = A^T x, same timing, cold: mm_gemv_t_f32 (16-column strips) and "
+        print("# transposed GEMV y = A^T x, same timing, cold: mm_gemv_t_f32 (column strips: 16 columns for N <= 6144, 32 for N <= 12288, else 64) and "
               "mm_gemv_t_f32_ws (row blocks, partial sums in a workspace, two launches)")
         for TM, TN in ((4096, 4096), (8192, 8192), (16384, 4096), (4096, 16384)):
             sets = max(2, min(16, (512 << 20) // (TM * TN * 4)))

@@ -5,16 +5,16 @@
 // ML-inference tutorial, "Matrix-Vector Multiplication") applied to the transpose:
 // each output is a column of A dotted with x. Reading A column-wise would stride
 // by a whole row per element, so the kernel still streams A along its rows and
-// gives each workgroup a strip of 16 columns over all M rows:
-//   * a wave reads 16 rows x 64 bytes per instruction (lane l: row l / 4 of the
-//     group, 4 columns at 4 * (l % 4)), 16-byte loads, up to 16 instructions in
-//     flight; the 4 waves take interleaved groups of 16 rows;
-//   * each lane keeps 4 column sums; at the end the 16 lanes that share columns
-//     are combined with a butterfly, then the 4 waves in LDS in wave order, so the
+// gives each workgroup a strip of STRIP columns (16, 32 or 64, chosen so that the N /
+// STRIP strips give about one workgroup per CU) over all M rows:
+//   * a wave reads 64 / (STRIP / 4) rows x 4 STRIP bytes per instruction (lane l: row
+//     l / (STRIP / 4) of the group, 4 columns at 4 (l % (STRIP / 4))), 16-byte loads, up
+//     to 16 instructions in flight; the waves take interleaved groups of rows;
+//   * each lane keeps 4 column sums; at the end the lanes that share columns are
+//     combined with a butterfly, then the waves in LDS in wave order, so the
 //     summation order is fixed and results are deterministic;
-//   * N / 16 strips give one workgroup per CU at N = 4096; consecutive strips go
-//     to the same XCD (the launch order is renumbered as in the GEMM), so the two
-//     halves of a 128-byte line are read through one L2.
+//   * consecutive strips go to the same XCD (the launch order is renumbered as in the
+//     GEMM), so neighbouring pieces of a 128-byte line are read through one L2.
 // Rows that are not 16-byte aligned (N % 4 != 0 or an unaligned A) use 4-byte loads.
 //
 // With a workspace (gemv_t_ws_launch) the rows are read as the GEMV reads them: a
@@ -35,7 +35,6 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kStrip = 16;        // columns per workgroup
 constexpr int kWaves = 4;         // waves per workgroup
-constexpr int kRowsPerLoad = 16;  // rows one wave instruction covers
 constexpr int kDepth = 16;        // row groups in flight per wave
 
 __device__ __forceinline__ int strip_of_block(int bid, int nblocks)
@@ -45,28 +44,30 @@ __device__ __forceinline__ int strip_of_block(int bid, int nblocks)
     return (xcd < r) ? xcd * (q + 1) + slot : r * (q + 1) + (xcd - r) * q + slot;
 }
 
-template <bool VEC>
-__global__ __launch_bounds__(kWaves * 64) void gemv_t_kernel(GemvArgs p)
+template <bool VEC, int STRIP = kStrip, int WAVES = kWaves>
+__global__ __launch_bounds__(WAVES * 64) void gemv_t_kernel(GemvArgs p)
 {
-    __shared__ f32x4 partial[(kWaves - 1) * 64];
-    const int64_t strips = ((int64_t)p.N + kStrip - 1) / kStrip;
+    constexpr int LPR = STRIP / 4;          // lanes per row (4 columns each)
+    constexpr int RPL = 64 / LPR;           // rows per wave instruction
+    __shared__ f32x4 partial[(WAVES - 1) * 64];
+    const int64_t strips = ((int64_t)p.N + STRIP - 1) / STRIP;
     const int64_t bid = linear_block();
     if (bid >= strips) return;  // padding of a 2-D grid (whole workgroup, before any barrier)
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int strip = strip_of_block((int)bid, (int)strips);
-    const int j0 = strip * kStrip + 4 * (lane & 3);   // this lane's first column
-    const int rsub = lane >> 2;                         // row within a 16-row group
-    const int ncols = p.N - j0;                         // columns left from j0 (may be <= 0)
+    const int j0 = strip * STRIP + 4 * (lane % LPR);   // this lane's first column
+    const int rsub = lane / LPR;                         // row within a group of RPL rows
+    const int ncols = p.N - j0;                          // columns left from j0 (may be <= 0)
 
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    // row groups g = w, w + 4, w + 8, ...; a round takes kDepth of them
-    const int groups = (p.M + kRowsPerLoad - 1) / kRowsPerLoad;
-    for (int g0 = w; g0 < groups; g0 += kWaves * kDepth) {
+    // row groups g = w, w + WAVES, ...; a round takes kDepth of them
+    const int groups = (p.M + RPL - 1) / RPL;
+    for (int g0 = w; g0 < groups; g0 += WAVES * kDepth) {
         f32x4 va[kDepth];
         float vx[kDepth];
 #pragma unroll
         for (int d = 0; d < kDepth; ++d) {
-            const int i = (g0 + d * kWaves) * kRowsPerLoad + rsub;
+            const int i = (g0 + d * WAVES) * RPL + rsub;
             const bool row_ok = i < p.M;
             const float *src = p.A + (int64_t)(row_ok ? i : 0) * p.N + j0;
             f32x4 v = {0.f, 0.f, 0.f, 0.f};
@@ -92,16 +93,16 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_t_kernel(GemvArgs p)
             acc[3] += va[d][3] * vx[d];
         }
     }
-    // lanes l, l ^ 4, l ^ 8, ... (same l % 4) hold the same 4 columns
+    // lanes l, l ^ LPR, l ^ 2 LPR, ... (same l % LPR) hold the same 4 columns
 #pragma unroll
-    for (int off = 4; off < 64; off <<= 1)
+    for (int off = LPR; off < 64; off <<= 1)
 #pragma unroll
         for (int c = 0; c < 4; ++c) acc[c] += __shfl_xor(acc[c], off, 64);
-    if (w > 0 && lane < 4) partial[(w - 1) * 64 + lane] = acc;
+    if (w > 0 && lane < LPR) partial[(w - 1) * 64 + lane] = acc;
     __syncthreads();
-    if (w > 0 || lane >= 4) return;  // no barrier follows
+    if (w > 0 || lane >= LPR) return;  // no barrier follows
 #pragma unroll 1
-    for (int v = 1; v < kWaves; ++v) acc += partial[(v - 1) * 64 + lane];
+    for (int v = 1; v < WAVES; ++v) acc += partial[(v - 1) * 64 + lane];
 #pragma unroll
     for (int c = 0; c < 4; ++c)
         if (c < ncols) p.y[j0 + c] = acc[c];
@@ -224,17 +225,26 @@ hipError_t gemv_t_ws_launch(const GemvArgs &a, float *ws, hipStream_t stream)
                            stream);
 }
 
+// Strip width by N: about one workgroup per CU. With N / 16 strips far above 256 the
+// 64-byte row pieces of 16-column strips cost (8192 x 8192: 75.4 us against 53.8 with
+// 32 columns; 4096 x 16384: 76.9 against 46.6 with 64 columns on 8 waves); with fewer
+// strips than CUs the wide ones leave CUs idle (4096 x 4096: 19.1 us with 16 columns,
+// 22.4 with 32, 28.1 with 64). Rows that are not 16-byte aligned keep 16-column strips.
 hipError_t gemv_t_launch(const GemvArgs &a, hipStream_t stream)
 {
     const bool vec = (a.N % 4 == 0) && ((uintptr_t)a.A % 16 == 0);
-    const int64_t strips = ((int64_t)a.N + kStrip - 1) / kStrip;
+    const int strip = !vec || a.N <= 16 * 384 ? 16 : a.N <= 32 * 384 ? 32 : 64;
+    const int waves = strip == 64 ? 8 : kWaves;
+    const int64_t strips = ((int64_t)a.N + strip - 1) / strip;
     unsigned gx, gy;
     if (!grid_for(strips, gx, gy)) return hipErrorInvalidConfiguration;
     GemvArgs arg = a;
     void *args[] = {&arg};
-    const void *fn = vec ? reinterpret_cast<const void *>(&gemv_t_kernel<true>)
-                         : reinterpret_cast<const void *>(&gemv_t_kernel<false>);
-    return hipLaunchKernel(fn, dim3(gx, gy), dim3(kWaves * 64), args, 0, stream);
+    const void *fn = !vec         ? reinterpret_cast<const void *>(&gemv_t_kernel<false>)
+                     : strip == 16 ? reinterpret_cast<const void *>(&gemv_t_kernel<true>)
+                     : strip == 32 ? reinterpret_cast<const void *>(&gemv_t_kernel<true, 32, 4>)
+                                   : reinterpret_cast<const void *>(&gemv_t_kernel<true, 64, 8>);
+    return hipLaunchKernel(fn, dim3(gx, gy), dim3(waves * 64), args, 0, stream);
 }
 
 }  // namespace mm
