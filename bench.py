@@ -20,14 +20,15 @@ CPU oracle (64+ sampled GEMM rows in full, every GEMV output) and the oracle's
 own time on a bounded sample of the same work is reported as `cpu_baseline`.
 
 Profiling helpers (same script, for rocprofv3 runs): --only gemm | gemv | copy | h16 |
-conv | conv7x7 | split | gemm1024 | ragged | gemvt | narrow | h16_1024 runs just that kernel `--steps` times with no oracle;
+conv | conv7x7 | split | gemm1024 | ragged | gemvt | narrow | h16_1024 | torch_gemm runs just that kernel `--steps` times with no oracle;
 `copy` is a plain device-to-device copy of known size used to calibrate HBM counters;
 `h16` is the bf16-input GEMM at the projection shape; `conv` the 3x3 convolution layer
 (N=32, C=K=128, 28x28), `conv7x7` the 7x7 stride-2 first layer (N=32, C=3, 224x224, K=64); `split` the FC layer on a batch of 128 through both K splits;
 `gemm1024` and `ragged` the fp32 GEMM at 1024^3 and 1000 x 1531 x 777; `gemvt` the
 transposed GEMV with a workspace (row blocks, then the sum) on the GEMV workload's matrices;
 `narrow` the FC layer on a batch of 64 (4096 x 64 x 4096) through mm_gemm_f32, A rotating
-over 8 matrices; `h16_1024` the bf16-input GEMM at 1024^3.
+over 8 matrices; `h16_1024` the bf16-input GEMM at 1024^3; `torch_gemm` torch.mm (TF32 off)
+on the GEMM workload's inputs, a reference point.
 
 Sweeps (tables, not the benchmark line): --sweep conv times every convolution tile
 configuration on the layer workloads; --sweep gemm times every GEMM tile
@@ -36,6 +37,8 @@ at N = 4096 for growing M, which separates its per-launch fixed cost from its
 streaming rate. Both time a run of back-to-back launches between two events on
 the launch stream (for the GEMV this agrees with rocprofv3's kernel durations;
 kernels much shorter than ~5 us are bounded by the host's launch rate instead).
+--sweep lib times torch's library routines (torch.mm, torch.mv, conv2d) beside this
+library's kernels on the same shapes.
 """
 import argparse
 import hashlib
@@ -228,13 +231,13 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="target length of the oracle's timed sample")
     ap.add_argument("--only", choices=["gemm", "gemv", "copy", "h16", "conv", "split", "gemm1024", "ragged",
-                                           "gemvt", "narrow", "h16_1024", "conv7x7"],
+                                           "gemvt", "narrow", "h16_1024", "conv7x7", "torch_gemm"],
                     default=None,
                     help="profiling helper: launch only this kernel --steps times")
     ap.add_argument("--clock-seconds", type=float, default=None,
                     help="length of the clock phase (default 2.5 s after the timed steps; "
                          "with --only h16 none unless given; 0: no clock reading)")
-    ap.add_argument("--sweep", choices=["gemm", "gemv", "h16", "conv"], default=None,
+    ap.add_argument("--sweep", choices=["gemm", "gemv", "h16", "conv", "lib"], default=None,
                     help="print a timing table instead of the benchmark line")
     args = ap.parse_args()
 
@@ -384,6 +387,15 @@ def main():
             gemm()
         torch.cuda.synchronize()
         log(f"gemm: {args.steps} launches")
+        return
+    if args.only == "torch_gemm":
+        # torch's own fp32 GEMM (rocBLAS / hipBLASLt) on the same resident inputs: a
+        # reference point for profiles, not part of the path
+        torch.backends.cuda.matmul.allow_tf32 = False
+        for _ in range(args.steps):
+            torch.mm(A, B, out=C)
+        torch.cuda.synchronize()
+        log(f"torch_gemm: {args.steps} launches")
         return
     if args.only == "gemv":
         for i in range(args.steps):
@@ -701,8 +713,95 @@ def sweep_conv(torch, mm, dev):
         del f, Bd, Cd
 
 
+def sweep_lib(torch, mm, dev):
+    """The framework's own library routines on the same shapes and timing: rocBLAS /
+    hipBLASLt behind torch.mm and torch.mv, MIOpen behind conv2d. A reference point for
+    each kernel, not part of the path."""
+    torch.backends.cuda.matmul.allow_tf32 = False
+    torch.backends.cudnn.allow_tf32 = False
+    print("# this library's kernels against torch's library routines on the same shapes (MI355X, "
+          "one GPU); GEMMs: launches captured in a HIP graph and replayed between two events, "
+          "median of 3 replays; GEMV: back-to-back launches rotating over >= 512 MiB of matrices "
+          "(cold); convolution: back-to-back launches")
+    print("#   fp32 GEMM: torch.mm with TF32 off; 16-bit GEMM: torch.mm writes a bf16 C, "
+          "mm_gemm_bf16 an fp32 C; transposed GEMV: torch.mv on A.t()")
+    print(f"{'op':>22s} {'shape':>22s} {'this library':>14s} {'torch':>14s} {'ratio':>6s}")
+
+    def row(op, shape, ours, lib, unit):
+        print(f"{op:>22s} {shape:>22s} {ours:9.1f} {unit:>4s} {lib:9.1f} {unit:>4s} "
+              f"{ours / lib:6.2f}", flush=True)
+    for dt, name in ((torch.float32, "fp32 GEMM"), (torch.bfloat16, "bf16 GEMM")):
+        shapes = ([(8192, 14336, 4096), (8192, 4096, 14336), (4096, 4096, 4096), (1024, 1024, 1024),
+                   (1000, 1531, 777), (4096, 64, 4096)] if dt == torch.float32 else
+                  [(8192, 14336, 4096), (4096, 4096, 4096), (1024, 1024, 1024), (1000, 1531, 777)])
+        for M, N, K in shapes:
+            A = torch.randn(M, K, device=dev).to(dt)
+            B = (torch.randn(K, N, device=dev) / K ** 0.5).to(dt)
+            C = torch.empty(M, N, device=dev)
+            Ct = torch.empty(M, N, device=dev, dtype=dt)
+            flop = rl.gemm_flops(M, N, K)
+            reps = max(3, min(200, int((2e11 if dt == torch.float32 else 2e12) / flop)))
+            if dt == torch.float32:
+                def ours(i, st):
+                    mm.mm_gemm_f32(M, N, K, A, K, B, N, C, N, st)
+            else:
+                def ours(i, st):
+                    mm.mm_gemm_bf16(M, N, K, A, K, B, N, C, N, st)
+
+            def lib(i, st):
+                torch.mm(A, B, out=Ct)
+            t_ours = flop / median_graph_ms(torch, ours, reps) / 1e9
+            t_lib = flop / median_graph_ms(torch, lib, reps) / 1e9
+            row(name, f"{M}x{N}x{K}", t_ours, t_lib, "TF/s")
+            del A, B, C, Ct
+    for TM, TN, trans in ((4096, 4096, False), (8192, 8192, False), (4096, 4096, True),
+                          (8192, 8192, True), (4096, 16384, True)):
+        sets = max(2, min(16, (512 << 20) // (TM * TN * 4)))
+        As = [torch.rand(TM, TN, device=dev) for _ in range(sets)]
+        xs = [torch.rand(TM if trans else TN, device=dev) for _ in range(sets)]
+        ys = [torch.empty(TN if trans else TM, device=dev) for _ in range(sets)]
+        if trans:
+            def ours(i, st):
+                k = i % sets
+                mm.mm_gemv_t_f32(TM, TN, As[k], xs[k], ys[k], st)
+
+            def lib(i, st):
+                k = i % sets
+                torch.mv(As[k].t(), xs[k], out=ys[k])
+        else:
+            def ours(i, st):
+                k = i % sets
+                mm.mm_gemv_f32(TM, TN, As[k], xs[k], ys[k], st)
+
+            def lib(i, st):
+                k = i % sets
+                torch.mv(As[k], xs[k], out=ys[k])
+        by = rl.FP32 * (TM * TN + TM + TN)
+        t_ours = by / burst_time_ms(torch, ours, 8 * sets) / 1e6
+        t_lib = by / burst_time_ms(torch, lib, 8 * sets) / 1e6
+        row("transposed GEMV" if trans else "GEMV", f"{TM}x{TN}", t_ours, t_lib, "GB/s")
+        del As, xs, ys
+    for cw in wl.CONV_WORKLOADS.values():
+        x, f, y = conv_tensors(torch, cw, dev)
+        P, Q = cw.out_hw()
+        flop = rl.conv_flops(cw.N, cw.C, cw.K, cw.R, cw.S, P, Q)
+
+        def ours(i, st):
+            launch_conv(mm, cw, x, f, y, st)
+
+        def lib(i, st):
+            torch.nn.functional.conv2d(x, f, stride=cw.stride, padding=cw.pad, dilation=cw.dilation)
+        reps = max(3, min(100, int(2e11 / flop)))
+        t_ours = flop / burst_time_ms(torch, ours, reps) / 1e9
+        t_lib = flop / burst_time_ms(torch, lib, reps) / 1e9
+        row("fp32 convolution", cw.name, t_ours, t_lib, "TF/s")
+        del x, f, y
+
+
 def sweep(kind, torch, mm, dev):
-    if kind == "conv":
+    if kind == "lib":
+        sweep_lib(torch, mm, dev)
+    elif kind == "conv":
         sweep_conv(torch, mm, dev)
     elif kind == "gemm":
         shapes = [(w.M, w.N, w.K, w.name) for w in wl.WORKLOADS.values() if w.op == "gemm"]

@@ -358,15 +358,15 @@ __global__ __launch_bounds__(T::NT) void conv_direct_kernel(GemmArgs p, Im2colOp
         }
     };
 
-    int a_off[T::QW][T::FM], b_off[T::QW][4][T::FN];
-    direct_operand_offsets<T>(lane, wm0, wn0, a_off, b_off);
-    f32x16 acc[T::FM][T::FN];
+    DirectOffsets<T> off;
+    direct_offsets<T>(lane, wm0, wn0, off);
+    typename T::Acc acc[T::FM][T::FN];
 #pragma unroll
     for (int i = 0; i < T::FM; ++i)
 #pragma unroll
         for (int jj = 0; jj < T::FN; ++jj)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) acc[i][jj][r] = 0.f;
+            for (int r = 0; r < T::ACC; ++r) acc[i][jj][r] = 0.f;
 
     // loads per wave per K-step (a partial step issues more: the count is then conservative)
     constexpr int L = T::A16 + T::B4;
@@ -382,7 +382,7 @@ __global__ __launch_bounds__(T::NT) void conv_direct_kernel(GemmArgs p, Im2colOp
         wait_steps<L, T::NS - 2>(nk - 1 - kt);
         __syncthreads();
         if (kIssueFirst && kt + T::NS - 1 < nk) issue(kt + T::NS - 1);
-        direct_multiply<T>((const lds_char *)lds + (kt % T::NS) * T::STAGE, a_off, b_off, acc);
+        direct_mma<T>((const lds_char *)lds + (kt % T::NS) * T::STAGE, off, acc);
         if (!kIssueFirst && kt + T::NS - 1 < nk) issue(kt + T::NS - 1);
     }
     direct_store<T>(p, m0, n0, n0, wm0, wn0, lane, acc, [&](int gn) { return o.c_column(p, gn); });

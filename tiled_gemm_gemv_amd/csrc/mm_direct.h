@@ -31,16 +31,24 @@ typedef __attribute__((address_space(3))) float lds_float;
 // (direct_f32_wide_ok), which keeps the narrow-lane code out of the kernel.
 // KS: wave groups that split each K-step's k groups (KS = 2: 8 waves on a 4-wave tile grid;
 // group g multiplies groups g QN / 2 .. of every step, and the two sums meet in LDS).
-template <int BM_, int BN_, int WM_, int WN_, int NS_, bool GEN_, int BK_ = 16, int KS_ = 1>
+// M16: the MFMA is v_mfma_f32_16x16x4_f32 instead of v_mfma_f32_32x32x2_f32 (same work
+// per cycle on paper; measured with independent MFMAs issued back to back, 16x16x4 runs at
+// 154.8 TFLOP/s from one wave per SIMD and 154.4 from two, 32x32x2 at 142.8 and 150.7).
+template <int BM_, int BN_, int WM_, int WN_, int NS_, bool GEN_, int BK_ = 16, int KS_ = 1, bool M16_ = false>
 struct DirectF32 {
     static constexpr int BM = BM_, BN = BN_, BK = BK_, NS = NS_, WM = WM_, WN = WN_, KS = KS_;
+    static constexpr bool M16 = M16_;
     static constexpr int QN = BK / 8;      // groups of 4 k per wave half and K-step
     static constexpr int QW = QN / KS;     // ... that one wave multiplies
+    static constexpr int TQ = BK / 4;      // M16: MFMA steps per K-step
     static constexpr int A_ROW = BK * 4;   // bytes per A row
     static constexpr bool GEN = GEN_;
     static constexpr int GRID = (BM / WM) * (BN / WN);  // waves of the tile's wave grid
     static constexpr int WAVES = GRID * KS, NT = WAVES * 64;
-    static constexpr int FM = WM / 32, FN = WN / 32;
+    static constexpr int MB = M16 ? 16 : 32;  // edge of an MFMA block
+    static constexpr int FM = WM / MB, FN = WN / MB;
+    static constexpr int ACC = MB * MB / 64;  // accumulator registers per block and lane
+    typedef float Acc __attribute__((ext_vector_type(ACC)));
     static constexpr int A_BYTES = BM * BK * 4, B_BYTES = BK * BN * 4;
     static constexpr int STAGE = A_BYTES + B_BYTES;
     static constexpr int B_ROW = BN * 4;  // bytes per B row
@@ -54,6 +62,7 @@ struct DirectF32 {
     static_assert((NS - 2) * LOADS_NARROW_B <= 63, "vmcnt range");
     static_assert(BK == 16 || ((BK == 32 || BK == 64) && !GEN), "BK of 32 or 64 only for the lean build");
     static_assert(KS == 1 || (KS == 2 && !GEN && QN % 2 == 0), "K-step groups split in two only in the lean build");
+    static_assert(!M16 || KS == 1, "the 16 x 16 MFMA tiles run each K-step in one wave group");
 };
 
 // Rows of 64 bytes: two rows per 128 bytes of banks. Rows of 128 bytes: the 8 chunk slots
@@ -66,8 +75,15 @@ __device__ __forceinline__ int swz_a(int row)
     else if constexpr (T::BK == 32) return ((row >> 1) & 7) ^ ((row & 1) << 2);
     else return row & 15;  // rows of 256 bytes: any 16 consecutive rows, 16 distinct slots
 }
+// B rows: with 32 x 32 MFMAs the wave halves read rows r and r + BK/2 at once, put on
+// opposite halves of the banks; with 16 x 16 MFMAs the four lane groups read rows
+// r + g BK/4, put on the four quarters (16 consecutive columns of a row span 64 bytes).
 template <class T>
-__device__ __forceinline__ int swz_b(int krow) { return ((krow / (T::BK / 2)) & 1) * 8; }
+__device__ __forceinline__ int swz_b(int krow)
+{
+    if constexpr (T::M16) return ((krow / (T::BK / 4)) & 1) * 8;
+    else return ((krow / (T::BK / 2)) & 1) * 8;
+}
 
 // VEC bytes per lane from src into LDS at lds_addr + VEC * lane (lds_addr wave-uniform).
 // The LDS address travels in M0 as an operand of the asm statement ("{m0}"), so the
@@ -119,9 +135,24 @@ __device__ __forceinline__ void wait_steps(int steps)
     }
 }
 
-// This lane's operand addresses inside a stage (bytes): A per group q and block i; B per
-// group q, step j and block jj (k = (BK / 2) (lane / 32) + 4 q + j, column wn0 + 32 jj +
-// lane % 32), for this wave's QW groups q = q0 + qq.
+// A lane's operand addresses inside a stage (bytes), fixed for the whole K loop.
+//   32 x 32 MFMAs: A per group q and block i; B per group q, step j and block jj
+//     (k = (BK / 2) (lane / 32) + 4 q + j, column wn0 + 32 jj + lane % 32).
+//   16 x 16 MFMAs: lane group g = lane / 16 takes k = (BK / 4) g + t at MFMA step t, so a
+//     16-byte read of A gives 4 steps (a[u][i]: steps 4u .. 4u + 3 of row block i, row
+//     wm0 + 16 i + lane % 16), and B's value for step t and column block jj sits at
+//     b[jj] + t B_ROW (column wn0 + 16 jj + lane % 16).
+template <class T, bool = T::M16>
+struct DirectOffsets {
+    int a[T::QW][T::FM];
+    int b[T::QW][4][T::FN];
+};
+template <class T>
+struct DirectOffsets<T, true> {
+    int a[T::TQ / 4][T::FM];
+    int b[T::FN];
+};
+
 template <class T>
 __device__ __forceinline__ void direct_operand_offsets(int lane, int wm0, int wn0, int (&a_off)[T::QW][T::FM],
                                                        int (&b_off)[T::QW][4][T::FN], int q0 = 0)
@@ -143,6 +174,31 @@ __device__ __forceinline__ void direct_operand_offsets(int lane, int wm0, int wn
                 b_off[qq][j][jj] = T::A_BYTES + krow * T::B_ROW + 16 * ((col >> 2) ^ swz_b<T>(krow)) +
                                    4 * (col & 3);
             }
+    }
+}
+
+// For this wave's QW groups q = q0 + qq of each K-step (32 x 32 MFMAs), or all of its
+// steps (16 x 16).
+template <class T>
+__device__ __forceinline__ void direct_offsets(int lane, int wm0, int wn0, DirectOffsets<T> &o, int q0 = 0)
+{
+    if constexpr (T::M16) {
+        const int g = lane >> 4, l16 = lane & 15;
+#pragma unroll
+        for (int u = 0; u < T::TQ / 4; ++u)
+#pragma unroll
+            for (int i = 0; i < T::FM; ++i) {
+                const int row = wm0 + 16 * i + l16;
+                o.a[u][i] = row * T::A_ROW + 16 * ((g * (T::TQ / 4) + u) ^ swz_a<T>(row));
+            }
+        const int krow = T::TQ * g;  // step 0's row; step t adds t B_ROW (same swizzle)
+#pragma unroll
+        for (int jj = 0; jj < T::FN; ++jj) {
+            const int col = wn0 + 16 * jj + l16;
+            o.b[jj] = T::A_BYTES + krow * T::B_ROW + 16 * ((col >> 2) ^ swz_b<T>(krow)) + 4 * (col & 3);
+        }
+    } else {
+        direct_operand_offsets<T>(lane, wm0, wn0, o.a, o.b, q0);
     }
 }
 
@@ -172,14 +228,68 @@ __device__ __forceinline__ void direct_multiply(const lds_char *st, const int (&
     }
 }
 
+// The MFMAs of one K-step on stage st, either MFMA shape.
+template <class T>
+__device__ __forceinline__ void direct_mma(const lds_char *st, const DirectOffsets<T> &o,
+                                           typename T::Acc (&acc)[T::FM][T::FN])
+{
+    if constexpr (T::M16) {
+#pragma unroll
+        for (int u = 0; u < T::TQ / 4; ++u) {
+            f32x4 a[T::FM];
+            float b[4][T::FN];
+#pragma unroll
+            for (int i = 0; i < T::FM; ++i)
+                a[i] = *(const __attribute__((address_space(3))) f32x4 *)(st + o.a[u][i]);
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+#pragma unroll
+                for (int jj = 0; jj < T::FN; ++jj)
+                    b[t][jj] = *(const lds_float *)(st + o.b[jj] + (4 * u + t) * T::B_ROW);
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+#pragma unroll
+                for (int i = 0; i < T::FM; ++i)
+#pragma unroll
+                    for (int jj = 0; jj < T::FN; ++jj)
+                        acc[i][jj] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[i][t], b[t][jj], acc[i][jj], 0, 0, 0);
+        }
+    } else {
+        direct_multiply<T>(st, o.a, o.b, acc);
+    }
+}
+
 // Accumulator layout of v_mfma_f32_32x32x2_f32: lane l, register r holds row
 // 8 (r / 4) + 4 (l / 32) + r % 4, column l % 32 of the 32 x 32 block. The tile's columns
 // start at nb0; element (gm, gn) of the product goes to C + gm * ldc + col_off(gn), for
 // gm < M, gn < N and gn >= n_first (columns left of n_first belong to another tile).
+// Of v_mfma_f32_16x16x4_f32: lane l, register r holds row 4 (l / 16) + r, column l % 16.
 template <class T, class ColOff>
 __device__ __forceinline__ void direct_store(const GemmArgs &p, int m0, int nb0, int n_first, int wm0, int wn0,
-                                             int lane, const f32x16 (&acc)[T::FM][T::FN], ColOff col_off)
+                                             int lane, const typename T::Acc (&acc)[T::FM][T::FN], ColOff col_off)
 {
+    if constexpr (T::M16) {
+        const int col_l = lane & 15, row_l = 4 * (lane >> 4);
+        int64_t coff[T::FN];
+        bool cok[T::FN];
+#pragma unroll
+        for (int jj = 0; jj < T::FN; ++jj) {
+            const int gn = nb0 + wn0 + jj * 16 + col_l;
+            cok[jj] = gn < p.N && gn >= n_first;
+            coff[jj] = cok[jj] ? col_off(gn) : 0;
+        }
+#pragma unroll
+        for (int i = 0; i < T::FM; ++i)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int gm = m0 + wm0 + i * 16 + row_l + r;
+                if (gm >= p.M) continue;
+#pragma unroll
+                for (int jj = 0; jj < T::FN; ++jj)
+                    if (cok[jj]) p.C[(int64_t)gm * p.ldc + coff[jj]] = acc[i][jj][r];
+            }
+        return;
+    }
     const int col_l = lane & 31, row_l = 4 * (lane >> 5);
     // a lane's column in each 32-column block, and its offset in C, once per block: inside
     // the guarded stores the compiler would evaluate col_off per element (for the
@@ -209,8 +319,9 @@ __device__ __forceinline__ void direct_store(const GemmArgs &p, int m0, int nb0,
 // depend on which half arrives first (0 + x is exact and x + y == y + x).
 template <class T>
 __device__ __forceinline__ void direct_store_add(const GemmArgs &p, int m0, int nb0, int n_first, int wm0, int wn0,
-                                                 int lane, const f32x16 (&acc)[T::FM][T::FN])
+                                                 int lane, const typename T::Acc (&acc)[T::FM][T::FN])
 {
+    static_assert(!T::M16, "the atomic epilogue is built for the 32 x 32 MFMA tiles only");
     const int col_l = lane & 31, row_l = 4 * (lane >> 5);
 #pragma unroll
     for (int i = 0; i < T::FM; ++i)

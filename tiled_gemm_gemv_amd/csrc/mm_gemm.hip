@@ -57,6 +57,8 @@ const ConfigEntry kConfigs[] = {
      &direct<DirectTile::T64K2>, 64, 64, 8, 2, 140, 16, 5.5},
     {"narrow 16x64 (16x16x4 MFMA), A and B moved into LDS in whole row segments (N % 4 == 0, K a multiple of 256 or 128; else config 8's kernel)",
      &gemm_narrow_launch, 16, 64, 16, 1, 0, 16},
+    {"128x128x16 w64x64 16x16x4 MFMA direct-to-LDS 4 stages (4 waves; K % 32 == 0: K-steps of 32, 2 stages)",
+     &direct<DirectTile::T128M16>, 128, 128, 4, 2, 150, 16, 5},
 };
 constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
 
@@ -94,11 +96,13 @@ int gemm_select_config(int64_t M, int64_t N, int64_t K, int64_t batch)
     // K % 32 == 0: the model rates it above 13 where a CU holds one tile (1024^3: 99 against
     // 97 TFLOP/s), and the two tie where it holds several, which 13 (listed first) takes
     // (1536^3: 100 against 92, 3072^3: 138 against 133, 8192 x 1792 x 4096: 141 against 136).
-    static const int kTileConfigs[] = {0, 1, 2, 3, 4, 5, 10, 11, 12, 13, 14};
+    // 16 is 11's tile on v_mfma_f32_16x16x4_f32 (rated above it: 149.5 against 147.1 at
+    // 8192 x 14336 x 4096, 148.0 against 145.2 at 4096^3), so 11 is never chosen.
+    static const int kTileConfigs[] = {0, 1, 2, 3, 4, 5, 10, 11, 12, 13, 14, 16};
     int best = 0;
     double best_t = 0;
     for (int c : kTileConfigs) {
-        if ((c == 10 || c == 11) && K < 2048) continue;
+        if ((c == 10 || c == 11 || c == 16) && K < 2048) continue;
         const double t = gemm_config_time(c, M, N, K, batch);
         if (c == 0 || t < best_t) {
             best = c;

@@ -131,20 +131,18 @@ __global__ __launch_bounds__(T::NT) void gemm_f32_direct_kernel(GemmArgs p)
     const unsigned lds0 = (unsigned)(uintptr_t)(lds_char *)lds;  // LDS byte offset of the array
     const int nk_full = p.K / T::BK;  // full K-steps; a partial one follows if K % 16 != 0
 
-    int a_off[T::QW][T::FM], b_off[T::QW][4][T::FN];
-    direct_operand_offsets<T>(lane, wm0, wn0, a_off, b_off, kg * T::QW);
+    DirectOffsets<T> off;
+    direct_offsets<T>(lane, wm0, wn0, off, kg * T::QW);
 
-    f32x16 acc[T::FM][T::FN];
+    typename T::Acc acc[T::FM][T::FN];
 #pragma unroll
     for (int i = 0; i < T::FM; ++i)
 #pragma unroll
         for (int jj = 0; jj < T::FN; ++jj)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) acc[i][jj][r] = 0.f;
+            for (int r = 0; r < T::ACC; ++r) acc[i][jj][r] = 0.f;
 
-    auto multiply = [&](int kt) {
-        direct_multiply<T>((const lds_char *)lds + (kt % T::NS) * T::STAGE, a_off, b_off, acc);
-    };
+    auto multiply = [&](int kt) { direct_mma<T>((const lds_char *)lds + (kt % T::NS) * T::STAGE, off, acc); };
 
     // The K loop, compiled once per kind of tile (16- or 4-byte B lanes), so that a K-step
     // tests nothing but whether it has a step to issue.
@@ -288,14 +286,15 @@ namespace {
 // 8 MFMAs per K-step). Where K % 32 == 0 too, K-steps of 32 in half as many stages (the
 // same LDS): whole 128-byte A lines and twice the MFMAs per barrier, 1-8% faster on the
 // 128 x 128 and 64 x 64 tiles.
-template <int BM, int BN, int WM, int WN, int NS, bool ADD = false>
+template <int BM, int BN, int WM, int WN, int NS, bool ADD = false, bool M16 = false>
 hipError_t launch_lean_or_general(const GemmArgs &a, hipStream_t stream)
 {
     if (direct_f32_wide_ok(a, BN) && a.K % 32 == 0)
-        return launch_direct<DirectF32<BM, BN, WM, WN, NS / 2, false, 32>, true, ADD>(a, stream);
-    if (direct_f32_wide_ok(a, BN)) return launch_direct<DirectF32<BM, BN, WM, WN, NS, false>, true, ADD>(a, stream);
-    return direct_f32_offsets_fit(a) ? launch_direct<DirectF32<BM, BN, WM, WN, NS, true>, true, ADD>(a, stream)
-                                     : launch_direct<DirectF32<BM, BN, WM, WN, NS, true>, false, ADD>(a, stream);
+        return launch_direct<DirectF32<BM, BN, WM, WN, NS / 2, false, 32, 1, M16>, true, ADD>(a, stream);
+    if (direct_f32_wide_ok(a, BN))
+        return launch_direct<DirectF32<BM, BN, WM, WN, NS, false, 16, 1, M16>, true, ADD>(a, stream);
+    return direct_f32_offsets_fit(a) ? launch_direct<DirectF32<BM, BN, WM, WN, NS, true, 16, 1, M16>, true, ADD>(a, stream)
+                                     : launch_direct<DirectF32<BM, BN, WM, WN, NS, true, 16, 1, M16>, false, ADD>(a, stream);
 }
 
 }  // namespace
@@ -310,6 +309,8 @@ hipError_t gemm_direct_launch(DirectTile t, const GemmArgs &a, hipStream_t strea
         return launch_direct<DirectF32<256, 256, 128, 64, 4, false>>(a, stream);
     case DirectTile::T128:
         return launch_lean_or_general<128, 128, 64, 64, 4>(a, stream);
+    case DirectTile::T128M16:
+        return launch_lean_or_general<128, 128, 64, 64, 4, false, true>(a, stream);
     case DirectTile::T64S8:
         return launch_lean_or_general<64, 64, 32, 32, 8>(a, stream);
     case DirectTile::T64S4:

@@ -124,7 +124,7 @@ hipError_t gemm_narrow_launch(const GemmArgs &a, hipStream_t stream);
 // (hipErrorInvalidValue otherwise). T64S8 / T64S4: 64 x 64 tiles with 8 / 4 LDS stages.
 // direct_f32_wide_ok(a, bn): every B load of a tile bn wide can take 16-byte lanes
 // (K % 16 == 0, and N % 4 == 0 or N >= bn) and the lane offsets fit 32 bits.
-enum class DirectTile { T256, T128, T64S8, T64S4, T64K2 };
+enum class DirectTile { T256, T128, T64S8, T64S4, T64K2, T128M16 };
 bool direct_f32_wide_ok(const GemmArgs &a, int bn);
 hipError_t gemm_direct_launch(DirectTile t, const GemmArgs &a, hipStream_t stream);
 // The 64 x 64 direct tile (4 stages; K-steps over two wave groups where K % 32 == 0, as
