@@ -731,8 +731,9 @@ def sweep_lib(torch, mm, dev):
         print(f"{op:>22s} {shape:>22s} {ours:9.1f} {unit:>4s} {lib:9.1f} {unit:>4s} "
               f"{ours / lib:6.2f}", flush=True)
     for dt, name in ((torch.float32, "fp32 GEMM"), (torch.bfloat16, "bf16 GEMM")):
-        shapes = ([(8192, 14336, 4096), (8192, 4096, 14336), (4096, 4096, 4096), (1024, 1024, 1024),
-                   (1000, 1531, 777), (4096, 64, 4096)] if dt == torch.float32 else
+        shapes = ([(8192, 14336, 4096), (8192, 4096, 14336), (4096, 4096, 4096), (2048, 2048, 2048),
+                   (1024, 1024, 1024), (1000, 1531, 777), (4096, 64, 4096), (4096, 32, 4096),
+                   (4096, 16, 4096)] if dt == torch.float32 else
                   [(8192, 14336, 4096), (4096, 4096, 4096), (1024, 1024, 1024), (1000, 1531, 777)])
         for M, N, K in shapes:
             A = torch.randn(M, K, device=dev).to(dt)
