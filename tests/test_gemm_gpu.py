@@ -122,7 +122,7 @@ DIRECT_SHAPES = [(1, 4, 16), (37, 8, 32), (300, 264, 48), (257, 520, 64), (300, 
                  (513, 260, 160), (129, 136, 4096), (1000, 1532, 800)]
 
 
-@pytest.mark.parametrize("cfg", [10, 11, 12, 13, None])
+@pytest.mark.parametrize("cfg", [10, 11, 12, 13, 16, None])
 @pytest.mark.parametrize("shape", DIRECT_SHAPES)
 def test_direct_pipeline_shapes(dev, cfg, shape):
     M, N, K = shape
@@ -147,6 +147,20 @@ def test_direct_256_same_bits_as_staged_256(dev, shape):
     assert np.array_equal(C10.view(np.int32), C0.view(np.int32))
 
 
+def test_16x16_tile_builds(dev):
+    """Configuration 16 (the 128 x 128 tile on 16 x 16 MFMAs) in each of its builds: K = 96
+    (lean, K-steps of 32), 112 (lean, K-steps of 16) and 100 (general, a partial last
+    K-step zero-filled in LDS): exact on integers, within tolerance on normal inputs."""
+    M, N = 300, 264
+    for K in (96, 112, 100):
+        A = wl.random_matrix(61 + K, M, K, "int4")
+        B = wl.random_matrix(62 + K, K, N, "int4")
+        assert_exact(gpu_gemm(A, B, dev, 16), A, B)
+        A = wl.random_matrix(63 + K, M, K, "normal")
+        B = wl.random_matrix(64 + K, K, N, "normal")
+        assert_tol(gpu_gemm(A, B, dev, 16), A, B)
+
+
 # Shapes that only the 4-byte DMA lanes take (K % 16 != 0, odd leading dimensions, N < 4):
 # a partial K-step alone (K < 16), after one or many full steps, with a pipeline deeper
 # than the K loop, and the ragged shape of the benchmark set (lda 777, ldb 1531).
@@ -154,7 +168,7 @@ DIRECT_RAGGED = [(1, 1, 1), (5, 3, 7), (64, 64, 15), (130, 70, 33), (257, 2, 1),
                  (1000, 1531, 777), (129, 67, 4099)]
 
 
-@pytest.mark.parametrize("cfg", [11, 12, 13])
+@pytest.mark.parametrize("cfg", [11, 12, 13, 16])
 @pytest.mark.parametrize("shape", DIRECT_RAGGED)
 def test_direct_pipeline_ragged(dev, cfg, shape):
     M, N, K = shape
@@ -196,7 +210,7 @@ def test_strided_poisoned_views(dev, cfg, offsets):
     assert outside_untouched(Cbuf, M, N)
 
 
-@pytest.mark.parametrize("cfg", [10, 11, 12, 13])
+@pytest.mark.parametrize("cfg", [10, 11, 12, 13, 16])
 @pytest.mark.parametrize("K", [96, 112])
 @pytest.mark.parametrize("offsets", [(0, 0), (1, 2)])
 def test_direct_lean_strided_poisoned_views(dev, cfg, K, offsets):
@@ -216,7 +230,7 @@ def test_direct_lean_strided_poisoned_views(dev, cfg, K, offsets):
     assert outside_untouched(Cbuf, M, N)
 
 
-@pytest.mark.parametrize("cfg", [10, 11, 12, 13])
+@pytest.mark.parametrize("cfg", [10, 11, 12, 13, 16])
 def test_direct_huge_leading_dimension(dev, cfg):
     """lda of 5M floats: 255 rows of it exceed the 32-bit lane offsets the lean builds
     use, so those shapes take the general build (or, for the 256 x 256 tile, the
