@@ -14,6 +14,10 @@
 //   * k order: lanes 0-31 take k = 4 q + j and lanes 32-63 k = BK/2 + 4 q + j at step j
 //     of group q (q < BK/8), so each k of the K-step is added once, in the order of the
 //     register-staged kernel with the same BK (the same bits).
+//   * Tiles on v_mfma_f32_16x16x4_f32 (M16): lane group g = lane / 16 takes k = (BK/4) g + t
+//     at MFMA step t, so one 16-byte read of A still serves 4 steps; the four groups read B
+//     rows r + g BK/4 at once, and swz_b puts groups 0/1 (and 2/3) on opposite bank halves
+//     (chunk index ^ 8, which keeps each 128-byte line of B whole in the DMA).
 // BK = 32 makes each A row of a K-step one whole 128-byte line (at BK = 16 a load of A
 // touches 16 half-used lines, and the DMA's LDS writes of those rows count bank-conflict
 // cycles) and doubles the MFMAs per barrier; with half the stages in the same LDS it
