@@ -38,7 +38,8 @@ streaming rate. Both time a run of back-to-back launches between two events on
 the launch stream (for the GEMV this agrees with rocprofv3's kernel durations;
 kernels much shorter than ~5 us are bounded by the host's launch rate instead).
 --sweep lib times torch's library routines (torch.mm, torch.mv, conv2d) beside this
-library's kernels on the same shapes.
+library's kernels on the same shapes; the benchmark line's `library_reference` does the
+same for its own GEMM and GEMV.
 """
 import argparse
 import hashlib
@@ -473,6 +474,31 @@ def main():
                   gemm_avg_s)
     torch.cuda.synchronize()
 
+    # ---- library reference: torch's own GEMM (rocBLAS / hipBLASLt, TF32 off) and GEMV on
+    # the same resident inputs, timed the same way, into separate outputs (C and y are
+    # verified below as this library computed them). A reference point, not the path.
+    torch.backends.cuda.matmul.allow_tf32 = False
+    Ct = torch.empty_like(C)
+    yts = [torch.empty_like(y) for y in yvs]
+    lib_reps = min(10, max(2, steps))
+    for _ in range(2):
+        torch.mm(A, B, out=Ct)
+    for i in range(GEMV_SETS):
+        torch.mv(Avs[i], xvs[i], out=yts[i])
+    torch.cuda.synchronize()
+    l0, l1, l2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+    l0.record(stream)
+    for _ in range(lib_reps):
+        torch.mm(A, B, out=Ct)
+    l1.record(stream)
+    for i in range(reps):
+        torch.mv(Avs[i % GEMV_SETS], xvs[i % GEMV_SETS], out=yts[i % GEMV_SETS])
+    l2.record(stream)
+    torch.cuda.synchronize()
+    lib_gemm_tflops = gemm_flop / (l0.elapsed_time(l1) / lib_reps / 1e3) / 1e12
+    lib_gemv_gbs = gemv_bytes / (l1.elapsed_time(l2) / reps / 1e3) / 1e9
+    del Ct, yts
+
     # ------------------------------------------- verification + CPU baseline leg
     import oracle
     from oracle import verify
@@ -583,6 +609,14 @@ def main():
                       f"GEMM, fp64 accumulation, {t_cpu:.2f} s on {cpu_model()}",
             "full_matrix_s_extrapolated": round(t_cpu * M / len(rows), 1),
         },
+        "library_reference": {
+            "gemm": {"value": round(lib_gemm_tflops, 3), "unit": "TFLOP/s",
+                     "this_over_library": round(gemm_tflops / lib_gemm_tflops, 4),
+                     "how": f"torch.mm (TF32 off) on the same A and B, {lib_reps} launches between two events"},
+            "gemv": {"value": round(lib_gemv_gbs, 1), "unit": "GB/s",
+                     "this_over_library": round(gemv_gbs / lib_gemv_gbs, 4),
+                     "how": f"torch.mv over the same {GEMV_SETS} rotating matrices, {reps} launches between two events"},
+            "note": "torch's own routines on this GPU, as a reference point; not part of the path"},
         "cpu_single_thread": {
             "gemm128": {"value": round(rl.gemm_flops(128, 128, 128) / min(t1g) / 1e9, 3), "unit": "GFLOP/s",
                         "ms": round(min(t1g) * 1e3, 3)},
