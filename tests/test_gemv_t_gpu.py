@@ -41,7 +41,8 @@ def reference(A, x):
 # at 8200 and 12292)
 @pytest.mark.parametrize("M,N", [(4096, 4096), (1, 1), (3, 5), (1000, 1531), (4097, 17),
                                  (20000, 64), (17, 4100), (333, 4095), (300, 8200),
-                                 (1000, 12288), (130, 12292), (70, 16384)])
+                                 (1000, 12288), (130, 12292), (70, 16384), (257, 6144),
+                                 (257, 6148), (65, 12284)])
 @pytest.mark.parametrize("a_offset", [0, 1])
 def test_shapes(dev, M, N, a_offset):
     A = wl.random_matrix(500 + M, M, N, "int4")
