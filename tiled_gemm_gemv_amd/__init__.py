@@ -17,7 +17,9 @@ Build it with `python -m tiled_gemm_gemv_amd.build`.
 import ctypes
 import os
 
-from .build import LIB as _LIB_PATH
+# the library build.py writes (not imported from there, so that `python -m
+# tiled_gemm_gemv_amd.build` runs the module once)
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmm.so")
 
 MM_OK = 0
 MM_ERR_INVALID_ARG = 1
